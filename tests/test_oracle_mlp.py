@@ -1,0 +1,151 @@
+"""Pins for the oracle's expert MLP, shared expert, combine and the whole
+forward.
+
+Pinned against: a dense fp64 evaluation of every expert on every token
+combined by a dense [T, E] weight matrix (no permutation at all; the "MoE vs
+dense reference" idea of the TE DeepSeekV3Layer test list), the special case
+one expert + k = 1 == a dense SwiGLU MLP (torch fp64), the closed form
+W1 = [I; I], W2 = I -> silu(x) * x, a constant-row combine, and MX layers
+checked against the same dense fp64 evaluation on brute-force-quantized
+operands.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mlp, mx, permute as pm, routing as rt
+from moe_synth import configs, gen
+from tests import brute
+
+
+def _layer(cfg, seed=0):
+    d = gen.host_inputs(cfg, seed)
+    shared = (d["w1s"], d["w2s"]) if cfg.n_shared else None
+    res = mlp.moe_forward(d["x"], d["w_router"], d["bias"], lambda e: d["w1"][e], lambda e: d["w2"][e],
+                          E=cfg.E, n_group=cfg.n_group, topk_group=cfg.topk_group, k=cfg.k,
+                          routed_scale=cfg.routed_scale, fmt=cfg.fmt, align=cfg.align,
+                          shared_w=shared)
+    return d, res
+
+
+def _dense_w(res, T, E):
+    dw = np.zeros((T, E))
+    np.put_along_axis(dw, res["idx"].astype(np.int64), res["w"].astype(np.float64), axis=1)
+    return dw
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "tiny_fp32_unitx", "mini_fp32"])
+def test_forward_equals_dense_fp64(name):
+    cfg = configs.get(name)
+    d, res = _layer(cfg)
+    ref = brute.dense_moe_fp64(d["x"], d["w1"], d["w2"], _dense_w(res, cfg.T, cfg.E))
+    assert brute.rel_l2(res["out"], ref) < 2e-6
+
+
+def test_forward_bf16_values_with_shared_equals_dense_fp64():
+    cfg = configs.get("mini_bf16")
+    d, res = _layer(cfg)
+    ref = brute.dense_moe_fp64(d["x"], d["w1"], d["w2"], _dense_w(res, cfg.T, cfg.E),
+                               shared=(d["w1s"], d["w2s"]))
+    assert brute.rel_l2(res["out"], ref) < 2e-6
+    # the shared expert alone matches a dense fp64 SwiGLU MLP
+    ref_s = brute.dense_moe_fp64(d["x"], d["w1s"][None], d["w2s"][None], np.ones((cfg.T, 1)))
+    assert brute.rel_l2(res["shared"], ref_s) < 2e-6
+
+
+def test_single_expert_k1_is_dense_swiglu():
+    g = np.random.default_rng(0)
+    T, H, F = 37, 64, 48
+    x = g.standard_normal((T, H)).astype(np.float32)
+    w1 = (g.standard_normal((2 * F, H)) / 8).astype(np.float32)
+    w2 = (g.standard_normal((H, F)) / 7).astype(np.float32)
+    res = mlp.moe_forward(x, np.ones((1, H), np.float32), np.zeros(1, np.float32),
+                          lambda e: w1, lambda e: w2, E=1, n_group=1, topk_group=1, k=1,
+                          routed_scale=1.0, fmt="fp32")
+    xt = torch.tensor(x, dtype=torch.float64)
+    a = xt @ torch.tensor(w1, dtype=torch.float64).T
+    ref = (torch.nn.functional.silu(a[:, :F]) * a[:, F:]) @ torch.tensor(w2, dtype=torch.float64).T
+    assert (res["w"] == 1.0).all()
+    assert brute.rel_l2(res["out"], ref.numpy()) < 2e-6
+
+
+def test_identity_weights_closed_form():
+    g = np.random.default_rng(1)
+    T, H, E = 20, 32, 4
+    x = g.standard_normal((T, H)).astype(np.float32)
+    eye = np.eye(H, dtype=np.float32)
+    w1 = np.concatenate([eye, eye])
+    res = mlp.moe_forward(x, g.standard_normal((E, H)).astype(np.float32), np.zeros(E, np.float32),
+                          lambda e: w1, lambda e: eye, E=E, n_group=2, topk_group=1, k=2,
+                          routed_scale=2.5, fmt="fp32")
+    x64 = x.astype(np.float64)
+    ref = 2.5 * x64 / (1 + np.exp(-x64)) * x64
+    assert np.allclose(res["out"], ref, rtol=3e-6, atol=1e-6)
+
+
+def test_combine_constant_rows():
+    T, k, H = 9, 3, 16
+    rm = np.arange(T * k).reshape(T, k)
+    w = np.random.default_rng(2).uniform(0.1, 1, (T, k)).astype(np.float32)
+    w = (w / w.sum(1, keepdims=True) * np.float32(2.5)).astype(np.float32)
+    y = np.full((T * k, H), 3.0, np.float32)
+    sh = np.full((T, H), 1.0, np.float32)
+    out = mlp.combine(y, rm, w, sh)
+    assert np.allclose(out, 3.0 * 2.5 + 1.0, rtol=1e-6)
+
+
+def test_combine_uses_row_map():
+    rng = np.random.default_rng(3)
+    idx = np.stack([rng.permutation(6)[:2] for _ in range(10)]).astype(np.int32)
+    _, _, rm, src = pm.permute_maps(idx, 6, 16)
+    y = rng.standard_normal((len(src), 8)).astype(np.float32)
+    w = rng.uniform(0, 1, (10, 2)).astype(np.float32)
+    out = mlp.combine(y, rm, w)
+    ref = np.array([sum(np.float64(w[t, j]) * y[rm[t, j]].astype(np.float64) for j in range(2)) for t in range(10)])
+    assert np.allclose(out, ref, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("name", ["mini_mxfp8_decode", "mini_mxfp4"])
+def test_mx_forward_against_brute_quantized_dense(name):
+    """MX layers: operands are re-quantized by the linear-search quantizer and
+    the layer is evaluated densely in fp64; h is quantized per row along F."""
+    cfg = configs.get(name)
+    T = 12
+    d = gen.host_inputs(cfg)
+    d["x"] = d["x"][:T]
+    fmt = mx.fmt_of(cfg.fmt)
+
+    def bq(v, axis=-1):
+        return brute.bf_fake_quant(v, fmt, axis)
+
+    experts = [0, 5]                      # a two-expert layer keeps the brute force quick
+    w1 = d["w1"][experts]
+    w2 = d["w2"][experts]
+    wr = d["w_router"][experts]
+    res = mlp.moe_forward(d["x"], wr, d["bias"][experts], lambda e: w1[e], lambda e: w2[e],
+                          E=2, n_group=1, topk_group=1, k=1, routed_scale=1.0, fmt=cfg.fmt)
+    xq = bq(d["x"])
+    w1q = [bq(w) for w in w1]
+    w2q = [bq(w) for w in w2]
+    out = np.zeros((T, cfg.H))
+    for t in range(T):
+        e = res["idx"][t, 0]
+        a = xq[t] @ w1q[e].T
+        F = cfg.F
+        h = a[:F] / (1 + np.exp(-a[:F])) * a[F:]
+        hq = bq(h.astype(np.float32)[None])[0]
+        out[t] = res["w"][t, 0] * (hq @ w2q[e].T)
+    # h is quantized from fp32 values on both sides; allow rare code flips
+    assert brute.rel_l2(res["out"], out) < 2e-3
+
+
+def test_forward_subset_of_tokens_matches_full():
+    cfg = configs.get("mini_bf16")
+    d, full = _layer(cfg)
+    toks = [0, 7, 299]
+    res = mlp.moe_forward(d["x"], d["w_router"], d["bias"], lambda e: d["w1"][e], lambda e: d["w2"][e],
+                          E=cfg.E, n_group=cfg.n_group, topk_group=cfg.topk_group, k=cfg.k,
+                          routed_scale=cfg.routed_scale, fmt=cfg.fmt, shared_w=(d["w1s"], d["w2s"]),
+                          tokens=toks)
+    # BLAS blocking differs with the row count, so equal to fp32 rounding
+    assert brute.rel_l2(res["out"], full["out"][toks]) < 1e-6
