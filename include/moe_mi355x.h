@@ -1,0 +1,266 @@
+/*
+ * moe_mi355x.h — C ABI of a sigmoid-routed mixture-of-experts layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the routed MoE of the page "[PyTorch] DeepSeekV3Layer: full
+ * MoE transformer layer (MLA + DeepSeek MoE)" (TransformerEngine pull
+ * request), section Description, DeepSeekV3MoE item: a fused sigmoid router
+ * with an aux-loss-free (selection-only) bias and grouped top-k, experts
+ * built as GroupedLinear -> ScaledSwiGLU -> GroupedLinear, local routing,
+ * and an optional shared expert. Its Performance section ("Where the time
+ * goes" table) names the remaining steps: a local permute into an
+ * expert-major staging buffer with zero-filled padding, the fused grouped
+ * MLP (fc1+SwiGLU, fc2, dGLU backward, wgrad) and MXFP8 quantization of the
+ * received rows. The 4-bit W4A4 MoE of "Mistral Large 3 NVFP4 TRTLLM MoE
+ * support" (sglang pull request, Modifications section) is served here by
+ * MXFP4.
+ *
+ * A forward pass is:
+ *   moe_route -> [moe_quantize_mx] -> moe_permute -> moe_grouped_mlp_fwd
+ *   (routed experts; again with E = 1 for a shared expert) -> moe_combine
+ * where moe_grouped_mlp_fwd is moe_grouped_fc1_swiglu followed by
+ * moe_grouped_fc2.
+ *
+ * Conventions for every call
+ *   - Pointers are device pointers owned by the caller unless stated; the
+ *     library never allocates and keeps no state between calls. Scratch
+ *     memory comes from the caller (size queries *_workspace).
+ *   - Tensors are dense and row-major; pointers to tensors must be 16-byte
+ *     aligned, and row strides are whole rows (no padding between rows).
+ *   - MX tensors: element codes [rows, K] bytes (E4M3) or [rows, K/2] bytes
+ *     (E2M1, two per byte, the even element in the low nibble), plus E8M0
+ *     scale bytes [rows, K/32] (scale = 2^(byte - 127)); blocks of 32
+ *     consecutive elements along K share one scale. K % 32 == 0.
+ *   - Calls are asynchronous on `stream` (0 = the null stream). All argument
+ *     checks run on the host before anything is enqueued: a call that
+ *     returns an error has enqueued nothing. Device faults surface at the
+ *     caller's next synchronization.
+ *   - Every call returns MOE_OK (0) or a negative moe_status;
+ *     moe_last_error() returns a message for the calling thread's last
+ *     failure. No C++ exception crosses the ABI.
+ *   - Calls touch only their arguments, so concurrent calls on different
+ *     streams with disjoint outputs are safe.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* bad shape, bad enum value or null pointer  */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but unsupported format combination   */
+  MOE_ERR_ALIGNMENT = -3,    /* pointer or row size not 16-byte aligned    */
+  MOE_ERR_WORKSPACE = -4,    /* workspace missing or too small             */
+  MOE_ERR_HIP = -5           /* the HIP runtime reported a launch error    */
+} moe_status;
+
+typedef enum moe_format {
+  MOE_F32 = 0,               /* IEEE binary32                              */
+  MOE_BF16 = 1,              /* bfloat16                                   */
+  MOE_MXFP8_E4M3 = 2,        /* E4M3 codes + E8M0 scales per 32 along K    */
+  MOE_MXFP4_E2M1 = 3         /* E2M1 codes (packed) + E8M0 scales per 32   */
+} moe_format;
+
+/* Version of this ABI (MOE_ABI_VERSION of the built library). */
+int moe_abi_version(void);
+
+/* Static text for a status code. */
+const char* moe_status_str(int status);
+
+/* Message of the calling thread's most recent failed call ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * moe_route — router GEMM, sigmoid scores, selection bias, grouped top-k,
+ * normalized and scaled combine weights. (TE DeepSeekV3Layer page,
+ * Description, DeepSeekV3MoE item: "fused sigmoid router with aux-loss-free
+ * bias and grouped top-k".)
+ *
+ *   logits[t, e] = sum_h x[t, h] * w_router[e, h]      (fp32 accumulate)
+ *   s = sigmoid(logits) evaluated in fp64, rounded once to fp32
+ *   sel = fp32(s + bias)                               (selection only)
+ *   n_group > 1: experts form n_group contiguous groups; a group scores the
+ *     fp32 sum of its two largest sel values; the topk_group best groups are
+ *     kept (ties: lower group index), all other experts are excluded
+ *   topk_idx[t, 0..k-1]: the k largest remaining sel, descending (ties:
+ *     lower expert index)
+ *   topk_w[t, j] = fp32(fp32(s[idx] / S) * routed_scale), S the fp32 sum of
+ *     the k chosen s in slot order
+ *
+ * x          [T, H] in x_fmt (MOE_F32 or MOE_BF16); w_router [E, H] in the
+ *            same format. Both may be NULL when logits_in is given.
+ * bias       [E] fp32 selection bias (required).
+ * logits_in  optional [T, E] fp32: when non-NULL the GEMM is skipped and
+ *            selection starts from these logits.
+ * logits_out optional [T, E] fp32: receives the logits used.
+ * topk_idx   [T, k] int32 out; topk_w [T, k] fp32 out.
+ * Limits: 1 <= E <= 512, E % n_group == 0, E / n_group >= 2 when
+ * n_group > 1, 1 <= topk_group <= n_group, 1 <= k <= min(16,
+ * topk_group * E / n_group), H % 32 == 0 (bf16) when the GEMM runs.
+ * T == 0 is a no-op.
+ */
+int moe_route(const void* x, int x_fmt, const void* w_router, const float* bias,
+              const float* logits_in, int T, int H, int E, int n_group,
+              int topk_group, int k, float routed_scale, float* logits_out,
+              int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+/*
+ * moe_quantize_mx — MX block quantization of a [rows, K] tensor along K
+ * (TE DeepSeekV3Layer page, Performance section, "Where the time goes":
+ * MXFP8 quantization of the received rows and of dense GEMM inputs).
+ *
+ * Per row and per block of 32 consecutive elements v along K:
+ *   amax = max |v|; amax == 0 -> scale byte 0;
+ *   otherwise e = floor(log2 amax) - emax (emax 8 for E4M3, 2 for E2M1),
+ *   clamped to [-127, 127], scale byte = e + 127;
+ *   code = element-grid value nearest to v / 2^e, ties to the even code,
+ *   saturated to +-448 (E4M3) / +-6 (E2M1); the code keeps v's sign bit.
+ * in      [rows, K] in in_fmt (MOE_F32 or MOE_BF16); rows may be 0.
+ * out_fmt MOE_MXFP8_E4M3 or MOE_MXFP4_E2M1.
+ * codes   [rows, K] (E4M3) or [rows, K/2] (E2M1) bytes out.
+ * scales  [rows, K/32] bytes out.
+ * axis    must be 0 (blocks along K); other values return
+ *         MOE_ERR_UNSUPPORTED.
+ */
+int moe_quantize_mx(const void* in, int in_fmt, int64_t rows, int K, int axis,
+                    int out_fmt, uint8_t* codes, uint8_t* scales,
+                    hipStream_t stream);
+
+/*
+ * moe_permute_rows_bound — rows of the expert-major buffer:
+ * T*k + E*(align-1). Returns -1 for invalid arguments.
+ */
+int64_t moe_permute_rows_bound(int T, int k, int E, int align);
+
+/* moe_permute_workspace — scratch bytes moe_permute needs. */
+size_t moe_permute_workspace(int T, int k, int E);
+
+/*
+ * moe_permute — expert-major permutation (TE DeepSeekV3Layer page,
+ * Performance section, "Where the time goes": local permute "dup" into an
+ * expert-major staging buffer with zero-filled padding).
+ *
+ *   counts[e]   number of (t, j) with topk_idx[t, j] == e
+ *   offsets[e]  sum over e' < e of counts[e'] rounded up to `align`;
+ *               offsets[E] is the used row count
+ *   row_map[t, j]  offsets[e] + rank of (t, j) among the pairs of expert e
+ *               in (t, j) lexicographic order (a stable order)
+ *   src_row[r]  token of row r, or -1 for every padding row, for all
+ *               r < moe_permute_rows_bound(T, k, E, align)
+ *   rows_out[r] = rows_in[src_row[r]] (row_bytes opaque bytes), zero bytes
+ *               for padding rows; scales_out likewise with scale_bytes per
+ *               row (for MX rows). Zero bytes decode to 0 in every format.
+ * Built with a per-wave histogram, a column scan and a stable scatter; no
+ * atomics, so results are deterministic.
+ *
+ * topk_idx [T, k] int32 with values in [0, E) (values outside give
+ *          undefined maps; not checked on the device).
+ * rows_in / rows_out: optional (both NULL: maps only). row_bytes % 16 == 0.
+ * scales_in / scales_out: optional, scale_bytes > 0 when given.
+ * align in {1, 16, 32, 64, 128}. ws: moe_permute_workspace(T, k, E) bytes.
+ * counts [E], offsets [E+1], row_map [T, k], src_row [bound] int32 out.
+ */
+int moe_permute(const int32_t* topk_idx, int T, int k, int E, int align,
+                const void* rows_in, int64_t row_bytes, const void* scales_in,
+                int64_t scale_bytes, int32_t* counts, int32_t* offsets,
+                int32_t* row_map, int32_t* src_row, void* rows_out,
+                void* scales_out, void* ws, size_t ws_bytes,
+                hipStream_t stream);
+
+/*
+ * moe_grouped_mlp_workspace — scratch bytes of moe_grouped_mlp_fwd (the
+ * SwiGLU output h of every row, plus its MX scales for MX formats).
+ */
+size_t moe_grouped_mlp_workspace(int E, int H, int F, int64_t rows, int a_fmt,
+                                 int w_fmt);
+
+/*
+ * moe_grouped_mlp_fwd — per expert e, on rows [offsets[e], offsets[e+1]):
+ *   A = X_e . W1_e^T          [n_e, 2F], fp32 accumulate
+ *   h = silu(A[:, :F]) * A[:, F:]   (W1 rows [0, F) gate, [F, 2F) up)
+ *   (MX formats: h is MX-quantized per row along F before fc2)
+ *   y = h . W2_e^T            [n_e, H]
+ * (TE DeepSeekV3Layer page, Description: GroupedLinear -> ScaledSwiGLU ->
+ * GroupedLinear; the routing weight is applied later by moe_combine, which
+ * equals scaling h since fc2 has no bias. sglang page, Highlights: fc1's
+ * weight holds the w1 (gate) and w3 (up) halves.)
+ *
+ * a        activations: [rows, H] in a_fmt (MOE_F32, MOE_BF16, or MX codes)
+ *          indexed by row, or — when src_row is non-NULL — token rows
+ *          [T, H] gathered through src_row (row r reads a[src_row[r]]; a
+ *          row with src_row -1 produces zero h).
+ * a_scales MX scales of a ([rows or T, H/32]), NULL for F32/BF16.
+ * w1       [E, 2F, H] and w2 [E, H, F] in w_fmt, with MX scales
+ *          w1_scales [E, 2F, H/32], w2_scales [E, H, F/32] (NULL otherwise).
+ * Supported (a_fmt, w_fmt, y_fmt): (F32, F32, F32), (BF16, BF16, BF16),
+ *          (MXFP8, MXFP8, BF16), (MXFP4, MXFP4, BF16).
+ * offsets  [E+1] int32 device array (as moe_permute writes it);
+ *          offsets[E] <= rows.
+ * act_save optional [rows, 2F] bf16: receives A (for the backward).
+ * y        [rows, H] in y_fmt; rows outside every segment are not written.
+ * ws       moe_grouped_mlp_workspace(E, H, F, rows, a_fmt, w_fmt) bytes.
+ * Limits: 1 <= E <= 1024; BF16: H % 128 == 0, F % 64 == 0; MXFP8:
+ * H % 128 == 0, F % 128 == 0; MXFP4: H % 256 == 0, F % 256 == 0.
+ * A shared expert is a call with E = 1, offsets = {0, T} and src_row NULL.
+ */
+int moe_grouped_mlp_fwd(const void* a, const uint8_t* a_scales, int a_fmt,
+                        const int32_t* src_row, const void* w1,
+                        const uint8_t* w1_scales, const void* w2,
+                        const uint8_t* w2_scales, int w_fmt,
+                        const int32_t* offsets, int E, int H, int F,
+                        int64_t rows, void* act_save, void* y, int y_fmt,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_grouped_fc1_swiglu — the first half of moe_grouped_mlp_fwd on its
+ * own: per expert segment, A = X_e . W1_e^T and h = silu(A[:, :F]) * A[:, F:]
+ * (MX formats: h MX-quantized per row along F). Same argument meaning,
+ * formats and limits as moe_grouped_mlp_fwd; w_fmt must equal a_fmt.
+ * h        [rows, F] out in a_fmt (F32, BF16, or MX codes [rows, F] /
+ *          [rows, F/2]); h_scales [rows, F/32] out for MX (NULL otherwise).
+ *          Rows outside every segment are not written.
+ */
+int moe_grouped_fc1_swiglu(const void* a, const uint8_t* a_scales, int a_fmt,
+                           const int32_t* src_row, const void* w1,
+                           const uint8_t* w1_scales, int w_fmt,
+                           const int32_t* offsets, int E, int H, int F,
+                           int64_t rows, void* act_save, void* h,
+                           uint8_t* h_scales, hipStream_t stream);
+
+/*
+ * moe_grouped_fc2 — the second half: per expert segment y = h_e . W2_e^T.
+ * h        [rows, F] in h_fmt with h_scales for MX (as fc1 writes them).
+ * w2       [E, H, F] in w_fmt (== h_fmt) with w2_scales [E, H, F/32] for MX.
+ * y        [rows, H] in y_fmt (F32 for the F32 layer, BF16 otherwise).
+ */
+int moe_grouped_fc2(const void* h, const uint8_t* h_scales, int h_fmt,
+                    const void* w2, const uint8_t* w2_scales, int w_fmt,
+                    const int32_t* offsets, int E, int H, int F, int64_t rows,
+                    void* y, int y_fmt, hipStream_t stream);
+
+/*
+ * moe_combine — weighted top-k reduce back to token order (TE
+ * DeepSeekV3Layer page, Performance section, "Where the time goes": local
+ * permute "reduce"; Description: optional shared expert added).
+ *   out[t] = sum_{j<k} topk_w[t, j] * y[row_map[t, j]]  (+ shared[t])
+ * accumulated in fp32 in slot order j = 0..k-1.
+ * y [rows, H] in y_fmt (MOE_F32 or MOE_BF16); shared optional [T, H] in
+ * y_fmt; out [T, H] in out_fmt (MOE_F32 or MOE_BF16). H % 8 == 0.
+ */
+int moe_combine(const void* y, int y_fmt, const int32_t* row_map,
+                const float* topk_w, const void* shared, int T, int k, int H,
+                void* out, int out_fmt, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

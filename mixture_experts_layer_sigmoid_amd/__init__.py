@@ -1,0 +1,18 @@
+"""Sigmoid-routed MoE layer for AMD Instinct MI355X (gfx950).
+
+The layer (router with selection-only bias and grouped top-k, expert-major
+permute, grouped fc1 + SwiGLU, grouped fc2, weighted combine, MX
+quantization) runs in the hand-written HIP library libmoe_mi355x.so behind
+the C ABI of include/moe_mi355x.h. This package is its Python binding: the
+functions in `_lib` carry the C names and only marshal arguments; `layer`
+strings them into a forward pass. There is no CPU fallback: every binding call
+loads the built library and raises when it is missing.
+"""
+from ._lib import (  # noqa: F401
+    load, MoEError, MOE_F32, MOE_BF16, MOE_MXFP8_E4M3, MOE_MXFP4_E2M1,
+    moe_abi_version, moe_route, moe_quantize_mx, moe_permute_rows_bound,
+    moe_permute_workspace, moe_permute, moe_grouped_mlp_workspace,
+    moe_grouped_mlp_fwd, moe_grouped_fc1_swiglu, moe_grouped_fc2, moe_combine,
+    SIGNATURES, LIB_PATH,
+)
+from .layer import MoEForward, ExpertWeights, quantize_mx, FMT  # noqa: F401

@@ -1,0 +1,152 @@
+"""ctypes binding of libmoe_mi355x.so (include/moe_mi355x.h).
+
+Argument marshalling only: every function takes torch tensors (device
+memory) or None, passes their data pointers and the current HIP stream to
+the C entry point of the same name, and raises MoEError on a non-zero
+status. Nothing here computes any part of the layer.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
+
+MOE_F32, MOE_BF16, MOE_MXFP8_E4M3, MOE_MXFP4_E2M1 = 0, 1, 2, 3
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
+          -3: "MOE_ERR_ALIGNMENT", -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
+
+# exported entry points and their ctypes signatures
+_P, _I, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "moe_abi_version": (_I, []),
+    "moe_status_str": (ctypes.c_char_p, [_I]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_route": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P]),
+    "moe_quantize_mx": (_I, [_P, _I, _I64, _I, _I, _I, _P, _P, _P]),
+    "moe_permute_rows_bound": (_I64, [_I, _I, _I, _I]),
+    "moe_permute_workspace": (_SZ, [_I, _I, _I]),
+    "moe_permute": (_I, [_P, _I, _I, _I, _I, _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_grouped_mlp_workspace": (_SZ, [_I, _I, _I, _I64, _I, _I]),
+    "moe_grouped_mlp_fwd": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _P,
+                                 _I, _P, _SZ, _P]),
+    "moe_grouped_fc1_swiglu": (_I, [_P, _P, _I, _P, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _P, _P, _P]),
+    "moe_grouped_fc2": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _I, _P]),
+    "moe_combine": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _P, _I, _P]),
+}
+
+_lib = None
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} -> {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m mixture_experts_layer_sigmoid_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(name: str, status: int):
+    if status != 0:
+        raise MoEError(name, status, load().moe_last_error().decode())
+
+
+def fmt_of_dtype(t) -> int:
+    import torch
+    return {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}[t.dtype]
+
+
+# -- thin wrappers, same names and argument order as the C ABI -------------
+def moe_abi_version() -> int:
+    return load().moe_abi_version()
+
+
+def moe_route(x, x_fmt, w_router, bias, logits_in, T, H, E, n_group, topk_group, k,
+              routed_scale, logits_out, topk_idx, topk_w, stream=None):
+    _check("moe_route", load().moe_route(
+        _ptr(x), x_fmt, _ptr(w_router), _ptr(bias), _ptr(logits_in), T, H, E, n_group,
+        topk_group, k, float(routed_scale), _ptr(logits_out), _ptr(topk_idx), _ptr(topk_w),
+        _stream(stream)))
+
+
+def moe_quantize_mx(inp, in_fmt, rows, K, axis, out_fmt, codes, scales, stream=None):
+    _check("moe_quantize_mx", load().moe_quantize_mx(
+        _ptr(inp), in_fmt, rows, K, axis, out_fmt, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def moe_permute_rows_bound(T, k, E, align) -> int:
+    return load().moe_permute_rows_bound(T, k, E, align)
+
+
+def moe_permute_workspace(T, k, E) -> int:
+    return load().moe_permute_workspace(T, k, E)
+
+
+def moe_permute(topk_idx, T, k, E, align, rows_in, row_bytes, scales_in, scale_bytes, counts,
+                offsets, row_map, src_row, rows_out, scales_out, ws, stream=None):
+    _check("moe_permute", load().moe_permute(
+        _ptr(topk_idx), T, k, E, align, _ptr(rows_in), row_bytes, _ptr(scales_in), scale_bytes,
+        _ptr(counts), _ptr(offsets), _ptr(row_map), _ptr(src_row), _ptr(rows_out),
+        _ptr(scales_out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def moe_grouped_mlp_workspace(E, H, F, rows, a_fmt, w_fmt) -> int:
+    return load().moe_grouped_mlp_workspace(E, H, F, rows, a_fmt, w_fmt)
+
+
+def moe_grouped_mlp_fwd(a, a_scales, a_fmt, src_row, w1, w1_scales, w2, w2_scales, w_fmt,
+                        offsets, E, H, F, rows, act_save, y, y_fmt, ws, stream=None):
+    _check("moe_grouped_mlp_fwd", load().moe_grouped_mlp_fwd(
+        _ptr(a), _ptr(a_scales), a_fmt, _ptr(src_row), _ptr(w1), _ptr(w1_scales), _ptr(w2),
+        _ptr(w2_scales), w_fmt, _ptr(offsets), E, H, F, rows, _ptr(act_save), _ptr(y), y_fmt,
+        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_grouped_fc1_swiglu(a, a_scales, a_fmt, src_row, w1, w1_scales, w_fmt, offsets, E, H, F,
+                           rows, act_save, h, h_scales, stream=None):
+    _check("moe_grouped_fc1_swiglu", load().moe_grouped_fc1_swiglu(
+        _ptr(a), _ptr(a_scales), a_fmt, _ptr(src_row), _ptr(w1), _ptr(w1_scales), w_fmt,
+        _ptr(offsets), E, H, F, rows, _ptr(act_save), _ptr(h), _ptr(h_scales), _stream(stream)))
+
+
+def moe_grouped_fc2(h, h_scales, h_fmt, w2, w2_scales, w_fmt, offsets, E, H, F, rows, y, y_fmt,
+                    stream=None):
+    _check("moe_grouped_fc2", load().moe_grouped_fc2(
+        _ptr(h), _ptr(h_scales), h_fmt, _ptr(w2), _ptr(w2_scales), w_fmt, _ptr(offsets), E, H, F,
+        rows, _ptr(y), y_fmt, _stream(stream)))
+
+
+def moe_combine(y, y_fmt, row_map, topk_w, shared, T, k, H, out, out_fmt, stream=None):
+    _check("moe_combine", load().moe_combine(
+        _ptr(y), y_fmt, _ptr(row_map), _ptr(topk_w), _ptr(shared), T, k, H, _ptr(out), out_fmt,
+        _stream(stream)))

@@ -1,0 +1,798 @@
+// moe_grouped_mlp_fwd: grouped fc1 + SwiGLU (+ MX quantization of h), then
+// grouped fc2, over expert-major row segments.
+//
+// Page "[PyTorch] DeepSeekV3Layer: full MoE transformer layer (MLA +
+// DeepSeek MoE)": Description (experts as GroupedLinear -> ScaledSwiGLU ->
+// GroupedLinear, fused into one grouped MLP) and Performance section ("Where
+// the time goes": fused grouped MLP, fc1+SwiGLU fwd and fc2 fwd, MXFP8).
+// Page "Mistral Large 3 NVFP4 TRTLLM MoE support", Highlights: fc1's weight
+// holds the w1 (gate) and w3 (up) halves; here rows [0, F) gate, [F, 2F) up.
+//
+// Kernel design (gfx950):
+//   * One persistent kernel per GEMM. A tile is (expert e, row block m,
+//     column block n): up to MMAX rows of the expert's segment against 128
+//     weight rows. Every workgroup builds the tile list from `offsets` in
+//     LDS (m-tiles per expert, prefix sum), so no host round trip is needed.
+//     Tiles are ordered expert-major, then column block, then row block, and
+//     the list is cut into 8 contiguous chunks, one per XCD (workgroups are
+//     dispatched to XCDs round-robin by index). The workgroups of one XCD
+//     thus run consecutive tiles together: the column blocks of one expert
+//     share its activation rows in that XCD's L2, and the row blocks of one
+//     weight tile (experts with more than MMAX rows) run side by side, so
+//     each weight byte comes from HBM once.
+//   * Both operands stream into LDS with direct global->LDS 16-byte loads
+//     (no register staging), STAGES deep. Each stage holds 128 bytes of K
+//     per row: 64 bf16, 128 E4M3 or 256 E2M1 values. Rows are stored with
+//     their eight 16-byte chunks XOR-swizzled by (row % 8), which keeps the
+//     MFMA operand reads (8 rows x 16 bytes per lane group) free of bank
+//     conflicts. MX block scales (one byte per 32 values) get their own
+//     small LDS arrays.
+//   * 4 wavefronts; wavefront w owns 32 weight rows (one 32x32 MFMA column
+//     block) and every row block of the tile, so each weight element is read
+//     from LDS once per row block and all four SIMDs stay busy whatever the
+//     row count. MFMA: 32x32x16 bf16, or the block-scaled 32x32x64 f8f6f4
+//     with E4M3 / E2M1 operands and E8M0 scales.
+//   * fc1 tiles pair 64 gate columns with the matching 64 up columns: wave w
+//     holds gate columns [16w, 16w+16) in its MFMA columns 0..15 and the
+//     same up columns in 16..31, so SwiGLU needs one lane exchange. h goes
+//     through LDS to coalesced bf16 stores or to the MX encoder (whole
+//     32-column blocks per row).
+//   * fc2 tiles store y (bf16) through LDS as full 16-byte row chunks.
+#include "common.h"
+#include "mx_codec.h"
+
+#include <algorithm>
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowBytes = 128;   // bytes of K per row per stage
+constexpr int kBRows = 128;      // weight rows per tile
+constexpr int kMaxGroups = 1024;
+
+enum { OP_BF16 = 0, OP_FP8 = 1, OP_FP4 = 2 };
+enum { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
+
+template <int OP>
+struct Op;
+template <>
+struct Op<OP_BF16> {
+  static constexpr int kScaleBytes = 0;  // per row per stage
+  static constexpr int kSub = 4;         // MFMA k-steps per stage
+};
+template <>
+struct Op<OP_FP8> {
+  static constexpr int kScaleBytes = 4;
+  static constexpr int kSub = 2;
+};
+template <>
+struct Op<OP_FP4> {
+  static constexpr int kScaleBytes = 8;
+  static constexpr int kSub = 4;
+};
+
+struct Args {
+  const uint8_t* a;        // activation rows (or token rows with gather)
+  int64_t a_row_bytes;
+  const uint8_t* a_sc;     // MX scales of a
+  int64_t a_sc_row_bytes;
+  const int32_t* gather;   // optional row -> source row (-1: padding)
+  const uint8_t* b;        // weights of expert 0
+  int64_t b_exp_bytes;
+  int64_t b_row_bytes;
+  const uint8_t* b_sc;
+  int64_t b_sc_exp_bytes;
+  int64_t b_sc_row_bytes;
+  int up_row;              // fc1: first row of the up half (F)
+  const int32_t* offsets;  // [E+1]
+  int E;
+  int64_t rows;            // rows of a / out (bound)
+  int n_blocks;            // column blocks per expert
+  int k_stages;            // K bytes / 128
+  uint8_t* out;
+  int64_t out_row_bytes;
+  uint8_t* out_sc;
+  int64_t out_sc_row_bytes;
+  uint16_t* act_save;      // optional [rows, 2F] bf16 (fc1 only)
+  int act_cols;            // 2F
+};
+
+template <int MMAX, int STAGES, int OP>
+struct Smem {
+  static constexpr int kA = MMAX * kRowBytes;
+  static constexpr int kB = kBRows * kRowBytes;
+  static constexpr int kASc = MMAX * Op<OP>::kScaleBytes;
+  static constexpr int kBSc = kBRows * Op<OP>::kScaleBytes;
+  static constexpr int kStage = kA + kB + kASc + kBSc;
+  static constexpr int kSched = (kMaxGroups + 1) * 4 + MMAX * 4 + 16;
+  static constexpr int kTotal = STAGES * kStage + kSched;
+};
+
+__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)lds, 4, 0, 0);
+}
+
+// Wait until at most n vector-memory operations of this wave are in flight.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define MOE_W(N) case N: wait_vmcnt<N>(); break;
+    MOE_W(0) MOE_W(1) MOE_W(2) MOE_W(3) MOE_W(4) MOE_W(5) MOE_W(6) MOE_W(7)
+    MOE_W(8) MOE_W(9) MOE_W(10) MOE_W(11) MOE_W(12) MOE_W(13) MOE_W(14) MOE_W(15)
+    MOE_W(16) MOE_W(17) MOE_W(18) MOE_W(19) MOE_W(20) MOE_W(21) MOE_W(22) MOE_W(23)
+    MOE_W(24) MOE_W(25) MOE_W(26) MOE_W(27) MOE_W(28) MOE_W(29) MOE_W(30) MOE_W(31)
+    MOE_W(32) MOE_W(33) MOE_W(34) MOE_W(35) MOE_W(36) MOE_W(37) MOE_W(38) MOE_W(39)
+    MOE_W(40) MOE_W(41) MOE_W(42) MOE_W(43) MOE_W(44) MOE_W(45) MOE_W(46) MOE_W(47)
+    MOE_W(48) MOE_W(49) MOE_W(50) MOE_W(51) MOE_W(52) MOE_W(53) MOE_W(54) MOE_W(55)
+    MOE_W(56) MOE_W(57) MOE_W(58) MOE_W(59) MOE_W(60) MOE_W(61) MOE_W(62)
+#undef MOE_W
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+// byte offset of 16-byte chunk c of row r inside a [rows][128 B] stage tile
+__device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float sig = 1.f / (1.f + expf(-g));
+  return g * sig * u;
+}
+
+template <int MMAX, int STAGES, int OP, int EPI, int OUTF>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
+  using S = Smem<MMAX, STAGES, OP>;
+  constexpr int kRB = MMAX / 32;        // row blocks per tile
+  constexpr int kSB = Op<OP>::kScaleBytes;
+  constexpr int kAIns = MMAX / 32;      // A load instructions per wave per stage (8 rows each)
+  constexpr int kBIns = kBRows / 32;    // B load instructions per wave per stage
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S::kTotal];
+  int32_t* s_mt = reinterpret_cast<int32_t*>(smem + STAGES * S::kStage);   // [E+1] m-tile prefix
+  int32_t* s_src = s_mt + (kMaxGroups + 1);                                  // [MMAX] source rows
+  int32_t* s_tot = s_src + MMAX;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = p.E;
+
+  // ---- tile list: m-tiles per expert, inclusive prefix in s_mt[1..E] ----
+  {
+    const int per = (E + kThreads - 1) / kThreads;
+    const int lo = tid * per, hi = min(E, lo + per);
+    int s = 0;
+    for (int e = lo; e < hi; ++e) {
+      int n_e = min(p.offsets[e + 1], (int)p.rows) - p.offsets[e];
+      n_e = n_e < 0 ? 0 : n_e;
+      const int mt = (n_e + MMAX - 1) / MMAX;
+      s_mt[e + 1] = mt;
+      s += mt;
+    }
+    __syncthreads();
+    __shared__ int32_t part[kThreads];
+    part[tid] = s;
+    __syncthreads();
+    for (int d = 1; d < kThreads; d <<= 1) {
+      const int v = tid >= d ? part[tid - d] : 0;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
+    }
+    int run = tid > 0 ? part[tid - 1] : 0;
+    for (int e = lo; e < hi; ++e) {
+      run += s_mt[e + 1];
+      s_mt[e + 1] = run;
+    }
+    if (tid == 0) {
+      s_mt[0] = 0;
+      s_tot[0] = part[kThreads - 1];
+    }
+    __syncthreads();
+  }
+  const int64_t total_tiles = static_cast<int64_t>(s_tot[0]) * p.n_blocks;
+  const XcdSlot xs = xcd_slot();
+  const int64_t c_lo = total_tiles * xs.xcd / kNumXcd;
+  const int64_t c_hi = total_tiles * (xs.xcd + 1) / kNumXcd;
+
+  for (int64_t t = c_lo + xs.slot; t < c_hi; t += xs.nslots) {
+    // ---- decode the tile ----
+    int e;
+    {
+      // find e with s_mt[e] * nb <= t < s_mt[e+1] * nb
+      int lo = 0, hi = E;  // invariant: s_mt[lo]*nb <= t < s_mt[hi]*nb
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (static_cast<int64_t>(s_mt[mid]) * p.n_blocks <= t) lo = mid;
+        else hi = mid;
+      }
+      e = lo;
+    }
+    const int mtiles = s_mt[e + 1] - s_mt[e];
+    const int64_t local = t - static_cast<int64_t>(s_mt[e]) * p.n_blocks;
+    const int nblk = static_cast<int>(local / mtiles);
+    const int mblk = static_cast<int>(local % mtiles);
+    const int seg_lo = p.offsets[e];
+    const int n_e = min(p.offsets[e + 1], (int)p.rows) - seg_lo;
+    const int rows_per = (n_e + mtiles - 1) / mtiles;  // balanced split, <= MMAX
+    const int row0 = seg_lo + mblk * rows_per;
+    const int nrows = min(rows_per, n_e - mblk * rows_per);
+    if (nrows <= 0) continue;  // uniform across the workgroup
+    const int nrb = (nrows + 31) >> 5;
+
+    // ---- per-lane global sources of this tile's loads ----
+    const uint8_t* a_src[kAIns];
+#pragma unroll
+    for (int i = 0; i < kAIns; ++i) {
+      const int r = 8 * (wave + 4 * i) + (lane >> 3);
+      int src = row0 + min(r, nrows - 1);
+      if (p.gather) {
+        src = p.gather[src];
+        if (src < 0) src = 0;  // padding row: loads any valid row, h is zeroed
+      }
+      a_src[i] = p.a + static_cast<int64_t>(src) * p.a_row_bytes + (((lane & 7) ^ (r & 7)) << 4);
+    }
+    if (p.gather && EPI == EPI_SWIGLU) {
+      for (int r = tid; r < MMAX; r += kThreads) s_src[r] = r < nrows ? p.gather[row0 + r] : 0;
+    }
+    const uint8_t* b_src[kBIns];
+    const uint8_t* bexp = p.b + static_cast<int64_t>(e) * p.b_exp_bytes;
+#pragma unroll
+    for (int i = 0; i < kBIns; ++i) {
+      const int br = 8 * (wave + 4 * i) + (lane >> 3);
+      int wrow;
+      if (EPI == EPI_SWIGLU) {
+        const int w = br >> 5, within = br & 31;
+        wrow = nblk * 64 + 16 * w + (within & 15) + (within >= 16 ? p.up_row : 0);
+      } else {
+        wrow = nblk * kBRows + br;
+      }
+      b_src[i] = bexp + static_cast<int64_t>(wrow) * p.b_row_bytes + (((lane & 7) ^ (br & 7)) << 4);
+    }
+    // ---- MX scale sources: kSB bytes (kSB/4 dwords) per row per stage; one
+    // 4-byte direct load per lane, 64/(kSB/4) rows per instruction ----
+    constexpr int kDpr = kSB > 0 ? kSB / 4 : 1;
+    constexpr int kScRows = 64 / kDpr;                 // rows per scale instruction
+    constexpr int kAScIns = kSB > 0 ? MMAX / kScRows : 1;
+    constexpr int kBScIns = kSB > 0 ? kBRows / kScRows : 1;
+    const uint8_t* asc_src[(kAScIns + 3) / 4];
+    const uint8_t* bsc_src[(kBScIns + 3) / 4];
+    if (kSB > 0) {
+#pragma unroll
+      for (int q = 0; q < (kAScIns + 3) / 4; ++q) {
+        const int j = wave + 4 * q;
+        const int r = min(j * kScRows + lane / kDpr, nrows - 1);
+        int src = row0 + r;
+        if (p.gather) {
+          src = p.gather[src];
+          if (src < 0) src = 0;
+        }
+        asc_src[q] = p.a_sc + static_cast<int64_t>(src) * p.a_sc_row_bytes + (lane % kDpr) * 4;
+      }
+      const uint8_t* bsexp = p.b_sc + static_cast<int64_t>(e) * p.b_sc_exp_bytes;
+#pragma unroll
+      for (int q = 0; q < (kBScIns + 3) / 4; ++q) {
+        const int r = (wave + 4 * q) * kScRows + lane / kDpr;
+        int wrow;
+        if (EPI == EPI_SWIGLU) {
+          const int w = r >> 5, within = r & 31;
+          wrow = nblk * 64 + 16 * w + (within & 15) + (within >= 16 ? p.up_row : 0);
+        } else {
+          wrow = nblk * kBRows + r;
+        }
+        bsc_src[q] = bsexp + static_cast<int64_t>(wrow) * p.b_sc_row_bytes + (lane % kDpr) * 4;
+      }
+    }
+
+    f32x16_t acc[kRB];
+#pragma unroll
+    for (int i = 0; i < kRB; ++i) acc[i] = f32x16_t{};
+
+    // vector-memory instructions this wave issues per stage: A instruction i
+    // covers rows [8*(wave+4i), +8) and is issued when that range starts
+    // below nrows; scale instruction q covers rows [(wave+4q)*kScRows, ...)
+    int my_a = 0;
+#pragma unroll
+    for (int i = 0; i < kAIns; ++i) my_a += (8 * (wave + 4 * i) < nrows) ? 1 : 0;
+    int my_asc = 0, my_bsc = 0;
+    if (kSB > 0) {
+#pragma unroll
+      for (int q = 0; q < (kAScIns + 3) / 4; ++q)
+        my_asc += ((wave + 4 * q) < kAScIns && (wave + 4 * q) * kScRows < nrows) ? 1 : 0;
+#pragma unroll
+      for (int q = 0; q < (kBScIns + 3) / 4; ++q) my_bsc += ((wave + 4 * q) < kBScIns) ? 1 : 0;
+    }
+    const int per_stage = my_a + kBIns + my_asc + my_bsc;
+
+    auto issue = [&](int kt) {
+      uint8_t* st = smem + (kt % STAGES) * S::kStage;
+      const int64_t kb = static_cast<int64_t>(kt) * kRowBytes;
+#pragma unroll
+      for (int i = 0; i < kAIns; ++i)
+        if (8 * (wave + 4 * i) < nrows) lds_load16(a_src[i] + kb, st + (wave + 4 * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < kBIns; ++i) lds_load16(b_src[i] + kb, st + S::kA + (wave + 4 * i) * 1024);
+      if (kSB > 0) {
+        const int64_t ks = static_cast<int64_t>(kt) * kSB;
+#pragma unroll
+        for (int q = 0; q < (kAScIns + 3) / 4; ++q) {
+          const int j = wave + 4 * q;
+          if (j < kAScIns && j * kScRows < nrows) lds_load4(asc_src[q] + ks, st + S::kA + S::kB + j * 256);
+        }
+#pragma unroll
+        for (int q = 0; q < (kBScIns + 3) / 4; ++q) {
+          const int j = wave + 4 * q;
+          if (j < kBScIns) lds_load4(bsc_src[q] + ks, st + S::kA + S::kB + S::kASc + j * 256);
+        }
+      }
+    };
+
+    const int KT = p.k_stages;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < KT) issue(s);
+
+    for (int kt = 0; kt < KT; ++kt) {
+      // stages issued after kt that may stay in flight
+      const int ahead = min(STAGES - 2, KT - 1 - kt);
+      wait_vm(ahead * per_stage);
+      __syncthreads();
+      if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+      const uint8_t* st = smem + (kt % STAGES) * S::kStage;
+      const uint8_t* sa = st;
+      const uint8_t* sb = st + S::kA;
+      const int brow = 32 * wave + (lane & 31);
+      const int g = lane >> 5;
+      if constexpr (OP == OP_BF16) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8_t bop = *reinterpret_cast<const bf16x8_t*>(sb + swz(brow, 2 * s + g));
+#pragma unroll
+          for (int mb = 0; mb < kRB; ++mb) {
+            if (mb < nrb) {
+              const int ar = mb * 32 + (lane & 31);
+              const bf16x8_t aop = *reinterpret_cast<const bf16x8_t*>(sa + swz(ar, 2 * s + g));
+              acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, acc[mb], 0, 0, 0);
+            }
+          }
+        }
+      } else {
+        const uint32_t* sasc = reinterpret_cast<const uint32_t*>(st + S::kA + S::kB);
+        const uint32_t* sbsc = reinterpret_cast<const uint32_t*>(st + S::kA + S::kB + S::kASc);
+        constexpr int dpr = kSB > 0 ? kSB / 4 : 1;
+        uint32_t bsc[dpr];
+#pragma unroll
+        for (int d = 0; d < dpr; ++d) bsc[d] = sbsc[brow * dpr + d];
+#pragma unroll
+        for (int s = 0; s < Op<OP>::kSub; ++s) {
+          i32x8_t bop;
+          if (OP == OP_FP8) {
+            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sb + swz(brow, 4 * s + g));
+            const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sb + swz(brow, 4 * s + 2 + g));
+            bop = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          } else {
+            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sb + swz(brow, 2 * s + g));
+            bop = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+          }
+          // this k-step covers blocks 2s and 2s+1 of the stage; lane group g
+          // supplies the scale of block 2s+g in the low byte of its operand
+          const int blk = 2 * s + g;
+          const int bw = blk >> 2, bsh = 8 * (blk & 3);
+#pragma unroll
+          for (int mb = 0; mb < kRB; ++mb) {
+            if (mb < nrb) {
+              const int ar = mb * 32 + (lane & 31);
+              i32x8_t aop;
+              if (OP == OP_FP8) {
+                const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz(ar, 4 * s + g));
+                const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sa + swz(ar, 4 * s + 2 + g));
+                aop = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+              } else {
+                const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz(ar, 2 * s + g));
+                aop = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+              }
+              const int asc = static_cast<int>((sasc[ar * dpr + bw] >> bsh) & 0xFFu);
+              const int bs = static_cast<int>((bsc[bw] >> bsh) & 0xFFu);
+              if (OP == OP_FP8)
+                acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc[mb], 0, 0, 0, asc, 0, bs);
+              else
+                acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc[mb], 4, 4, 0, asc, 0, bs);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();  // all waves done with the stage buffers
+
+    // ---- epilogue: accumulators -> LDS tile [rows][kCs] fp32, then a
+    // row-major pass (SwiGLU / act save / MX encode / bf16) with 16-byte
+    // global stores ----
+    // C layout of a 32x32 MFMA: lane l, element r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
+    constexpr int kCs = kBRows + 4;  // padded row stride (floats)
+    static_assert(MMAX * kCs * 4 <= STAGES * S::kStage, "epilogue tile must fit the stage buffers");
+    float* cs = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int mb = 0; mb < kRB; ++mb) {
+      if (mb < nrb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          cs[row * kCs + 32 * wave + (lane & 31)] = acc[mb][r];
+        }
+      }
+    }
+    __syncthreads();
+    if constexpr (EPI == EPI_SWIGLU) {
+      // h column c (0..63) of this tile: gate at tile column 32*(c/16) + c%16,
+      // up at the same + 16
+      if constexpr (OUTF == MOE_BF16) {
+        for (int i = tid; i < nrows * 8; i += kThreads) {
+          const int row = i >> 3, c0 = (i & 7) * 8;
+          const bool zero = p.gather && s_src[row] < 0;
+          const float* gp = cs + row * kCs + 32 * (c0 >> 4) + (c0 & 15);
+          const float* up = gp + 16;
+          float h[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) h[q] = zero ? 0.f : silu_mul(gp[q], up[q]);
+          const int64_t grow = row0 + row;
+          *reinterpret_cast<u32x4_t*>(p.out + grow * p.out_row_bytes + (nblk * 64 + c0) * 2) =
+              u32x4_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                      pack_bf16x2(h[6], h[7])};
+          if (p.act_save) {
+            uint16_t* ar = p.act_save + grow * p.act_cols + nblk * 64 + c0;
+            *reinterpret_cast<u32x4_t*>(ar) =
+                u32x4_t{pack_bf16x2(gp[0], gp[1]), pack_bf16x2(gp[2], gp[3]),
+                        pack_bf16x2(gp[4], gp[5]), pack_bf16x2(gp[6], gp[7])};
+            *reinterpret_cast<u32x4_t*>(ar + p.up_row) =
+                u32x4_t{pack_bf16x2(up[0], up[1]), pack_bf16x2(up[2], up[3]),
+                        pack_bf16x2(up[4], up[5]), pack_bf16x2(up[6], up[7])};
+          }
+        }
+      } else {
+        constexpr bool fp4 = OUTF == MOE_MXFP4_E2M1;
+        for (int i = tid; i < nrows * 2; i += kThreads) {
+          const int row = i >> 1, blk = i & 1;
+          const bool zero = p.gather && s_src[row] < 0;
+          float v[32];
+#pragma unroll
+          for (int q = 0; q < 32; ++q) {
+            const int c = blk * 32 + q;
+            const float* gp = cs + row * kCs + 32 * (c >> 4) + (c & 15);
+            v[q] = zero ? 0.f : silu_mul(gp[0], gp[16]);
+          }
+          uint32_t words[8];
+          const uint32_t sb = mx_encode_block<fp4>(v, words);
+          const int64_t r = row0 + row;
+          if (fp4) {
+            *reinterpret_cast<u32x4_t*>(p.out + r * p.out_row_bytes + (nblk * 2 + blk) * 16) =
+                u32x4_t{words[0], words[1], words[2], words[3]};
+          } else {
+            u32x4_t* o = reinterpret_cast<u32x4_t*>(p.out + r * p.out_row_bytes + (nblk * 2 + blk) * 32);
+            o[0] = u32x4_t{words[0], words[1], words[2], words[3]};
+            o[1] = u32x4_t{words[4], words[5], words[6], words[7]};
+          }
+          p.out_sc[r * p.out_sc_row_bytes + nblk * 2 + blk] = static_cast<uint8_t>(sb);
+          if (p.act_save) {
+            for (int q = 0; q < 32; q += 8) {
+              const int c = blk * 32 + q;
+              const float* gp = cs + row * kCs + 32 * (c >> 4) + (c & 15);
+              uint16_t* ar = p.act_save + r * p.act_cols + nblk * 64 + c;
+              *reinterpret_cast<u32x4_t*>(ar) =
+                  u32x4_t{pack_bf16x2(gp[0], gp[1]), pack_bf16x2(gp[2], gp[3]),
+                          pack_bf16x2(gp[4], gp[5]), pack_bf16x2(gp[6], gp[7])};
+              *reinterpret_cast<u32x4_t*>(ar + p.up_row) =
+                  u32x4_t{pack_bf16x2(gp[16], gp[17]), pack_bf16x2(gp[18], gp[19]),
+                          pack_bf16x2(gp[20], gp[21]), pack_bf16x2(gp[22], gp[23])};
+            }
+          }
+        }
+      }
+    } else {
+      for (int i = tid; i < nrows * 16; i += kThreads) {
+        const int row = i >> 4, c0 = (i & 15) * 8;
+        const float* v = cs + row * kCs + c0;
+        *reinterpret_cast<u32x4_t*>(p.out + static_cast<int64_t>(row0 + row) * p.out_row_bytes +
+                                    (nblk * kBRows + c0) * 2) =
+            u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7])};
+      }
+    }
+    __syncthreads();  // LDS reused by the next tile
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path (the small fp32 layer): plain FMA, one thread per output.
+__global__ __launch_bounds__(256) void fc1_swiglu_f32_kernel(const float* __restrict__ a,
+                                                             const int32_t* __restrict__ gather,
+                                                             const float* __restrict__ w1,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int E, int H, int F, int64_t rows,
+                                                             float* __restrict__ h,
+                                                             uint16_t* __restrict__ act_save) {
+  const int64_t used = min(static_cast<int64_t>(offsets[E]), rows);
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < used * F; i += 256ll * gridDim.x) {
+    const int64_t r = i / F;
+    const int c = static_cast<int>(i % F);
+    int lo = 0, hi = E;  // expert of row r: offsets[lo] <= r < offsets[lo+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (offsets[mid] <= r) lo = mid;
+      else hi = mid;
+    }
+    int64_t src = r;
+    if (gather) src = gather[r];
+    if (src < 0) {
+      h[r * F + c] = 0.f;
+      continue;
+    }
+    const float* x = a + src * H;
+    const float* wg = w1 + (static_cast<int64_t>(lo) * 2 * F + c) * H;
+    const float* wu = wg + static_cast<int64_t>(F) * H;
+    float g = 0.f, u = 0.f;
+    for (int k = 0; k < H; ++k) {
+      g = fmaf(x[k], wg[k], g);
+      u = fmaf(x[k], wu[k], u);
+    }
+    if (act_save) {
+      act_save[r * 2 * F + c] = f32_to_bf16_bits(g);
+      act_save[r * 2 * F + F + c] = f32_to_bf16_bits(u);
+    }
+    h[r * F + c] = silu_mul(g, u);
+  }
+}
+
+__global__ __launch_bounds__(256) void fc2_f32_kernel(const float* __restrict__ h,
+                                                      const float* __restrict__ w2,
+                                                      const int32_t* __restrict__ offsets, int E,
+                                                      int H, int F, int64_t rows,
+                                                      float* __restrict__ y) {
+  const int64_t used = min(static_cast<int64_t>(offsets[E]), rows);
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < used * H; i += 256ll * gridDim.x) {
+    const int64_t r = i / H;
+    const int c = static_cast<int>(i % H);
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (offsets[mid] <= r) lo = mid;
+      else hi = mid;
+    }
+    const float* hr = h + r * F;
+    const float* w = w2 + (static_cast<int64_t>(lo) * H + c) * F;
+    float acc = 0.f;
+    for (int k = 0; k < F; ++k) acc = fmaf(hr[k], w[k], acc);
+    y[r * H + c] = acc;
+  }
+}
+
+template <int MMAX, int STAGES, int OP, int EPI, int OUTF>
+int launch_gemm(const Args& a, hipStream_t stream) {
+  const int grid = kNumCu;  // one workgroup per CU (LDS-bound), persistent
+  hipLaunchKernelGGL((grouped_gemm_kernel<MMAX, STAGES, OP, EPI, OUTF>), dim3(grid),
+                     dim3(kThreads), 0, stream, a);
+  return check_launch("moe_grouped_mlp_fwd");
+}
+
+int elem_bits(int fmt) {
+  switch (fmt) {
+    case MOE_F32: return 32;
+    case MOE_BF16: return 16;
+    case MOE_MXFP8_E4M3: return 8;
+    case MOE_MXFP4_E2M1: return 4;
+    default: return 0;
+  }
+}
+
+static size_t h_bytes_of(int64_t rows, int F, int fmt) {
+  const size_t h = static_cast<size_t>(rows) * F * elem_bits(fmt) / 8;
+  return (h + 255) & ~static_cast<size_t>(255);
+}
+
+static bool is_mx(int f) { return f == MOE_MXFP8_E4M3 || f == MOE_MXFP4_E2M1; }
+
+// Shared argument checks of the grouped calls; `h_fmt` is the format of the
+// SwiGLU output (the activation format of the layer), `y_fmt` that of y.
+static int check_formats(const char* fn, int a_fmt, int w_fmt, int y_fmt, int H, int F) {
+  const bool f32 = a_fmt == MOE_F32 && w_fmt == MOE_F32 && y_fmt == MOE_F32;
+  const bool bf16 = a_fmt == MOE_BF16 && w_fmt == MOE_BF16 && y_fmt == MOE_BF16;
+  const bool fp8 = a_fmt == MOE_MXFP8_E4M3 && w_fmt == MOE_MXFP8_E4M3 && y_fmt == MOE_BF16;
+  const bool fp4 = a_fmt == MOE_MXFP4_E2M1 && w_fmt == MOE_MXFP4_E2M1 && y_fmt == MOE_BF16;
+  std::string f(fn);
+  MOE_REQUIRE(f32 || bf16 || fp8 || fp4, MOE_ERR_UNSUPPORTED,
+              f + ": supported (a, w, y) formats are (F32,F32,F32), (BF16,BF16,BF16), "
+                  "(MXFP8,MXFP8,BF16), (MXFP4,MXFP4,BF16)");
+  if (bf16)
+    MOE_REQUIRE(H % 128 == 0 && F % 64 == 0, MOE_ERR_INVALID_ARG,
+                f + ": bf16 needs H % 128 == 0 and F % 64 == 0");
+  if (fp8)
+    MOE_REQUIRE(H % 128 == 0 && F % 128 == 0, MOE_ERR_INVALID_ARG,
+                f + ": MXFP8 needs H % 128 == 0 and F % 128 == 0");
+  if (fp4)
+    MOE_REQUIRE(H % 256 == 0 && F % 256 == 0, MOE_ERR_INVALID_ARG,
+                f + ": MXFP4 needs H % 256 == 0 and F % 256 == 0");
+  return MOE_OK;
+}
+
+static bool scale_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+static int fc1_impl(const void* a, const uint8_t* a_scales, int a_fmt, const int32_t* src_row,
+                    const void* w1, const uint8_t* w1_scales, const int32_t* offsets, int E, int H,
+                    int F, int64_t rows, void* act_save, void* h, uint8_t* h_scales,
+                    hipStream_t stream) {
+  const int bits = elem_bits(a_fmt);
+  if (a_fmt == MOE_F32) {
+    const int64_t g1 = std::min<int64_t>(65536, (rows * F + 255) / 256);
+    hipLaunchKernelGGL(fc1_swiglu_f32_kernel, dim3(g1), dim3(256), 0, stream,
+                       static_cast<const float*>(a), src_row, static_cast<const float*>(w1),
+                       offsets, E, H, F, rows, static_cast<float*>(h),
+                       static_cast<uint16_t*>(act_save));
+    return check_launch("moe_grouped_fc1_swiglu");
+  }
+  Args f1{};
+  f1.a = static_cast<const uint8_t*>(a);
+  f1.a_row_bytes = static_cast<int64_t>(H) * bits / 8;
+  f1.a_sc = a_scales;
+  f1.a_sc_row_bytes = H / 32;
+  f1.gather = src_row;
+  f1.b = static_cast<const uint8_t*>(w1);
+  f1.b_row_bytes = static_cast<int64_t>(H) * bits / 8;
+  f1.b_exp_bytes = 2ll * F * f1.b_row_bytes;
+  f1.b_sc = w1_scales;
+  f1.b_sc_row_bytes = H / 32;
+  f1.b_sc_exp_bytes = 2ll * F * (H / 32);
+  f1.up_row = F;
+  f1.offsets = offsets;
+  f1.E = E;
+  f1.rows = rows;
+  f1.n_blocks = F / 64;
+  f1.k_stages = static_cast<int>(f1.a_row_bytes / kRowBytes);
+  f1.out = static_cast<uint8_t*>(h);
+  f1.out_row_bytes = static_cast<int64_t>(F) * bits / 8;
+  f1.out_sc = h_scales;
+  f1.out_sc_row_bytes = F / 32;
+  f1.act_save = static_cast<uint16_t*>(act_save);
+  f1.act_cols = 2 * F;
+  if (a_fmt == MOE_BF16) return launch_gemm<256, 3, OP_BF16, EPI_SWIGLU, MOE_BF16>(f1, stream);
+  if (a_fmt == MOE_MXFP8_E4M3)
+    return launch_gemm<256, 3, OP_FP8, EPI_SWIGLU, MOE_MXFP8_E4M3>(f1, stream);
+  return launch_gemm<256, 3, OP_FP4, EPI_SWIGLU, MOE_MXFP4_E2M1>(f1, stream);
+}
+
+static int fc2_impl(const void* h, const uint8_t* h_scales, int h_fmt, const void* w2,
+                    const uint8_t* w2_scales, const int32_t* offsets, int E, int H, int F,
+                    int64_t rows, void* y, hipStream_t stream) {
+  const int bits = elem_bits(h_fmt);
+  if (h_fmt == MOE_F32) {
+    const int64_t g2 = std::min<int64_t>(65536, (rows * H + 255) / 256);
+    hipLaunchKernelGGL(fc2_f32_kernel, dim3(g2), dim3(256), 0, stream,
+                       static_cast<const float*>(h), static_cast<const float*>(w2), offsets, E, H,
+                       F, rows, static_cast<float*>(y));
+    return check_launch("moe_grouped_fc2");
+  }
+  Args f2{};
+  f2.a = static_cast<const uint8_t*>(h);
+  f2.a_row_bytes = static_cast<int64_t>(F) * bits / 8;
+  f2.a_sc = h_scales;
+  f2.a_sc_row_bytes = F / 32;
+  f2.gather = nullptr;
+  f2.b = static_cast<const uint8_t*>(w2);
+  f2.b_row_bytes = static_cast<int64_t>(F) * bits / 8;
+  f2.b_exp_bytes = static_cast<int64_t>(H) * f2.b_row_bytes;
+  f2.b_sc = w2_scales;
+  f2.b_sc_row_bytes = F / 32;
+  f2.b_sc_exp_bytes = static_cast<int64_t>(H) * (F / 32);
+  f2.up_row = 0;
+  f2.offsets = offsets;
+  f2.E = E;
+  f2.rows = rows;
+  f2.n_blocks = H / kBRows;
+  f2.k_stages = static_cast<int>(f2.a_row_bytes / kRowBytes);
+  f2.out = static_cast<uint8_t*>(y);
+  f2.out_row_bytes = static_cast<int64_t>(H) * 2;
+  if (h_fmt == MOE_BF16) return launch_gemm<256, 3, OP_BF16, EPI_PLAIN, MOE_BF16>(f2, stream);
+  if (h_fmt == MOE_MXFP8_E4M3) return launch_gemm<256, 3, OP_FP8, EPI_PLAIN, MOE_BF16>(f2, stream);
+  return launch_gemm<256, 3, OP_FP4, EPI_PLAIN, MOE_BF16>(f2, stream);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_grouped_mlp_workspace(int E, int H, int F, int64_t rows, int a_fmt,
+                                            int w_fmt) {
+  (void)E;
+  (void)H;
+  (void)w_fmt;
+  if (rows < 0 || F <= 0 || elem_bits(a_fmt) == 0) return 0;
+  size_t sc = is_mx(a_fmt) ? static_cast<size_t>(rows) * (F / 32) : 0;
+  sc = (sc + 255) & ~static_cast<size_t>(255);
+  return h_bytes_of(rows, F, a_fmt) + sc;
+}
+
+extern "C" int moe_grouped_fc1_swiglu(const void* a, const uint8_t* a_scales, int a_fmt,
+                                      const int32_t* src_row, const void* w1,
+                                      const uint8_t* w1_scales, int w_fmt,
+                                      const int32_t* offsets, int E, int H, int F, int64_t rows,
+                                      void* act_save, void* h, uint8_t* h_scales,
+                                      hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(E >= 1 && E <= kMaxGroups && H > 0 && F > 0 && rows >= 0, MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc1_swiglu: need 1 <= E <= 1024, H > 0, F > 0, rows >= 0");
+  const int y_like = a_fmt == MOE_F32 ? MOE_F32 : MOE_BF16;
+  int st = check_formats("moe_grouped_fc1_swiglu", a_fmt, w_fmt, y_like, H, F);
+  if (st) return st;
+  MOE_REQUIRE(offsets && w1 && h && (rows == 0 || a), MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc1_swiglu: null pointer");
+  if (is_mx(a_fmt))
+    MOE_REQUIRE(a_scales && w1_scales && h_scales, MOE_ERR_INVALID_ARG,
+                "moe_grouped_fc1_swiglu: MX formats need a_scales, w1_scales and h_scales");
+  MOE_REQUIRE(aligned16(a) && aligned16(w1) && aligned16(h) && (!act_save || aligned16(act_save)),
+              MOE_ERR_ALIGNMENT, "moe_grouped_fc1_swiglu: tensors must be 16-byte aligned");
+  if (is_mx(a_fmt))
+    MOE_REQUIRE(scale_aligned(a_scales) && scale_aligned(w1_scales), MOE_ERR_ALIGNMENT,
+                "moe_grouped_fc1_swiglu: scale arrays must be 4-byte aligned");
+  if (rows == 0) return MOE_OK;
+  return fc1_impl(a, a_scales, a_fmt, src_row, w1, w1_scales, offsets, E, H, F, rows, act_save, h,
+                  h_scales, stream);
+}
+
+extern "C" int moe_grouped_fc2(const void* h, const uint8_t* h_scales, int h_fmt, const void* w2,
+                               const uint8_t* w2_scales, int w_fmt, const int32_t* offsets, int E,
+                               int H, int F, int64_t rows, void* y, int y_fmt,
+                               hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(E >= 1 && E <= kMaxGroups && H > 0 && F > 0 && rows >= 0, MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc2: need 1 <= E <= 1024, H > 0, F > 0, rows >= 0");
+  int st = check_formats("moe_grouped_fc2", h_fmt, w_fmt, y_fmt, H, F);
+  if (st) return st;
+  MOE_REQUIRE(offsets && w2 && y && (rows == 0 || h), MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc2: null pointer");
+  if (is_mx(h_fmt))
+    MOE_REQUIRE(h_scales && w2_scales, MOE_ERR_INVALID_ARG,
+                "moe_grouped_fc2: MX formats need h_scales and w2_scales");
+  MOE_REQUIRE(aligned16(h) && aligned16(w2) && aligned16(y), MOE_ERR_ALIGNMENT,
+              "moe_grouped_fc2: tensors must be 16-byte aligned");
+  if (is_mx(h_fmt))
+    MOE_REQUIRE(scale_aligned(h_scales) && scale_aligned(w2_scales), MOE_ERR_ALIGNMENT,
+                "moe_grouped_fc2: scale arrays must be 4-byte aligned");
+  if (rows == 0) return MOE_OK;
+  return fc2_impl(h, h_scales, h_fmt, w2, w2_scales, offsets, E, H, F, rows, y, stream);
+}
+
+extern "C" int moe_grouped_mlp_fwd(const void* a, const uint8_t* a_scales, int a_fmt,
+                                   const int32_t* src_row, const void* w1,
+                                   const uint8_t* w1_scales, const void* w2,
+                                   const uint8_t* w2_scales, int w_fmt, const int32_t* offsets,
+                                   int E, int H, int F, int64_t rows, void* act_save, void* y,
+                                   int y_fmt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(E >= 1 && E <= kMaxGroups && H > 0 && F > 0 && rows >= 0, MOE_ERR_INVALID_ARG,
+              "moe_grouped_mlp_fwd: need 1 <= E <= 1024, H > 0, F > 0, rows >= 0");
+  int st = check_formats("moe_grouped_mlp_fwd", a_fmt, w_fmt, y_fmt, H, F);
+  if (st) return st;
+  MOE_REQUIRE(offsets && w1 && w2 && y && (rows == 0 || a), MOE_ERR_INVALID_ARG,
+              "moe_grouped_mlp_fwd: null pointer");
+  const bool mx = is_mx(a_fmt);
+  if (mx)
+    MOE_REQUIRE(a_scales && w1_scales && w2_scales, MOE_ERR_INVALID_ARG,
+                "moe_grouped_mlp_fwd: MX formats need a_scales, w1_scales and w2_scales");
+  MOE_REQUIRE(aligned16(a) && aligned16(w1) && aligned16(w2) && aligned16(y) &&
+                  (!act_save || aligned16(act_save)),
+              MOE_ERR_ALIGNMENT, "moe_grouped_mlp_fwd: tensors must be 16-byte aligned");
+  if (mx)
+    MOE_REQUIRE(scale_aligned(a_scales) && scale_aligned(w1_scales) && scale_aligned(w2_scales),
+                MOE_ERR_ALIGNMENT, "moe_grouped_mlp_fwd: scale arrays must be 4-byte aligned");
+  const size_t need = moe_grouped_mlp_workspace(E, H, F, rows, a_fmt, w_fmt);
+  MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "moe_grouped_mlp_fwd: workspace too small");
+  if (rows == 0) return MOE_OK;
+  uint8_t* h = static_cast<uint8_t*>(ws);
+  uint8_t* h_sc = mx ? h + h_bytes_of(rows, F, a_fmt) : nullptr;
+  st = fc1_impl(a, a_scales, a_fmt, src_row, w1, w1_scales, offsets, E, H, F, rows, act_save, h,
+                h_sc, stream);
+  if (st) return st;
+  return fc2_impl(h, h_sc, a_fmt, w2, w2_scales, offsets, E, H, F, rows, y, stream);
+}

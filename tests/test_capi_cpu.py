@@ -1,0 +1,131 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, and its host-side argument checks return the documented
+status codes before anything is enqueued (no call here reaches the device).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_sigmoid_amd as moe
+from mixture_experts_layer_sigmoid_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WS = 0, -1, -2, -3, -4
+A = 0x10000  # aligned fake device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libmoe_mi355x.so is not built (run __graft_entry__.build())")
+    return L.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.SIGNATURES), "binding and header disagree"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.moe_abi_version() == 1
+    assert lib.moe_status_str(0) == b"ok"
+    assert lib.moe_status_str(-4) == b"workspace missing or too small"
+
+
+def _route(lib, **kw):
+    a = dict(x=A, x_fmt=1, w=A, bias=A, lin=None, T=4, H=64, E=16, ng=4, tg=2, k=4, scale=1.0,
+             lout=None, idx=A, w_out=A)
+    a.update(kw)
+    return lib.moe_route(a["x"], a["x_fmt"], a["w"], a["bias"], a["lin"], a["T"], a["H"], a["E"],
+                         a["ng"], a["tg"], a["k"], a["scale"], a["lout"], a["idx"], a["w_out"], None)
+
+
+def test_route_validation(lib):
+    assert _route(lib, E=0) == INVALID
+    assert _route(lib, E=513) == INVALID
+    assert _route(lib, ng=3) == INVALID                 # 16 % 3
+    assert _route(lib, E=8, ng=8, tg=2, k=2) == INVALID  # groups of 1
+    assert _route(lib, tg=5) == INVALID
+    assert _route(lib, k=9) == INVALID                  # > topk_group * E / n_group
+    assert _route(lib, k=17, E=64, ng=1, tg=1) == INVALID
+    assert _route(lib, bias=None) == INVALID
+    assert _route(lib, x_fmt=2) == UNSUPPORTED
+    assert _route(lib, H=48) == INVALID                 # bf16 needs H % 32
+    assert _route(lib, x=A + 8) == ALIGN
+    assert b"aligned" in lib.moe_last_error()
+    assert _route(lib, T=0) == OK                       # nothing to do, nothing launched
+    assert _route(lib, T=0, x=None, w=None, lin=A) == OK
+
+
+def test_quantize_validation(lib):
+    q = lambda **k: lib.moe_quantize_mx(k.get("inp", A), k.get("fi", 1), k.get("rows", 4),
+                                        k.get("K", 64), k.get("axis", 0), k.get("fo", 2),
+                                        k.get("c", A), k.get("s", A), None)
+    assert q(K=48) == INVALID
+    assert q(axis=1) == UNSUPPORTED
+    assert q(fo=1) == UNSUPPORTED
+    assert q(fi=2) == UNSUPPORTED
+    assert q(c=A + 4) == ALIGN
+    assert q(rows=0) == OK
+
+
+def test_permute_bounds_and_validation(lib):
+    assert lib.moe_permute_rows_bound(64, 4, 16, 32) == 64 * 4 + 16 * 31
+    assert lib.moe_permute_rows_bound(-1, 4, 16, 1) == -1
+    ws = lib.moe_permute_workspace(4096, 8, 256)
+    assert ws == 32 * 256 * 4
+    p = lambda **k: lib.moe_permute(A, k.get("T", 8), 2, 4, k.get("align", 1), k.get("rin"),
+                                    k.get("rb", 0), None, 0, A, A, A, A, k.get("rout"), None,
+                                    k.get("ws", A), k.get("wsb", 1 << 20), None)
+    assert p(align=3) == INVALID
+    assert p(wsb=0) == WS
+    assert p(ws=None) == WS
+    assert p(rin=A) == INVALID                  # rows_in without rows_out
+    assert p(rin=A, rout=A, rb=24) == ALIGN
+    assert p(T=-1) == INVALID
+
+
+def test_grouped_mlp_validation(lib):
+    need = lib.moe_grouped_mlp_workspace(8, 256, 128, 100, 1, 1)
+    assert need >= 100 * 128 * 2
+
+    def g(**k):
+        return lib.moe_grouped_mlp_fwd(A, k.get("asc"), k.get("af", 1), None, A, k.get("w1s"), A,
+                                       k.get("w2s"), k.get("wf", 1), A, 8, k.get("H", 256),
+                                       k.get("F", 128), 100, None, k.get("y", A), k.get("yf", 1),
+                                       k.get("ws", A), k.get("wsb", need), None)
+    assert g(wf=0) == UNSUPPORTED
+    assert g(af=2, wf=2, yf=1) == INVALID or g(af=2, wf=2, yf=1) == UNSUPPORTED
+    assert g(H=200) == INVALID
+    assert g(F=96) == INVALID
+    assert g(y=A + 2) == ALIGN
+    assert g(wsb=need - 1) == WS
+    assert g(af=3, wf=3, yf=1, H=256, F=128, asc=A, w1s=A, w2s=A) == INVALID   # fp4 needs F % 256
+
+
+def test_combine_validation(lib):
+    c = lambda **k: lib.moe_combine(A, k.get("yf", 1), A, A, None, k.get("T", 4), 2, k.get("H", 64),
+                                    k.get("out", A), k.get("of", 1), None)
+    assert c(H=60) == INVALID
+    assert c(yf=2) == UNSUPPORTED
+    assert c(out=A + 4) == ALIGN
+    assert c(T=0) == OK
+
+
+def test_binding_raises_with_message(lib):
+    with pytest.raises(moe.MoEError) as ei:
+        L._check("moe_route", _route(lib, E=0))
+    assert "E must be" in str(ei.value)
