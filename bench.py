@@ -95,7 +95,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_bf16_t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=32)
+    ap.add_argument("--cpu-tokens", type=int, default=96)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the layer runs on a single MI355X with no "

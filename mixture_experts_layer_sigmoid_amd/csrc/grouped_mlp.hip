@@ -42,34 +42,24 @@
 #include "mx_codec.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;   // bytes of K per row per stage
-constexpr int kBRows = 128;      // weight rows per tile
 constexpr int kMaxGroups = 1024;
 
 enum { OP_BF16 = 0, OP_FP8 = 1, OP_FP4 = 2 };
 enum { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
 
-template <int OP>
-struct Op;
-template <>
-struct Op<OP_BF16> {
-  static constexpr int kScaleBytes = 0;  // per row per stage
-  static constexpr int kSub = 4;         // MFMA k-steps per stage
-};
-template <>
-struct Op<OP_FP8> {
-  static constexpr int kScaleBytes = 4;
-  static constexpr int kSub = 2;
-};
-template <>
-struct Op<OP_FP4> {
-  static constexpr int kScaleBytes = 8;
-  static constexpr int kSub = 4;
+// Per-format constants for RB bytes of K per row per stage: MFMA k-steps per
+// stage (32x32x16 bf16 consumes 32 bytes of K per row, 32x32x64 E4M3 64
+// bytes, 32x32x64 E2M1 32 bytes) and MX scale bytes per row per stage (one
+// per 32 elements).
+template <int OP, int RB>
+struct Op {
+  static constexpr int kSub = OP == OP_FP8 ? RB / 64 : RB / 32;
+  static constexpr int kScaleBytes = OP == OP_BF16 ? 0 : (OP == OP_FP8 ? RB / 32 : RB / 16);
 };
 
 struct Args {
@@ -98,14 +88,15 @@ struct Args {
   int act_cols;            // 2F
 };
 
-template <int MMAX, int STAGES, int OP>
+template <int MMAX, int STAGES, int NCB, int OP, int RB>
 struct Smem {
-  static constexpr int kA = MMAX * kRowBytes;
-  static constexpr int kB = kBRows * kRowBytes;
-  static constexpr int kASc = MMAX * Op<OP>::kScaleBytes;
-  static constexpr int kBSc = kBRows * Op<OP>::kScaleBytes;
+  static constexpr int kBRows = 128 * NCB;
+  static constexpr int kA = MMAX * RB;
+  static constexpr int kB = kBRows * RB;
+  static constexpr int kASc = MMAX * Op<OP, RB>::kScaleBytes;
+  static constexpr int kBSc = kBRows * Op<OP, RB>::kScaleBytes;
   static constexpr int kStage = kA + kB + kASc + kBSc;
-  static constexpr int kSched = (kMaxGroups + 1) * 4 + MMAX * 4 + 16;
+  static constexpr int kSched = (kMaxGroups + 2) * 4 + MMAX * 4;
   static constexpr int kTotal = STAGES * kStage + kSched;
 };
 
@@ -135,32 +126,84 @@ __device__ __forceinline__ void wait_vm(int n) {
   }
 }
 
+// Workgroup barrier for the stage pipeline: waits only for this wave's LDS
+// operations (not for the global->LDS loads still in flight, which the
+// explicit vmcnt accounting covers) before s_barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // byte offset of 16-byte chunk c of row r inside a [rows][128 B] stage tile
-__device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
+// A stage tile stores row r's RB/16 chunks of 16 bytes XOR-permuted by a key
+// of r: (r/2)%8 for 128-byte rows, (r/4)%4 for 64-byte rows. Either way any
+// 16 consecutive rows put one logical chunk into 16 distinct 16-byte bank
+// groups of a 256-byte LDS line, so the MFMA operand reads (16 lanes = 16
+// consecutive rows per LDS cycle) are free of bank conflicts.
+template <int RB>
+__device__ __forceinline__ int swz_key(int r) {
+  return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+template <int RB>
+__device__ __forceinline__ int swz(int r, int c) { return r * RB + ((c ^ swz_key<RB>(r)) << 4); }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   const float sig = 1.f / (1.f + expf(-g));
   return g * sig * u;
 }
 
-template <int MMAX, int STAGES, int OP, int EPI, int OUTF>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
-  using S = Smem<MMAX, STAGES, OP>;
+// Weight row that tile row `br` streams. fc1 (SwiGLU): tile rows come in
+// groups of 32 = 16 gate rows then the matching 16 up rows, group q covering
+// h columns [16q, 16q+16) of the tile; fc2: consecutive output rows.
+template <int EPI, int NCB>
+__device__ __forceinline__ int weight_row(int nblk, int br, int up_row) {
+  if (EPI == EPI_SWIGLU) {
+    const int q = br >> 5, within = br & 31;
+    return nblk * (64 * NCB) + 16 * q + (within & 15) + (within >= 16 ? up_row : 0);
+  }
+  return nblk * (128 * NCB) + br;
+}
+
+// MMAX:   rows per tile (multiple of 32 * WM, <= 256)
+// STAGES: pipeline depth
+// RB:     bytes of K per row per stage (128 or 64)
+// NCB:    32-column MFMA blocks per wavefront (tile = 128 * NCB weight rows)
+// WM:     wavefront groups along the rows (4 * WM wavefronts; wave w owns
+//         column group w % 4 and row blocks w / 4, w / 4 + WM, ...)
+// OCC:    workgroups resident per CU (persistent grid = 256 * OCC)
+template <int MMAX, int STAGES, int NCB, int WM, int OCC, int RB, int OP, int EPI, int OUTF>
+__global__ __launch_bounds__(256 * WM) __attribute__((amdgpu_waves_per_eu(OCC * WM, OCC * WM)))
+void grouped_gemm_kernel(Args p) {
+  using S = Smem<MMAX, STAGES, NCB, OP, RB>;
+  using O = Op<OP, RB>;
+  constexpr int kCpr = RB / 16;         // 16-byte chunks per row per stage
+  constexpr int kRpi = 1024 / RB;       // rows per 1 KB direct-load instruction
+  constexpr int NT = 256 * WM;          // threads
+  constexpr int NW = 4 * WM;            // wavefronts
   constexpr int kRB = MMAX / 32;        // row blocks per tile
-  constexpr int kSB = Op<OP>::kScaleBytes;
-  constexpr int kAIns = MMAX / 32;      // A load instructions per wave per stage (8 rows each)
-  constexpr int kBIns = kBRows / 32;    // B load instructions per wave per stage
+  constexpr int kRBW = kRB / WM;        // row blocks per wavefront
+  static_assert(kRB % WM == 0, "row blocks must split evenly over the wave groups");
+  constexpr int kSB = O::kScaleBytes;
+  static_assert(kSB % 4 == 0, "MX scales are staged as whole dwords per row");
+  constexpr int kBR = S::kBRows;        // weight rows per tile
+  constexpr int kAIns = MMAX / (kRpi * NW);  // A load instructions per wave per stage
+  constexpr int kBIns = kBR / (kRpi * NW);   // B load instructions per wave per stage
+  static_assert(kAIns >= 1 && kBIns >= 1, "tile too small for the wavefront count");
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::kTotal];
   int32_t* s_mt = reinterpret_cast<int32_t*>(smem + STAGES * S::kStage);   // [E+1] m-tile prefix
   int32_t* s_src = s_mt + (kMaxGroups + 1);                                  // [MMAX] source rows
   int32_t* s_tot = s_src + MMAX;
+  // [NT] scan scratch; aliases the stage buffers, which the tile-list scan
+  // finishes with before the first load is issued
+  int32_t* part = reinterpret_cast<int32_t*>(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wn = wave & 3, wm = wave >> 2;
   const int E = p.E;
 
   // ---- tile list: m-tiles per expert, inclusive prefix in s_mt[1..E] ----
   {
-    const int per = (E + kThreads - 1) / kThreads;
+    const int per = (E + NT - 1) / NT;
     const int lo = tid * per, hi = min(E, lo + per);
     int s = 0;
     for (int e = lo; e < hi; ++e) {
@@ -170,11 +213,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
       s_mt[e + 1] = mt;
       s += mt;
     }
-    __syncthreads();
-    __shared__ int32_t part[kThreads];
     part[tid] = s;
     __syncthreads();
-    for (int d = 1; d < kThreads; d <<= 1) {
+    for (int d = 1; d < NT; d <<= 1) {
       const int v = tid >= d ? part[tid - d] : 0;
       __syncthreads();
       part[tid] += v;
@@ -187,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
     }
     if (tid == 0) {
       s_mt[0] = 0;
-      s_tot[0] = part[kThreads - 1];
+      s_tot[0] = part[NT - 1];
     }
     __syncthreads();
   }
@@ -197,11 +238,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
   const int64_t c_hi = total_tiles * (xs.xcd + 1) / kNumXcd;
 
   for (int64_t t = c_lo + xs.slot; t < c_hi; t += xs.nslots) {
-    // ---- decode the tile ----
+    // ---- decode the tile: expert e (s_mt[e]*nb <= t < s_mt[e+1]*nb),
+    // then column block (slow) and row block (fast) inside the expert ----
     int e;
     {
-      // find e with s_mt[e] * nb <= t < s_mt[e+1] * nb
-      int lo = 0, hi = E;  // invariant: s_mt[lo]*nb <= t < s_mt[hi]*nb
+      int lo = 0, hi = E;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (static_cast<int64_t>(s_mt[mid]) * p.n_blocks <= t) lo = mid;
@@ -215,9 +256,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
     const int mblk = static_cast<int>(local % mtiles);
     const int seg_lo = p.offsets[e];
     const int n_e = min(p.offsets[e + 1], (int)p.rows) - seg_lo;
-    const int rows_per = (n_e + mtiles - 1) / mtiles;  // balanced split, <= MMAX
-    const int row0 = seg_lo + mblk * rows_per;
-    const int nrows = min(rows_per, n_e - mblk * rows_per);
+    // full MMAX-row tiles first, the remainder last (MFMA padding only in
+    // the last tile's final 32-row block)
+    const int row0 = seg_lo + mblk * MMAX;
+    const int nrows = min(MMAX, n_e - mblk * MMAX);
     if (nrows <= 0) continue;  // uniform across the workgroup
     const int nrb = (nrows + 31) >> 5;
 
@@ -225,43 +267,37 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
     const uint8_t* a_src[kAIns];
 #pragma unroll
     for (int i = 0; i < kAIns; ++i) {
-      const int r = 8 * (wave + 4 * i) + (lane >> 3);
+      const int r = kRpi * (wave + NW * i) + lane / kCpr;
       int src = row0 + min(r, nrows - 1);
       if (p.gather) {
         src = p.gather[src];
         if (src < 0) src = 0;  // padding row: loads any valid row, h is zeroed
       }
-      a_src[i] = p.a + static_cast<int64_t>(src) * p.a_row_bytes + (((lane & 7) ^ (r & 7)) << 4);
+      a_src[i] = p.a + static_cast<int64_t>(src) * p.a_row_bytes + (((lane % kCpr) ^ swz_key<RB>(r)) << 4);
     }
     if (p.gather && EPI == EPI_SWIGLU) {
-      for (int r = tid; r < MMAX; r += kThreads) s_src[r] = r < nrows ? p.gather[row0 + r] : 0;
+      for (int r = tid; r < MMAX; r += NT) s_src[r] = r < nrows ? p.gather[row0 + r] : 0;
     }
     const uint8_t* b_src[kBIns];
     const uint8_t* bexp = p.b + static_cast<int64_t>(e) * p.b_exp_bytes;
 #pragma unroll
     for (int i = 0; i < kBIns; ++i) {
-      const int br = 8 * (wave + 4 * i) + (lane >> 3);
-      int wrow;
-      if (EPI == EPI_SWIGLU) {
-        const int w = br >> 5, within = br & 31;
-        wrow = nblk * 64 + 16 * w + (within & 15) + (within >= 16 ? p.up_row : 0);
-      } else {
-        wrow = nblk * kBRows + br;
-      }
-      b_src[i] = bexp + static_cast<int64_t>(wrow) * p.b_row_bytes + (((lane & 7) ^ (br & 7)) << 4);
+      const int br = kRpi * (wave + NW * i) + lane / kCpr;
+      const int wrow = weight_row<EPI, NCB>(nblk, br, p.up_row);
+      b_src[i] = bexp + static_cast<int64_t>(wrow) * p.b_row_bytes + (((lane % kCpr) ^ swz_key<RB>(br)) << 4);
     }
     // ---- MX scale sources: kSB bytes (kSB/4 dwords) per row per stage; one
     // 4-byte direct load per lane, 64/(kSB/4) rows per instruction ----
     constexpr int kDpr = kSB > 0 ? kSB / 4 : 1;
     constexpr int kScRows = 64 / kDpr;                 // rows per scale instruction
     constexpr int kAScIns = kSB > 0 ? MMAX / kScRows : 1;
-    constexpr int kBScIns = kSB > 0 ? kBRows / kScRows : 1;
-    const uint8_t* asc_src[(kAScIns + 3) / 4];
-    const uint8_t* bsc_src[(kBScIns + 3) / 4];
+    constexpr int kBScIns = kSB > 0 ? kBR / kScRows : 1;
+    const uint8_t* asc_src[(kAScIns + NW - 1) / NW];
+    const uint8_t* bsc_src[(kBScIns + NW - 1) / NW];
     if (kSB > 0) {
 #pragma unroll
-      for (int q = 0; q < (kAScIns + 3) / 4; ++q) {
-        const int j = wave + 4 * q;
+      for (int q = 0; q < (kAScIns + NW - 1) / NW; ++q) {
+        const int j = wave + NW * q;
         const int r = min(j * kScRows + lane / kDpr, nrows - 1);
         int src = row0 + r;
         if (p.gather) {
@@ -272,57 +308,53 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
       }
       const uint8_t* bsexp = p.b_sc + static_cast<int64_t>(e) * p.b_sc_exp_bytes;
 #pragma unroll
-      for (int q = 0; q < (kBScIns + 3) / 4; ++q) {
-        const int r = (wave + 4 * q) * kScRows + lane / kDpr;
-        int wrow;
-        if (EPI == EPI_SWIGLU) {
-          const int w = r >> 5, within = r & 31;
-          wrow = nblk * 64 + 16 * w + (within & 15) + (within >= 16 ? p.up_row : 0);
-        } else {
-          wrow = nblk * kBRows + r;
-        }
+      for (int q = 0; q < (kBScIns + NW - 1) / NW; ++q) {
+        const int r = min((wave + NW * q) * kScRows + lane / kDpr, kBR - 1);
+        const int wrow = weight_row<EPI, NCB>(nblk, r, p.up_row);
         bsc_src[q] = bsexp + static_cast<int64_t>(wrow) * p.b_sc_row_bytes + (lane % kDpr) * 4;
       }
     }
 
-    f32x16_t acc[kRB];
+    f32x16_t acc[kRBW][NCB];
 #pragma unroll
-    for (int i = 0; i < kRB; ++i) acc[i] = f32x16_t{};
+    for (int i = 0; i < kRBW; ++i)
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) acc[i][c] = f32x16_t{};
 
     // vector-memory instructions this wave issues per stage: A instruction i
     // covers rows [8*(wave+4i), +8) and is issued when that range starts
-    // below nrows; scale instruction q covers rows [(wave+4q)*kScRows, ...)
+    // below nrows; scale instruction j covers rows [j*kScRows, ...)
     int my_a = 0;
 #pragma unroll
-    for (int i = 0; i < kAIns; ++i) my_a += (8 * (wave + 4 * i) < nrows) ? 1 : 0;
+    for (int i = 0; i < kAIns; ++i) my_a += (kRpi * (wave + NW * i) < nrows) ? 1 : 0;
     int my_asc = 0, my_bsc = 0;
     if (kSB > 0) {
 #pragma unroll
-      for (int q = 0; q < (kAScIns + 3) / 4; ++q)
-        my_asc += ((wave + 4 * q) < kAScIns && (wave + 4 * q) * kScRows < nrows) ? 1 : 0;
+      for (int q = 0; q < (kAScIns + NW - 1) / NW; ++q)
+        my_asc += ((wave + NW * q) < kAScIns && (wave + NW * q) * kScRows < nrows) ? 1 : 0;
 #pragma unroll
-      for (int q = 0; q < (kBScIns + 3) / 4; ++q) my_bsc += ((wave + 4 * q) < kBScIns) ? 1 : 0;
+      for (int q = 0; q < (kBScIns + NW - 1) / NW; ++q) my_bsc += ((wave + NW * q) < kBScIns) ? 1 : 0;
     }
     const int per_stage = my_a + kBIns + my_asc + my_bsc;
 
     auto issue = [&](int kt) {
       uint8_t* st = smem + (kt % STAGES) * S::kStage;
-      const int64_t kb = static_cast<int64_t>(kt) * kRowBytes;
+      const int64_t kb = static_cast<int64_t>(kt) * RB;
+#pragma unroll
+      for (int i = 0; i < kBIns; ++i) lds_load16(b_src[i] + kb, st + S::kA + (wave + NW * i) * 1024);
 #pragma unroll
       for (int i = 0; i < kAIns; ++i)
-        if (8 * (wave + 4 * i) < nrows) lds_load16(a_src[i] + kb, st + (wave + 4 * i) * 1024);
-#pragma unroll
-      for (int i = 0; i < kBIns; ++i) lds_load16(b_src[i] + kb, st + S::kA + (wave + 4 * i) * 1024);
+        if (kRpi * (wave + NW * i) < nrows) lds_load16(a_src[i] + kb, st + (wave + NW * i) * 1024);
       if (kSB > 0) {
         const int64_t ks = static_cast<int64_t>(kt) * kSB;
 #pragma unroll
-        for (int q = 0; q < (kAScIns + 3) / 4; ++q) {
-          const int j = wave + 4 * q;
+        for (int q = 0; q < (kAScIns + NW - 1) / NW; ++q) {
+          const int j = wave + NW * q;
           if (j < kAScIns && j * kScRows < nrows) lds_load4(asc_src[q] + ks, st + S::kA + S::kB + j * 256);
         }
 #pragma unroll
-        for (int q = 0; q < (kBScIns + 3) / 4; ++q) {
-          const int j = wave + 4 * q;
+        for (int q = 0; q < (kBScIns + NW - 1) / NW; ++q) {
+          const int j = wave + NW * q;
           if (j < kBScIns) lds_load4(bsc_src[q] + ks, st + S::kA + S::kB + S::kASc + j * 256);
         }
       }
@@ -333,76 +365,107 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
     for (int s = 0; s < STAGES - 1; ++s)
       if (s < KT) issue(s);
 
-    for (int kt = 0; kt < KT; ++kt) {
-      // stages issued after kt that may stay in flight
-      const int ahead = min(STAGES - 2, KT - 1 - kt);
-      wait_vm(ahead * per_stage);
-      __syncthreads();
-      if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
-      const uint8_t* st = smem + (kt % STAGES) * S::kStage;
+    // number of this wave's row blocks (mb = wm, wm + WM, ...) that hold rows
+    const int nv = nrb > wm ? min(kRBW, (nrb - wm + WM - 1) / WM) : 0;
+    const int g = lane >> 5;
+
+    // One stage of MFMAs for the first NV row blocks of this wave. Operands of
+    // k-step s+1 are read from LDS before the MFMAs of k-step s are issued,
+    // so LDS latency overlaps the matrix cores.
+    auto stage_mfma = [&](const uint8_t* st, auto nv_c) {
+      constexpr int NV = decltype(nv_c)::value;
       const uint8_t* sa = st;
       const uint8_t* sb = st + S::kA;
-      const int brow = 32 * wave + (lane & 31);
-      const int g = lane >> 5;
       if constexpr (OP == OP_BF16) {
+        bf16x8_t ao[2][NV > 0 ? NV : 1], bo[2][NCB];
+        auto load = [&](int s, int buf) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8_t bop = *reinterpret_cast<const bf16x8_t*>(sb + swz(brow, 2 * s + g));
+          for (int c = 0; c < NCB; ++c)
+            bo[buf][c] = *reinterpret_cast<const bf16x8_t*>(sb + swz<RB>(32 * (wn * NCB + c) + (lane & 31), 2 * s + g));
 #pragma unroll
-          for (int mb = 0; mb < kRB; ++mb) {
-            if (mb < nrb) {
-              const int ar = mb * 32 + (lane & 31);
-              const bf16x8_t aop = *reinterpret_cast<const bf16x8_t*>(sa + swz(ar, 2 * s + g));
-              acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, acc[mb], 0, 0, 0);
-            }
-          }
+          for (int i = 0; i < NV; ++i)
+            ao[buf][i] = *reinterpret_cast<const bf16x8_t*>(sa + swz<RB>((wm + WM * i) * 32 + (lane & 31), 2 * s + g));
+        };
+        load(0, 0);
+#pragma unroll
+        for (int s = 0; s < O::kSub; ++s) {
+          if (s + 1 < O::kSub) load(s + 1, (s + 1) & 1);
+#pragma unroll
+          for (int i = 0; i < NV; ++i)
+#pragma unroll
+            for (int c = 0; c < NCB; ++c)
+              acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[s & 1][i], bo[s & 1][c], acc[i][c], 0, 0, 0);
         }
       } else {
+        constexpr int dpr = kSB > 0 ? kSB / 4 : 1;
         const uint32_t* sasc = reinterpret_cast<const uint32_t*>(st + S::kA + S::kB);
         const uint32_t* sbsc = reinterpret_cast<const uint32_t*>(st + S::kA + S::kB + S::kASc);
-        constexpr int dpr = kSB > 0 ? kSB / 4 : 1;
-        uint32_t bsc[dpr];
+        uint32_t bsc[NCB][dpr], asc[NV > 0 ? NV : 1][dpr];
 #pragma unroll
-        for (int d = 0; d < dpr; ++d) bsc[d] = sbsc[brow * dpr + d];
+        for (int c = 0; c < NCB; ++c)
 #pragma unroll
-        for (int s = 0; s < Op<OP>::kSub; ++s) {
-          i32x8_t bop;
+          for (int d = 0; d < dpr; ++d) bsc[c][d] = sbsc[(32 * (wn * NCB + c) + (lane & 31)) * dpr + d];
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+          for (int d = 0; d < dpr; ++d) asc[i][d] = sasc[((wm + WM * i) * 32 + (lane & 31)) * dpr + d];
+        i32x8_t ao[2][NV > 0 ? NV : 1], bo[2][NCB];
+        auto opnd = [&](const uint8_t* base, int row, int s) -> i32x8_t {
           if (OP == OP_FP8) {
-            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sb + swz(brow, 4 * s + g));
-            const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sb + swz(brow, 4 * s + 2 + g));
-            bop = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          } else {
-            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sb + swz(brow, 2 * s + g));
-            bop = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(base + swz<RB>(row, 4 * s + g));
+            const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(base + swz<RB>(row, 4 * s + 2 + g));
+            return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
           }
-          // this k-step covers blocks 2s and 2s+1 of the stage; lane group g
+          // E2M1, 32x32x64: lane group g holds k [32g, 32g+32) (16 bytes)
+          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(base + swz<RB>(row, 2 * s + g));
+          return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+        };
+        auto load = [&](int s, int buf) {
+#pragma unroll
+          for (int c = 0; c < NCB; ++c) bo[buf][c] = opnd(sb, 32 * (wn * NCB + c) + (lane & 31), s);
+#pragma unroll
+          for (int i = 0; i < NV; ++i) ao[buf][i] = opnd(sa, (wm + WM * i) * 32 + (lane & 31), s);
+        };
+        constexpr int kSub = O::kSub;
+        load(0, 0);
+#pragma unroll
+        for (int s = 0; s < kSub; ++s) {
+          if (s + 1 < kSub) load(s + 1, (s + 1) & 1);
+          // k-step s covers MX blocks 2s and 2s+1 of the stage; lane group g
           // supplies the scale of block 2s+g in the low byte of its operand
           const int blk = 2 * s + g;
           const int bw = blk >> 2, bsh = 8 * (blk & 3);
 #pragma unroll
-          for (int mb = 0; mb < kRB; ++mb) {
-            if (mb < nrb) {
-              const int ar = mb * 32 + (lane & 31);
-              i32x8_t aop;
-              if (OP == OP_FP8) {
-                const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz(ar, 4 * s + g));
-                const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sa + swz(ar, 4 * s + 2 + g));
-                aop = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-              } else {
-                const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz(ar, 2 * s + g));
-                aop = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
-              }
-              const int asc = static_cast<int>((sasc[ar * dpr + bw] >> bsh) & 0xFFu);
-              const int bs = static_cast<int>((bsc[bw] >> bsh) & 0xFFu);
+          for (int i = 0; i < NV; ++i) {
+            const int as = static_cast<int>((asc[i][bw] >> bsh) & 0xFFu);
+#pragma unroll
+            for (int c = 0; c < NCB; ++c) {
+              const int bs = static_cast<int>((bsc[c][bw] >> bsh) & 0xFFu);
               if (OP == OP_FP8)
-                acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc[mb], 0, 0, 0, asc, 0, bs);
+                acc[i][c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ao[s & 1][i], bo[s & 1][c], acc[i][c], 0, 0, 0, as, 0, bs);
               else
-                acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc[mb], 4, 4, 0, asc, 0, bs);
+                acc[i][c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ao[s & 1][i], bo[s & 1][c], acc[i][c], 4, 4, 0, as, 0, bs);
             }
           }
         }
+      }
+    };
+
+    for (int kt = 0; kt < KT; ++kt) {
+      // stages issued after kt that may stay in flight
+      const int ahead = min(STAGES - 2, KT - 1 - kt);
+      wait_vm(ahead * per_stage);
+      // every wave's loads of stage kt have landed; LDS reads of stage kt-1
+      // are done (the load below reuses that buffer)
+      lds_barrier();
+      if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+      const uint8_t* st = smem + (kt % STAGES) * S::kStage;
+      switch (nv) {
+#define MOE_NV(N) case N: if constexpr (N <= kRBW) stage_mfma(st, std::integral_constant<int, N>{}); break;
+        MOE_NV(1) MOE_NV(2) MOE_NV(3) MOE_NV(4) MOE_NV(5) MOE_NV(6) MOE_NV(7) MOE_NV(8)
+#undef MOE_NV
+        default: break;
       }
     }
     __syncthreads();  // all waves done with the stage buffers
@@ -411,26 +474,31 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
     // row-major pass (SwiGLU / act save / MX encode / bf16) with 16-byte
     // global stores ----
     // C layout of a 32x32 MFMA: lane l, element r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
-    constexpr int kCs = kBRows + 4;  // padded row stride (floats)
+    constexpr int kCs = kBR + 4;  // padded row stride (floats)
     static_assert(MMAX * kCs * 4 <= STAGES * S::kStage, "epilogue tile must fit the stage buffers");
     float* cs = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int mb = 0; mb < kRB; ++mb) {
+    for (int i = 0; i < kRBW; ++i) {
+      const int mb = wm + WM * i;
       if (mb < nrb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          cs[row * kCs + 32 * wave + (lane & 31)] = acc[mb][r];
+        for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            cs[row * kCs + 32 * (wn * NCB + c) + (lane & 31)] = acc[i][c][r];
+          }
         }
       }
     }
     __syncthreads();
     if constexpr (EPI == EPI_SWIGLU) {
-      // h column c (0..63) of this tile: gate at tile column 32*(c/16) + c%16,
-      // up at the same + 16
+      // h column c (0..64*NCB) of this tile: gate at tile column
+      // 32*(c/16) + c%16, up at the same + 16
+      constexpr int kHc = 64 * NCB;
       if constexpr (OUTF == MOE_BF16) {
-        for (int i = tid; i < nrows * 8; i += kThreads) {
-          const int row = i >> 3, c0 = (i & 7) * 8;
+        for (int i = tid; i < nrows * (kHc / 8); i += NT) {
+          const int row = i / (kHc / 8), c0 = (i % (kHc / 8)) * 8;
           const bool zero = p.gather && s_src[row] < 0;
           const float* gp = cs + row * kCs + 32 * (c0 >> 4) + (c0 & 15);
           const float* up = gp + 16;
@@ -438,11 +506,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
 #pragma unroll
           for (int q = 0; q < 8; ++q) h[q] = zero ? 0.f : silu_mul(gp[q], up[q]);
           const int64_t grow = row0 + row;
-          *reinterpret_cast<u32x4_t*>(p.out + grow * p.out_row_bytes + (nblk * 64 + c0) * 2) =
+          *reinterpret_cast<u32x4_t*>(p.out + grow * p.out_row_bytes + (nblk * kHc + c0) * 2) =
               u32x4_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
                       pack_bf16x2(h[6], h[7])};
           if (p.act_save) {
-            uint16_t* ar = p.act_save + grow * p.act_cols + nblk * 64 + c0;
+            uint16_t* ar = p.act_save + grow * p.act_cols + nblk * kHc + c0;
             *reinterpret_cast<u32x4_t*>(ar) =
                 u32x4_t{pack_bf16x2(gp[0], gp[1]), pack_bf16x2(gp[2], gp[3]),
                         pack_bf16x2(gp[4], gp[5]), pack_bf16x2(gp[6], gp[7])};
@@ -453,8 +521,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
         }
       } else {
         constexpr bool fp4 = OUTF == MOE_MXFP4_E2M1;
-        for (int i = tid; i < nrows * 2; i += kThreads) {
-          const int row = i >> 1, blk = i & 1;
+        constexpr int kBlk = kHc / 32;  // 32-column MX blocks per row of the tile
+        for (int i = tid; i < nrows * kBlk; i += NT) {
+          const int row = i / kBlk, blk = i % kBlk;
           const bool zero = p.gather && s_src[row] < 0;
           float v[32];
 #pragma unroll
@@ -466,20 +535,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
           uint32_t words[8];
           const uint32_t sb = mx_encode_block<fp4>(v, words);
           const int64_t r = row0 + row;
+          const int gblk = nblk * kBlk + blk;
           if (fp4) {
-            *reinterpret_cast<u32x4_t*>(p.out + r * p.out_row_bytes + (nblk * 2 + blk) * 16) =
+            *reinterpret_cast<u32x4_t*>(p.out + r * p.out_row_bytes + gblk * 16) =
                 u32x4_t{words[0], words[1], words[2], words[3]};
           } else {
-            u32x4_t* o = reinterpret_cast<u32x4_t*>(p.out + r * p.out_row_bytes + (nblk * 2 + blk) * 32);
+            u32x4_t* o = reinterpret_cast<u32x4_t*>(p.out + r * p.out_row_bytes + gblk * 32);
             o[0] = u32x4_t{words[0], words[1], words[2], words[3]};
             o[1] = u32x4_t{words[4], words[5], words[6], words[7]};
           }
-          p.out_sc[r * p.out_sc_row_bytes + nblk * 2 + blk] = static_cast<uint8_t>(sb);
+          p.out_sc[r * p.out_sc_row_bytes + gblk] = static_cast<uint8_t>(sb);
           if (p.act_save) {
             for (int q = 0; q < 32; q += 8) {
               const int c = blk * 32 + q;
               const float* gp = cs + row * kCs + 32 * (c >> 4) + (c & 15);
-              uint16_t* ar = p.act_save + r * p.act_cols + nblk * 64 + c;
+              uint16_t* ar = p.act_save + r * p.act_cols + nblk * kHc + c;
               *reinterpret_cast<u32x4_t*>(ar) =
                   u32x4_t{pack_bf16x2(gp[0], gp[1]), pack_bf16x2(gp[2], gp[3]),
                           pack_bf16x2(gp[4], gp[5]), pack_bf16x2(gp[6], gp[7])};
@@ -491,11 +561,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Args p) {
         }
       }
     } else {
-      for (int i = tid; i < nrows * 16; i += kThreads) {
-        const int row = i >> 4, c0 = (i & 15) * 8;
+      for (int i = tid; i < nrows * (kBR / 8); i += NT) {
+        const int row = i / (kBR / 8), c0 = (i % (kBR / 8)) * 8;
         const float* v = cs + row * kCs + c0;
         *reinterpret_cast<u32x4_t*>(p.out + static_cast<int64_t>(row0 + row) * p.out_row_bytes +
-                                    (nblk * kBRows + c0) * 2) =
+                                    (static_cast<int64_t>(nblk) * kBR + c0) * 2) =
             u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                     pack_bf16x2(v[6], v[7])};
       }
@@ -568,12 +638,14 @@ __global__ __launch_bounds__(256) void fc2_f32_kernel(const float* __restrict__ 
   }
 }
 
-template <int MMAX, int STAGES, int OP, int EPI, int OUTF>
-int launch_gemm(const Args& a, hipStream_t stream) {
-  const int grid = kNumCu;  // one workgroup per CU (LDS-bound), persistent
-  hipLaunchKernelGGL((grouped_gemm_kernel<MMAX, STAGES, OP, EPI, OUTF>), dim3(grid),
-                     dim3(kThreads), 0, stream, a);
-  return check_launch("moe_grouped_mlp_fwd");
+template <int MMAX, int STAGES, int NCB, int WM, int OCC, int RB, int OP, int EPI, int OUTF>
+int launch_gemm(Args a, hipStream_t stream) {
+  a.n_blocks /= NCB;
+  a.k_stages = static_cast<int>(a.a_row_bytes / RB);
+  const int grid = kNumCu * OCC;  // persistent: OCC workgroups per CU
+  hipLaunchKernelGGL((grouped_gemm_kernel<MMAX, STAGES, NCB, WM, OCC, RB, OP, EPI, OUTF>), dim3(grid),
+                     dim3(256 * WM), 0, stream, a);
+  return check_launch("grouped GEMM");
 }
 
 int elem_bits(int fmt) {
@@ -648,17 +720,25 @@ static int fc1_impl(const void* a, const uint8_t* a_scales, int a_fmt, const int
   f1.E = E;
   f1.rows = rows;
   f1.n_blocks = F / 64;
-  f1.k_stages = static_cast<int>(f1.a_row_bytes / kRowBytes);
   f1.out = static_cast<uint8_t*>(h);
   f1.out_row_bytes = static_cast<int64_t>(F) * bits / 8;
   f1.out_sc = h_scales;
   f1.out_sc_row_bytes = F / 32;
   f1.act_save = static_cast<uint16_t*>(act_save);
   f1.act_cols = 2 * F;
-  if (a_fmt == MOE_BF16) return launch_gemm<256, 3, OP_BF16, EPI_SWIGLU, MOE_BF16>(f1, stream);
+  // 128-row tiles of 256 weight rows (two 32-column MFMA blocks per wave, 8
+  // waves) for routed experts; 256-row tiles of 128 weight rows for a single
+  // dense group (a shared expert: more rows per weight tile, fewer weight
+  // re-reads) or when F is not a multiple of 128
+  const bool wide = F % 128 == 0 && E > 1;
+  if (a_fmt == MOE_BF16)
+    return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_BF16, EPI_SWIGLU, MOE_BF16>(f1, stream)
+                : launch_gemm<256, 3, 1, 2, 1, 128, OP_BF16, EPI_SWIGLU, MOE_BF16>(f1, stream);
   if (a_fmt == MOE_MXFP8_E4M3)
-    return launch_gemm<256, 3, OP_FP8, EPI_SWIGLU, MOE_MXFP8_E4M3>(f1, stream);
-  return launch_gemm<256, 3, OP_FP4, EPI_SWIGLU, MOE_MXFP4_E2M1>(f1, stream);
+    return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP8, EPI_SWIGLU, MOE_MXFP8_E4M3>(f1, stream)
+                : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP8, EPI_SWIGLU, MOE_MXFP8_E4M3>(f1, stream);
+  return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP4, EPI_SWIGLU, MOE_MXFP4_E2M1>(f1, stream)
+              : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP4, EPI_SWIGLU, MOE_MXFP4_E2M1>(f1, stream);
 }
 
 static int fc2_impl(const void* h, const uint8_t* h_scales, int h_fmt, const void* w2,
@@ -688,13 +768,18 @@ static int fc2_impl(const void* h, const uint8_t* h_scales, int h_fmt, const voi
   f2.offsets = offsets;
   f2.E = E;
   f2.rows = rows;
-  f2.n_blocks = H / kBRows;
-  f2.k_stages = static_cast<int>(f2.a_row_bytes / kRowBytes);
+  f2.n_blocks = H / 128;
   f2.out = static_cast<uint8_t*>(y);
   f2.out_row_bytes = static_cast<int64_t>(H) * 2;
-  if (h_fmt == MOE_BF16) return launch_gemm<256, 3, OP_BF16, EPI_PLAIN, MOE_BF16>(f2, stream);
-  if (h_fmt == MOE_MXFP8_E4M3) return launch_gemm<256, 3, OP_FP8, EPI_PLAIN, MOE_BF16>(f2, stream);
-  return launch_gemm<256, 3, OP_FP4, EPI_PLAIN, MOE_BF16>(f2, stream);
+  const bool wide = H % 256 == 0 && E > 1;
+  if (h_fmt == MOE_BF16)
+    return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_BF16, EPI_PLAIN, MOE_BF16>(f2, stream)
+                : launch_gemm<256, 3, 1, 2, 1, 128, OP_BF16, EPI_PLAIN, MOE_BF16>(f2, stream);
+  if (h_fmt == MOE_MXFP8_E4M3)
+    return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP8, EPI_PLAIN, MOE_BF16>(f2, stream)
+                : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP8, EPI_PLAIN, MOE_BF16>(f2, stream);
+  return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP4, EPI_PLAIN, MOE_BF16>(f2, stream)
+              : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP4, EPI_PLAIN, MOE_BF16>(f2, stream);
 }
 
 }  // namespace

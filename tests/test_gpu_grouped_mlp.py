@@ -110,6 +110,21 @@ def test_stage_parity(gpu_lib, name, T, k, heavy, align):
     assert rel_l2(save[:used][live], a_ref[:used][live]) < 1e-2
 
 
+def test_fallback_tiles_bf16(gpu_lib):
+    """F % 128 != 0 and H % 256 != 0 select the 256-row, 128-column tiles."""
+    cfg = configs.MoEConfig(**{**configs.get("mini_bf16").__dict__, "name": "fallback_bf16",
+                               "H": 384, "F": 192, "E": 12, "T": 150, "n_group": 4, "topk_group": 2,
+                               "k": 3, "F_shared": 192, "family": "fallback_bf16"})
+    log("grouped MLP fallback tiles H=384 F=192")
+    h = gen.host_inputs(cfg)
+    idx = _routing(cfg.T, cfg.E, 3, 5, heavy=120)
+    _, offsets, _, src = pm.permute_maps(idx, cfg.E, 1)
+    ew = _weights_dev(cfg, h)
+    y, _ = _run(cfg, dev(h["x"], "bf16"), ew, offsets, src, len(src), cfg.T)
+    y_ref, _ = _oracle_rows(cfg, h, offsets, src, cfg.E)
+    assert rel_l2(y, y_ref) < TOL["bf16"]
+
+
 @pytest.mark.parametrize("name", ["mini_bf16", "mini_mxfp8_decode", "mini_mxfp4", "mini_fp32"])
 def test_direct_rows_equal_gathered_rows(gpu_lib, name):
     cfg = configs.get(name)

@@ -46,7 +46,8 @@ def test_every_finite_bf16(gpu_lib, fmt):
 def test_fp32_wide_range(gpu_lib, fmt, rows, K):
     log(f"quantize fp32 {rows}x{K} {fmt}")
     g = np.random.default_rng(rows * K)
-    v = (g.standard_normal((rows, K)) * np.exp2(g.integers(-140, 100, (rows, K // 32, 1)))).reshape(rows, K)
+    scale = np.exp2(g.integers(-140, 100, (rows, K // 32, 1)).astype(np.float64))
+    v = (g.standard_normal((rows, K // 32, 32)) * scale).reshape(rows, K)
     v = v.astype(np.float32)
     v[0, :32] = 0.0                      # all-zero block
     if K >= 64:
