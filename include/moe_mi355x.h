@@ -126,10 +126,13 @@ int moe_route(const void* x, int x_fmt, const void* w_router, const float* bias,
  *   saturated to +-448 (E4M3) / +-6 (E2M1); the code keeps v's sign bit.
  * in      [rows, K] in in_fmt (MOE_F32 or MOE_BF16); rows may be 0.
  * out_fmt MOE_MXFP8_E4M3 or MOE_MXFP4_E2M1.
- * codes   [rows, K] (E4M3) or [rows, K/2] (E2M1) bytes out.
- * scales  [rows, K/32] bytes out.
- * axis    must be 0 (blocks along K); other values return
- *         MOE_ERR_UNSUPPORTED.
+ * axis 0  blocks of 32 along K: codes [rows, K] (E4M3) or [rows, K/2]
+ *         (E2M1), scales [rows, K/32].
+ * axis 1  blocks of 32 consecutive rows of each column, output K-major
+ *         (transposed): codes [K, rows] or [K, rows/2], scales [K, rows/32];
+ *         needs in_fmt MOE_BF16 and rows % 32 == 0. This is the layout a
+ *         GEMM contracting over the rows consumes (the backward's
+ *         transposed weight copies).
  */
 int moe_quantize_mx(const void* in, int in_fmt, int64_t rows, int K, int axis,
                     int out_fmt, uint8_t* codes, uint8_t* scales,
@@ -259,6 +262,102 @@ int moe_grouped_fc2(const void* h, const uint8_t* h_scales, int h_fmt,
 int moe_combine(const void* y, int y_fmt, const int32_t* row_map,
                 const float* topk_w, const void* shared, int T, int k, int H,
                 void* out, int out_fmt, hipStream_t stream);
+
+/*
+ * ---- Backward of the routed expert path (TE DeepSeekV3Layer page,
+ * Performance section, "Where the time goes": dGLU bwd and wgrad of the
+ * fused grouped MLP in MXFP8; the local permute's reduce). Routing weights
+ * are constants and quantizers pass gradients straight through. Call order:
+ *   moe_combine_bwd -> moe_quantize_mx (dY rows) ->
+ *   moe_grouped_fc2_dgrad_dswiglu -> moe_grouped_fc1_dgrad -> moe_unpermute
+ *   moe_quantize_mx_segments (dY, h, dA, x) -> moe_grouped_wgrad (dW2, dW1)
+ */
+
+/*
+ * moe_combine_bwd — dy[r] = topk_w[t, j] * dout[t] for the expert-major row
+ * r = row_map[t, j]; every row with src_row[r] == -1 is zero.
+ * dout [T, H] in dout_fmt (MOE_BF16 or MOE_F32); dy [rows, H] bf16 out.
+ */
+int moe_combine_bwd(const void* dout, int dout_fmt, const int32_t* row_map,
+                    const int32_t* src_row, const float* topk_w, int T, int k,
+                    int H, int64_t rows, void* dy, hipStream_t stream);
+
+/*
+ * moe_unpermute — dx[t] = sum_j dx_perm[row_map[t, j]], fp32 accumulation
+ * in slot order (the permute "reduce" of the backward). With k = 1 it is
+ * the exact inverse of moe_permute's gather.
+ * dx_perm [rows, H] and dx [T, H] in MOE_F32 or MOE_BF16.
+ */
+int moe_unpermute(const void* dx_perm, int fmt, const int32_t* row_map, int T,
+                  int k, int H, void* dx, int out_fmt, hipStream_t stream);
+
+/* moe_segments_kstride — row width (elements) of the K-major outputs of
+ * moe_quantize_mx_segments: rows + 127*E rounded up to 128. -1 if invalid. */
+int64_t moe_segments_kstride(int64_t rows, int E);
+
+/*
+ * moe_quantize_mx_segments — MX quantization of expert-major rows along the
+ * rows of each expert segment (the weight-gradient operands): segment e is
+ * rows [offsets[e], offsets[e+1]) (lengths multiples of 32, as moe_permute
+ * with align 32 writes them); column c of segment e becomes K-major codes
+ * codes[c, kofs[e] .. kofs[e] + len_e) in blocks of 32 rows, the segment
+ * padded with zeros to a multiple of 128, kofs[e] the sum of the padded
+ * lengths before e (written to kofs [E+1]).
+ * mode 0: in [rows, C] bf16, row r used as is (zero where src_row[r] < 0)
+ * mode 1: in [T, C] bf16 token rows gathered through src_row (zero for -1)
+ * mode 2: in [rows, 2C] bf16 = the saved fc1 output (gate | up); the value
+ *         is silu(gate) * up (h recomputed), zero where src_row[r] < 0
+ * codes [C, kstride] (E4M3) or [C, kstride/2] (E2M1), scales [C, kstride/32];
+ * kstride >= moe_segments_kstride(rows, E), a multiple of 128.
+ */
+int moe_quantize_mx_segments(const void* in, int mode, const int32_t* src_row,
+                             const int32_t* offsets, int E, int64_t rows,
+                             int C, int64_t kstride, int out_fmt,
+                             uint8_t* codes, uint8_t* scales, int32_t* kofs,
+                             hipStream_t stream);
+
+/*
+ * moe_grouped_fc2_dgrad_dswiglu — per expert segment, dH = dY . W2 with W2
+ * given transposed w2t [E, F, H] (contraction over H contiguous), then the
+ * SwiGLU backward with the saved fc1 output A = (g | u):
+ *   dgate = dH * u * sig(g) * (1 + g * (1 - sig(g))),  dup = dH * silu(g)
+ * dy      [rows, H] in fmt (MX: codes + dy_scales [rows, H/32]).
+ * act_save [rows, 2F] bf16 (moe_grouped_fc1_swiglu's act_save).
+ * da      [rows, 2F] out: MX codes (+ da_scales [rows, 2F/32], blocks along
+ *         2F) or bf16 when fmt is MOE_BF16; da_bf16 optional bf16 copy.
+ * Limits: H % 128 == 0 (256 for MXFP4), F % 128 == 0.
+ */
+int moe_grouped_fc2_dgrad_dswiglu(const void* dy, const uint8_t* dy_scales,
+                                  int fmt, const void* w2t,
+                                  const uint8_t* w2t_scales,
+                                  const int32_t* offsets, int E, int H, int F,
+                                  int64_t rows, const void* act_save, void* da,
+                                  uint8_t* da_scales, void* da_bf16,
+                                  hipStream_t stream);
+
+/*
+ * moe_grouped_fc1_dgrad — per expert segment dX_rows = dA . W1 with W1 given
+ * transposed w1t [E, H, 2F] (contraction over 2F contiguous).
+ * da [rows, 2F] in fmt (MX codes + da_scales); dx_perm [rows, H] bf16 out.
+ */
+int moe_grouped_fc1_dgrad(const void* da, const uint8_t* da_scales, int fmt,
+                          const void* w1t, const uint8_t* w1t_scales,
+                          const int32_t* offsets, int E, int H, int F,
+                          int64_t rows, void* dx_perm, hipStream_t stream);
+
+/*
+ * moe_grouped_wgrad — per expert e, dw[e] = A_e^T-contracted product over
+ * the K segment [kofs[e], kofs[e+1]):  dw[e][m, n] = sum_k at[m, k] bt[n, k]
+ * at [M, kstride], bt [N, kstride] MXFP8 K-major codes with scales
+ * [M or N, kstride/32] (moe_quantize_mx_segments' outputs); dw [E, M, N]
+ * bf16 out; an expert with an empty segment gets exact zeros.
+ * Limits: fmt MOE_MXFP8_E4M3; M % 128 == 0 and N % 256 == 0, or M % 256 == 0
+ * and N % 128 == 0; kstride % 128 == 0.
+ */
+int moe_grouped_wgrad(const void* at, const uint8_t* at_scales, const void* bt,
+                      const uint8_t* bt_scales, int fmt, const int32_t* kofs,
+                      int E, int M, int N, int64_t kstride, void* dw,
+                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,250 @@
+// Backward of the routed expert path: combine backward, segment-transposed
+// MX quantization of the backward GEMM operands, and the C entry points of
+// the backward grouped GEMMs (fc2 data gradient fused with the SwiGLU
+// backward, fc1 data gradient, weight gradients).
+//
+// Page "[PyTorch] DeepSeekV3Layer: full MoE transformer layer (MLA +
+// DeepSeek MoE)", Performance section, "Where the time goes" table: the
+// fused grouped MLP runs "dGLU bwd" and "wgrad" in MXFP8, and the local
+// permute runs its reduce in the backward too. Readings where the page is
+// silent: routing weights are constants; quantizers pass gradients straight
+// through; every backward GEMM operand is MX quantized along that GEMM's
+// contraction axis (weights from a second, transposed quantization of the
+// same masters; activations along the rows of each expert segment, in
+// blocks of 32 rows of the segment padded to a multiple of 32).
+#include "common.h"
+#include "mx_codec.h"
+
+#include <algorithm>
+
+namespace moe {
+namespace {
+
+constexpr int kMaxE = 1024;
+
+// dy[r] = w[t, j] * dout[t] for the row r = row_map[t, j]; padding rows
+// (src_row -1) are zero. One workgroup per row.
+template <int DF>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const void* __restrict__ dout,
+                                                          const int32_t* __restrict__ row_map,
+                                                          const int32_t* __restrict__ src_row,
+                                                          const float* __restrict__ w, int k, int H,
+                                                          int64_t rows, uint16_t* __restrict__ dy) {
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const int t = src_row[r];
+    float wj = 0.f;
+    if (t >= 0) {
+      for (int j = 0; j < k; ++j)
+        if (row_map[static_cast<int64_t>(t) * k + j] == r) wj = w[static_cast<int64_t>(t) * k + j];
+    }
+    uint16_t* o = dy + r * H;
+    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+      float v[8];
+      if (t >= 0) {
+        if (DF == MOE_BF16) {
+          const u32x4_t q = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(dout) +
+                                                              static_cast<int64_t>(t) * H + c);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(q[i] << 16);
+            v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+          }
+        } else {
+          const float* s = static_cast<const float*>(dout) + static_cast<int64_t>(t) * H + c;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = s[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] *= wj;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+      }
+      *reinterpret_cast<u32x4_t*>(o + c) = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    }
+  }
+}
+
+enum { SEG_ROWS = 0, SEG_GATHER = 1, SEG_SWIGLU = 2 };
+
+// Segment-transposed MX quantization. Input rows r (expert-major, segments
+// [offsets[e], offsets[e+1]) with lengths multiple of 32) of C columns:
+//   SEG_ROWS:   in[r, c] (bf16), zero where src_row[r] < 0
+//   SEG_GATHER: in[src_row[r], c] (bf16 token rows), zero where src_row < 0
+//   SEG_SWIGLU: silu(in[r, c]) * in[r, C + c] (in is [rows, 2C] bf16),
+//               zero where src_row[r] < 0
+// Output K-major: codes[c, kofs[e] + i] for the segment's rows i, each
+// segment padded with zeros to a multiple of `pad` columns; scales
+// [c, kstride/32], one per 32 columns. kofs[e] = sum over e' < e of the
+// padded lengths (written to kofs_out when given, kofs_out[E] = total).
+// offsets == nullptr means one segment [0, rows); src_row == nullptr means
+// every row is live (SEG_ROWS / SEG_SWIGLU only).
+template <int MODE, bool FP4>
+__global__ __launch_bounds__(256) void quantize_segments_kernel(
+    const uint16_t* __restrict__ in, const int32_t* __restrict__ src_row,
+    const int32_t* __restrict__ offsets, int E, int64_t rows, int C, int64_t kstride, int pad,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int32_t* __restrict__ kofs_out) {
+  __shared__ int32_t s_kofs[kMaxE + 1];
+  __shared__ int32_t part[256];
+  const int tid = threadIdx.x;
+  {
+    const int per = (E + 255) / 256;
+    const int lo = tid * per, hi = min(E, lo + per);
+    int s = 0;
+    for (int e = lo; e < hi; ++e) {
+      const int seg = offsets ? offsets[e + 1] - offsets[e] : static_cast<int>(rows);
+      s_kofs[e + 1] = (seg + pad - 1) / pad * pad;
+      s += s_kofs[e + 1];
+    }
+    part[tid] = s;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const int v = tid >= d ? part[tid - d] : 0;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
+    }
+    int run = tid > 0 ? part[tid - 1] : 0;
+    for (int e = lo; e < hi; ++e) {
+      run += s_kofs[e + 1];
+      s_kofs[e + 1] = run;
+    }
+    if (tid == 0) s_kofs[0] = 0;
+    __syncthreads();
+  }
+  if (blockIdx.x == 0 && kofs_out)
+    for (int e = tid; e <= E; e += 256) kofs_out[e] = s_kofs[e];
+  const int kblocks = s_kofs[E] / 32;
+  const int cgroups = (C + 255) / 256;
+  for (int64_t wi = blockIdx.x; wi < static_cast<int64_t>(kblocks) * cgroups; wi += gridDim.x) {
+    const int kb = static_cast<int>(wi / cgroups);
+    const int c = static_cast<int>(wi % cgroups) * 256 + tid;
+    if (c >= C) continue;
+    // the segment holding output columns [32kb, 32kb+32)
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_kofs[mid] <= kb * 32) lo = mid;
+      else hi = mid;
+    }
+    const int e = lo;
+    const int local = kb * 32 - s_kofs[e];
+    const int64_t seg_lo = offsets ? offsets[e] : 0;
+    const int seg = offsets ? offsets[e + 1] - offsets[e] : static_cast<int>(rows);
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float x = 0.f;
+      if (local + i < seg) {
+        const int64_t r = seg_lo + local + i;
+        const int src = src_row ? src_row[r] : static_cast<int>(r);
+        if (src >= 0) {
+          if (MODE == SEG_ROWS) {
+            x = bf16_bits_to_f32(in[r * C + c]);
+          } else if (MODE == SEG_GATHER) {
+            x = bf16_bits_to_f32(in[static_cast<int64_t>(src) * C + c]);
+          } else {
+            const float g = bf16_bits_to_f32(in[r * 2 * C + c]);
+            const float u = bf16_bits_to_f32(in[r * 2 * C + C + c]);
+            x = g * (1.f / (1.f + expf(-g))) * u;
+          }
+        }
+      }
+      v[i] = x;
+    }
+    uint32_t words[8];
+    const uint32_t sb = mx_encode_block<FP4>(v, words);
+    if (FP4) {
+      *reinterpret_cast<u32x4_t*>(codes + static_cast<int64_t>(c) * (kstride / 2) + kb * 16) =
+          u32x4_t{words[0], words[1], words[2], words[3]};
+    } else {
+      u32x4_t* o = reinterpret_cast<u32x4_t*>(codes + static_cast<int64_t>(c) * kstride + kb * 32);
+      o[0] = u32x4_t{words[0], words[1], words[2], words[3]};
+      o[1] = u32x4_t{words[4], words[5], words[6], words[7]};
+    }
+    scales[static_cast<int64_t>(c) * (kstride / 32) + kb] = static_cast<uint8_t>(sb);
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_combine_bwd(const void* dout, int dout_fmt, const int32_t* row_map,
+                               const int32_t* src_row, const float* topk_w, int T, int k, int H,
+                               int64_t rows, void* dy, hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(T >= 0 && k >= 1 && H > 0 && H % 8 == 0 && rows >= 0, MOE_ERR_INVALID_ARG,
+              "moe_combine_bwd: need T >= 0, k >= 1, H a positive multiple of 8, rows >= 0");
+  MOE_REQUIRE(dout_fmt == MOE_BF16 || dout_fmt == MOE_F32, MOE_ERR_UNSUPPORTED,
+              "moe_combine_bwd: dout_fmt must be MOE_BF16 or MOE_F32");
+  if (rows == 0) return MOE_OK;
+  MOE_REQUIRE(dy && src_row && (T == 0 || (dout && row_map && topk_w)), MOE_ERR_INVALID_ARG,
+              "moe_combine_bwd: null pointer");
+  MOE_REQUIRE(aligned16(dy) && (!dout || aligned16(dout)), MOE_ERR_ALIGNMENT,
+              "moe_combine_bwd: dout and dy must be 16-byte aligned");
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(rows, 16384));
+  if (dout_fmt == MOE_BF16)
+    hipLaunchKernelGGL(combine_bwd_kernel<MOE_BF16>, dim3(grid), dim3(256), 0, stream, dout, row_map,
+                       src_row, topk_w, k, H, rows, static_cast<uint16_t*>(dy));
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<MOE_F32>, dim3(grid), dim3(256), 0, stream, dout, row_map,
+                       src_row, topk_w, k, H, rows, static_cast<uint16_t*>(dy));
+  return check_launch("moe_combine_bwd");
+}
+
+extern "C" int64_t moe_segments_kstride(int64_t rows, int E) {
+  if (rows < 0 || E < 1) return -1;
+  return (rows + static_cast<int64_t>(E) * 127 + 127) / 128 * 128;
+}
+
+extern "C" int moe_quantize_mx_segments(const void* in, int mode, const int32_t* src_row,
+                                        const int32_t* offsets, int E, int64_t rows, int C,
+                                        int64_t kstride, int out_fmt, uint8_t* codes,
+                                        uint8_t* scales, int32_t* kofs, hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(E >= 1 && E <= kMaxE && C > 0 && rows >= 0, MOE_ERR_INVALID_ARG,
+              "moe_quantize_mx_segments: need 1 <= E <= 1024, C > 0, rows >= 0");
+  MOE_REQUIRE(mode >= SEG_ROWS && mode <= SEG_SWIGLU, MOE_ERR_INVALID_ARG,
+              "moe_quantize_mx_segments: mode must be 0 (rows), 1 (gather) or 2 (swiglu)");
+  MOE_REQUIRE(out_fmt == MOE_MXFP8_E4M3 || out_fmt == MOE_MXFP4_E2M1, MOE_ERR_UNSUPPORTED,
+              "moe_quantize_mx_segments: out_fmt must be an MX format");
+  MOE_REQUIRE(kstride >= moe_segments_kstride(rows, E) && kstride % 128 == 0, MOE_ERR_INVALID_ARG,
+              "moe_quantize_mx_segments: kstride below moe_segments_kstride(rows, E) or not a "
+              "multiple of 128");
+  MOE_REQUIRE(in && src_row && offsets && codes && scales && kofs, MOE_ERR_INVALID_ARG,
+              "moe_quantize_mx_segments: null pointer");
+  MOE_REQUIRE(aligned16(codes), MOE_ERR_ALIGNMENT, "moe_quantize_mx_segments: codes not 16-byte aligned");
+  const int64_t work = (kstride / 32) * ((C + 255) / 256);
+  const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>(work, 16384)));
+  const bool fp4 = out_fmt == MOE_MXFP4_E2M1;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, static_cast<const uint16_t*>(in),
+                       src_row, offsets, E, rows, C, kstride, 128, codes, scales, kofs);
+  };
+  if (mode == SEG_ROWS) fp4 ? go(quantize_segments_kernel<SEG_ROWS, true>) : go(quantize_segments_kernel<SEG_ROWS, false>);
+  else if (mode == SEG_GATHER) fp4 ? go(quantize_segments_kernel<SEG_GATHER, true>) : go(quantize_segments_kernel<SEG_GATHER, false>);
+  else fp4 ? go(quantize_segments_kernel<SEG_SWIGLU, true>) : go(quantize_segments_kernel<SEG_SWIGLU, false>);
+  return check_launch("moe_quantize_mx_segments");
+}
+
+namespace moe {
+// moe_quantize_mx with axis 1: [rows, K] -> K-major codes [K, rows] (E2M1:
+// [K, rows/2]) and scales [K, rows/32], blocks of 32 consecutive rows.
+int quantize_mx_columns(const void* in, int64_t rows, int K, int out_fmt, uint8_t* codes,
+                        uint8_t* scales, hipStream_t stream) {
+  const int64_t work = (rows / 32) * ((K + 255) / 256);
+  const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>(work, 16384)));
+  if (out_fmt == MOE_MXFP4_E2M1)
+    hipLaunchKernelGGL((quantize_segments_kernel<SEG_ROWS, true>), dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(in), nullptr, nullptr, 1, rows, K, rows, 32,
+                       codes, scales, nullptr);
+  else
+    hipLaunchKernelGGL((quantize_segments_kernel<SEG_ROWS, false>), dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(in), nullptr, nullptr, 1, rows, K, rows, 32,
+                       codes, scales, nullptr);
+  return check_launch("moe_quantize_mx");
+}
+}  // namespace moe

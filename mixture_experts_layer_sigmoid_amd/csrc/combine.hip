@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     for (int j = 0; j < k; ++j) {
-      const float wj = w[static_cast<int64_t>(t) * k + j];
+      const float wj = w ? w[static_cast<int64_t>(t) * k + j] : 1.f;
       const int64_t row = row_map[static_cast<int64_t>(t) * k + j];
       float v[8];
       load8<YF>(y, row * H + c * 8, v);
@@ -102,4 +102,31 @@ extern "C" int moe_combine(const void* y, int y_fmt, const int32_t* row_map, con
     else launch(combine_kernel<MOE_F32, MOE_F32>);
   }
   return check_launch("moe_combine");
+}
+
+// Summing un-permute for the backward: dx[t] = sum_j dx_perm[row_map[t, j]]
+// (the combine with unit weights and no shared row).
+extern "C" int moe_unpermute(const void* dx_perm, int fmt, const int32_t* row_map, int T, int k,
+                             int H, void* dx, int out_fmt, hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(T >= 0 && k >= 1 && H > 0 && H % 8 == 0, MOE_ERR_INVALID_ARG,
+              "moe_unpermute: need T >= 0, k >= 1, H a positive multiple of 8");
+  MOE_REQUIRE((fmt == MOE_F32 || fmt == MOE_BF16) && (out_fmt == MOE_F32 || out_fmt == MOE_BF16),
+              MOE_ERR_UNSUPPORTED, "moe_unpermute: formats must be MOE_F32 or MOE_BF16");
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(dx_perm && row_map && dx, MOE_ERR_INVALID_ARG, "moe_unpermute: null pointer");
+  MOE_REQUIRE(aligned16(dx_perm) && aligned16(dx), MOE_ERR_ALIGNMENT,
+              "moe_unpermute: dx_perm and dx must be 16-byte aligned");
+  const float* none = nullptr;
+  auto launch = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(T), dim3(256), 0, stream, dx_perm, row_map, none, nullptr, T, k, H, dx);
+  };
+  if (fmt == MOE_BF16) {
+    if (out_fmt == MOE_BF16) launch(combine_kernel<MOE_BF16, MOE_BF16>);
+    else launch(combine_kernel<MOE_BF16, MOE_F32>);
+  } else {
+    if (out_fmt == MOE_BF16) launch(combine_kernel<MOE_F32, MOE_BF16>);
+    else launch(combine_kernel<MOE_F32, MOE_F32>);
+  }
+  return check_launch("moe_unpermute");
 }

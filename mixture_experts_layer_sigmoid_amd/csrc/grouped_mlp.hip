@@ -50,7 +50,13 @@ namespace {
 constexpr int kMaxGroups = 1024;
 
 enum { OP_BF16 = 0, OP_FP8 = 1, OP_FP4 = 2 };
-enum { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
+enum { EPI_SWIGLU = 0, EPI_PLAIN = 1, EPI_DSWIGLU = 2 };
+// MODE_M: groups are row segments [offsets[e], offsets[e+1]) of A and of the
+//         output, K fixed (the forward GEMMs and the data gradients);
+// MODE_K: groups are K segments [kofs[e], kofs[e+1]) of A and B (both stored
+//         K-major), M and N fixed, one output matrix per group (the weight
+//         gradients).
+enum { MODE_M = 0, MODE_K = 1 };
 
 // Per-format constants for RB bytes of K per row per stage: MFMA k-steps per
 // stage (32x32x16 bf16 consumes 32 bytes of K per row, 32x32x64 E4M3 64
@@ -86,6 +92,14 @@ struct Args {
   int64_t out_sc_row_bytes;
   uint16_t* act_save;      // optional [rows, 2F] bf16 (fc1 only)
   int act_cols;            // 2F
+  // MODE_K
+  const int32_t* kofs;     // [E+1] K offsets (elements) of the groups
+  int m_blocks;            // row tiles of the fixed M
+  int64_t out_exp_bytes;   // bytes of one group's output matrix
+  int bits;                // bits per element of A and B
+  // EPI_DSWIGLU
+  const uint16_t* a_saved; // saved fc1 output A [rows, 2F] bf16 (gate | up)
+  uint16_t* da_bf16;       // optional bf16 copy of dA [rows, 2F]
 };
 
 template <int MMAX, int STAGES, int NCB, int OP, int RB>
@@ -170,7 +184,8 @@ __device__ __forceinline__ int weight_row(int nblk, int br, int up_row) {
 // WM:     wavefront groups along the rows (4 * WM wavefronts; wave w owns
 //         column group w % 4 and row blocks w / 4, w / 4 + WM, ...)
 // OCC:    workgroups resident per CU (persistent grid = 256 * OCC)
-template <int MMAX, int STAGES, int NCB, int WM, int OCC, int RB, int OP, int EPI, int OUTF>
+template <int MMAX, int STAGES, int NCB, int WM, int OCC, int RB, int OP, int EPI, int OUTF,
+          int MODE = MODE_M>
 __global__ __launch_bounds__(256 * WM) __attribute__((amdgpu_waves_per_eu(OCC * WM, OCC * WM)))
 void grouped_gemm_kernel(Args p) {
   using S = Smem<MMAX, STAGES, NCB, OP, RB>;
@@ -202,7 +217,7 @@ void grouped_gemm_kernel(Args p) {
   const int E = p.E;
 
   // ---- tile list: m-tiles per expert, inclusive prefix in s_mt[1..E] ----
-  {
+  if constexpr (MODE == MODE_M) {
     const int per = (E + NT - 1) / NT;
     const int lo = tid * per, hi = min(E, lo + per);
     int s = 0;
@@ -232,16 +247,29 @@ void grouped_gemm_kernel(Args p) {
     }
     __syncthreads();
   }
-  const int64_t total_tiles = static_cast<int64_t>(s_tot[0]) * p.n_blocks;
-  const XcdSlot xs = xcd_slot();
-  const int64_t c_lo = total_tiles * xs.xcd / kNumXcd;
-  const int64_t c_hi = total_tiles * (xs.xcd + 1) / kNumXcd;
+  // MODE_M: the tile list is cut into 8 contiguous chunks, one per XCD;
+  // MODE_K: plain grid stride, so the tiles of one group spread over every
+  // XCD (groups' K lengths are skewed; this balances the work)
+  int64_t t_first, t_end, t_step;
+  if constexpr (MODE == MODE_M) {
+    const int64_t total_tiles = static_cast<int64_t>(s_tot[0]) * p.n_blocks;
+    const XcdSlot xs = xcd_slot();
+    t_first = total_tiles * xs.xcd / kNumXcd + xs.slot;
+    t_end = total_tiles * (xs.xcd + 1) / kNumXcd;
+    t_step = xs.nslots;
+  } else {
+    t_first = blockIdx.x;
+    t_end = static_cast<int64_t>(E) * p.m_blocks * p.n_blocks;
+    t_step = gridDim.x;
+  }
 
-  for (int64_t t = c_lo + xs.slot; t < c_hi; t += xs.nslots) {
-    // ---- decode the tile: expert e (s_mt[e]*nb <= t < s_mt[e+1]*nb),
-    // then column block (slow) and row block (fast) inside the expert ----
-    int e;
-    {
+  for (int64_t t = t_first; t < t_end; t += t_step) {
+    int e, nblk, mblk, row0, nrows, KT;
+    int64_t kbyte0 = 0;        // MODE_K: byte offset of the group's K segment
+    int64_t kscale0 = 0;       // MODE_K: its offset in the scale rows (one per 32)
+    if constexpr (MODE == MODE_M) {
+      // ---- decode: expert e (s_mt[e]*nb <= t < s_mt[e+1]*nb), then column
+      // block (slow) and row block (fast) inside the expert ----
       int lo = 0, hi = E;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -249,17 +277,30 @@ void grouped_gemm_kernel(Args p) {
         else hi = mid;
       }
       e = lo;
+      const int mtiles = s_mt[e + 1] - s_mt[e];
+      const int64_t local = t - static_cast<int64_t>(s_mt[e]) * p.n_blocks;
+      nblk = static_cast<int>(local / mtiles);
+      mblk = static_cast<int>(local % mtiles);
+      const int seg_lo = p.offsets[e];
+      const int n_e = min(p.offsets[e + 1], (int)p.rows) - seg_lo;
+      // full MMAX-row tiles first, the remainder last (MFMA padding only in
+      // the last tile's final 32-row block)
+      row0 = seg_lo + mblk * MMAX;
+      nrows = min(MMAX, n_e - mblk * MMAX);
+      KT = p.k_stages;
+    } else {
+      const int64_t per = static_cast<int64_t>(p.m_blocks) * p.n_blocks;
+      e = static_cast<int>(t / per);
+      const int rem = static_cast<int>(t % per);
+      mblk = rem / p.n_blocks;
+      nblk = rem % p.n_blocks;
+      row0 = mblk * MMAX;
+      nrows = MMAX;
+      const int k0 = p.kofs[e], k1 = p.kofs[e + 1];
+      kbyte0 = static_cast<int64_t>(k0) * p.bits / 8;
+      kscale0 = k0 / 32;
+      KT = static_cast<int>((static_cast<int64_t>(k1 - k0) * p.bits / 8) / RB);
     }
-    const int mtiles = s_mt[e + 1] - s_mt[e];
-    const int64_t local = t - static_cast<int64_t>(s_mt[e]) * p.n_blocks;
-    const int nblk = static_cast<int>(local / mtiles);
-    const int mblk = static_cast<int>(local % mtiles);
-    const int seg_lo = p.offsets[e];
-    const int n_e = min(p.offsets[e + 1], (int)p.rows) - seg_lo;
-    // full MMAX-row tiles first, the remainder last (MFMA padding only in
-    // the last tile's final 32-row block)
-    const int row0 = seg_lo + mblk * MMAX;
-    const int nrows = min(MMAX, n_e - mblk * MMAX);
     if (nrows <= 0) continue;  // uniform across the workgroup
     const int nrb = (nrows + 31) >> 5;
 
@@ -273,13 +314,14 @@ void grouped_gemm_kernel(Args p) {
         src = p.gather[src];
         if (src < 0) src = 0;  // padding row: loads any valid row, h is zeroed
       }
-      a_src[i] = p.a + static_cast<int64_t>(src) * p.a_row_bytes + (((lane % kCpr) ^ swz_key<RB>(r)) << 4);
+      a_src[i] = p.a + static_cast<int64_t>(src) * p.a_row_bytes + kbyte0 +
+                 (((lane % kCpr) ^ swz_key<RB>(r)) << 4);
     }
     if (p.gather && EPI == EPI_SWIGLU) {
       for (int r = tid; r < MMAX; r += NT) s_src[r] = r < nrows ? p.gather[row0 + r] : 0;
     }
     const uint8_t* b_src[kBIns];
-    const uint8_t* bexp = p.b + static_cast<int64_t>(e) * p.b_exp_bytes;
+    const uint8_t* bexp = MODE == MODE_M ? p.b + static_cast<int64_t>(e) * p.b_exp_bytes : p.b + kbyte0;
 #pragma unroll
     for (int i = 0; i < kBIns; ++i) {
       const int br = kRpi * (wave + NW * i) + lane / kCpr;
@@ -304,9 +346,10 @@ void grouped_gemm_kernel(Args p) {
           src = p.gather[src];
           if (src < 0) src = 0;
         }
-        asc_src[q] = p.a_sc + static_cast<int64_t>(src) * p.a_sc_row_bytes + (lane % kDpr) * 4;
+        asc_src[q] = p.a_sc + static_cast<int64_t>(src) * p.a_sc_row_bytes + kscale0 + (lane % kDpr) * 4;
       }
-      const uint8_t* bsexp = p.b_sc + static_cast<int64_t>(e) * p.b_sc_exp_bytes;
+      const uint8_t* bsexp = MODE == MODE_M ? p.b_sc + static_cast<int64_t>(e) * p.b_sc_exp_bytes
+                                            : p.b_sc + kscale0;
 #pragma unroll
       for (int q = 0; q < (kBScIns + NW - 1) / NW; ++q) {
         const int r = min((wave + NW * q) * kScRows + lane / kDpr, kBR - 1);
@@ -360,7 +403,6 @@ void grouped_gemm_kernel(Args p) {
       }
     };
 
-    const int KT = p.k_stages;
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
       if (s < KT) issue(s);
@@ -560,14 +602,93 @@ void grouped_gemm_kernel(Args p) {
           }
         }
       }
-    } else {
+    } else if constexpr (EPI == EPI_PLAIN) {
+      uint8_t* obase = MODE == MODE_K ? p.out + static_cast<int64_t>(e) * p.out_exp_bytes : p.out;
       for (int i = tid; i < nrows * (kBR / 8); i += NT) {
         const int row = i / (kBR / 8), c0 = (i % (kBR / 8)) * 8;
         const float* v = cs + row * kCs + c0;
-        *reinterpret_cast<u32x4_t*>(p.out + static_cast<int64_t>(row0 + row) * p.out_row_bytes +
+        *reinterpret_cast<u32x4_t*>(obase + static_cast<int64_t>(row0 + row) * p.out_row_bytes +
                                     (static_cast<int64_t>(nblk) * kBR + c0) * 2) =
             u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                     pack_bf16x2(v[6], v[7])};
+      }
+    } else {
+      // dSwiGLU: the tile holds dH for columns [nblk*kBR, +kBR) of F; with the
+      // saved fc1 output (g | u) it gives dA = [dgate | dup]:
+      //   dgate = dH * u * sig(g) * (1 + g * (1 - sig(g))),  dup = dH * silu(g)
+      const int F = p.up_row;
+      const int64_t a2 = 2ll * F;  // elements per saved / dA row
+      if constexpr (OUTF == MOE_BF16) {
+        for (int i = tid; i < nrows * (kBR / 8); i += NT) {
+          const int row = i / (kBR / 8), c0 = (i % (kBR / 8)) * 8;
+          const int col = nblk * kBR + c0;
+          const int64_t grow = row0 + row;
+          const u32x4_t gw = *reinterpret_cast<const u32x4_t*>(p.a_saved + grow * a2 + col);
+          const u32x4_t uw = *reinterpret_cast<const u32x4_t*>(p.a_saved + grow * a2 + F + col);
+          float dg[8], du[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint32_t gb = (q & 1) ? (gw[q >> 1] & 0xFFFF0000u) : (gw[q >> 1] << 16);
+            const uint32_t ub = (q & 1) ? (uw[q >> 1] & 0xFFFF0000u) : (uw[q >> 1] << 16);
+            const float g = __uint_as_float(gb), u = __uint_as_float(ub);
+            const float dh = cs[row * kCs + c0 + q];
+            const float sig = 1.f / (1.f + expf(-g));
+            dg[q] = dh * u * sig * (1.f + g * (1.f - sig));
+            du[q] = dh * (g * sig);
+          }
+          uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + grow * a2;
+          *reinterpret_cast<u32x4_t*>(o + col) =
+              u32x4_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]), pack_bf16x2(dg[4], dg[5]),
+                      pack_bf16x2(dg[6], dg[7])};
+          *reinterpret_cast<u32x4_t*>(o + F + col) =
+              u32x4_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]), pack_bf16x2(du[4], du[5]),
+                      pack_bf16x2(du[6], du[7])};
+        }
+      } else {
+        constexpr bool fp4 = OUTF == MOE_MXFP4_E2M1;
+        constexpr int kBlkBytes = fp4 ? 16 : 32;
+        for (int i = tid; i < nrows * (kBR / 32); i += NT) {
+          const int row = i / (kBR / 32), blk = i % (kBR / 32);
+          const int col = nblk * kBR + blk * 32;
+          const int64_t grow = row0 + row;
+          float dg[32], du[32];
+#pragma unroll
+          for (int w8 = 0; w8 < 4; ++w8) {
+            const u32x4_t gw = *reinterpret_cast<const u32x4_t*>(p.a_saved + grow * a2 + col + w8 * 8);
+            const u32x4_t uw = *reinterpret_cast<const u32x4_t*>(p.a_saved + grow * a2 + F + col + w8 * 8);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const uint32_t gb = (q & 1) ? (gw[q >> 1] & 0xFFFF0000u) : (gw[q >> 1] << 16);
+              const uint32_t ub = (q & 1) ? (uw[q >> 1] & 0xFFFF0000u) : (uw[q >> 1] << 16);
+              const float g = __uint_as_float(gb), u = __uint_as_float(ub);
+              const float dh = cs[row * kCs + blk * 32 + w8 * 8 + q];
+              const float sig = 1.f / (1.f + expf(-g));
+              dg[w8 * 8 + q] = dh * u * sig * (1.f + g * (1.f - sig));
+              du[w8 * 8 + q] = dh * (g * sig);
+            }
+          }
+          uint32_t words[8];
+          uint8_t* orow = p.out + grow * p.out_row_bytes;
+          uint8_t* srow = p.out_sc + grow * p.out_sc_row_bytes;
+#pragma unroll
+          for (int part = 0; part < 2; ++part) {
+            const float* v = part ? du : dg;
+            const int c = part ? F + col : col;
+            const uint32_t sb = mx_encode_block<fp4>(v, words);
+            u32x4_t* o = reinterpret_cast<u32x4_t*>(orow + (c / 32) * kBlkBytes);
+            o[0] = u32x4_t{words[0], words[1], words[2], words[3]};
+            if (!fp4) o[1] = u32x4_t{words[4], words[5], words[6], words[7]};
+            srow[c / 32] = static_cast<uint8_t>(sb);
+            if (p.da_bf16) {
+              uint16_t* ob = p.da_bf16 + grow * a2 + c;
+#pragma unroll
+              for (int w8 = 0; w8 < 4; ++w8)
+                *reinterpret_cast<u32x4_t*>(ob + w8 * 8) =
+                    u32x4_t{pack_bf16x2(v[w8 * 8 + 0], v[w8 * 8 + 1]), pack_bf16x2(v[w8 * 8 + 2], v[w8 * 8 + 3]),
+                            pack_bf16x2(v[w8 * 8 + 4], v[w8 * 8 + 5]), pack_bf16x2(v[w8 * 8 + 6], v[w8 * 8 + 7])};
+            }
+          }
+        }
       }
     }
     __syncthreads();  // LDS reused by the next tile
@@ -638,12 +759,14 @@ __global__ __launch_bounds__(256) void fc2_f32_kernel(const float* __restrict__ 
   }
 }
 
-template <int MMAX, int STAGES, int NCB, int WM, int OCC, int RB, int OP, int EPI, int OUTF>
+template <int MMAX, int STAGES, int NCB, int WM, int OCC, int RB, int OP, int EPI, int OUTF,
+          int MODE = MODE_M>
 int launch_gemm(Args a, hipStream_t stream) {
   a.n_blocks /= NCB;
-  a.k_stages = static_cast<int>(a.a_row_bytes / RB);
+  if (MODE == MODE_M) a.k_stages = static_cast<int>(a.a_row_bytes / RB);
+  else a.m_blocks /= MMAX / 32;  // caller passes M / 32
   const int grid = kNumCu * OCC;  // persistent: OCC workgroups per CU
-  hipLaunchKernelGGL((grouped_gemm_kernel<MMAX, STAGES, NCB, WM, OCC, RB, OP, EPI, OUTF>), dim3(grid),
+  hipLaunchKernelGGL((grouped_gemm_kernel<MMAX, STAGES, NCB, WM, OCC, RB, OP, EPI, OUTF, MODE>), dim3(grid),
                      dim3(256 * WM), 0, stream, a);
   return check_launch("grouped GEMM");
 }
@@ -880,4 +1003,131 @@ extern "C" int moe_grouped_mlp_fwd(const void* a, const uint8_t* a_scales, int a
                 h_sc, stream);
   if (st) return st;
   return fc2_impl(h, h_sc, a_fmt, w2, w2_scales, offsets, E, H, F, rows, y, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Backward grouped GEMMs (page "[PyTorch] DeepSeekV3Layer: full MoE
+// transformer layer (MLA + DeepSeek MoE)", Performance section, "Where the
+// time goes": dGLU bwd and wgrad of the fused grouped MLP).
+
+extern "C" int moe_grouped_fc2_dgrad_dswiglu(const void* dy, const uint8_t* dy_scales, int fmt,
+                                             const void* w2t, const uint8_t* w2t_scales,
+                                             const int32_t* offsets, int E, int H, int F,
+                                             int64_t rows, const void* act_save, void* da,
+                                             uint8_t* da_scales, void* da_bf16,
+                                             hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(E >= 1 && E <= kMaxGroups && H > 0 && F > 0 && rows >= 0, MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc2_dgrad_dswiglu: need 1 <= E <= 1024, H > 0, F > 0, rows >= 0");
+  MOE_REQUIRE(fmt == MOE_BF16 || fmt == MOE_MXFP8_E4M3 || fmt == MOE_MXFP4_E2M1, MOE_ERR_UNSUPPORTED,
+              "moe_grouped_fc2_dgrad_dswiglu: fmt must be BF16, MXFP8 or MXFP4");
+  const int kmul = fmt == MOE_MXFP4_E2M1 ? 256 : 128;
+  MOE_REQUIRE(H % kmul == 0 && F % 128 == 0, MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc2_dgrad_dswiglu: need H % 128 == 0 (256 for MXFP4) and F % 128 == 0");
+  MOE_REQUIRE(offsets && w2t && act_save && da && (rows == 0 || dy), MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc2_dgrad_dswiglu: null pointer");
+  if (is_mx(fmt))
+    MOE_REQUIRE(dy_scales && w2t_scales && da_scales && scale_aligned(dy_scales) &&
+                    scale_aligned(w2t_scales),
+                MOE_ERR_INVALID_ARG, "moe_grouped_fc2_dgrad_dswiglu: MX needs 4-byte aligned scales");
+  MOE_REQUIRE(aligned16(dy) && aligned16(w2t) && aligned16(act_save) && aligned16(da) &&
+                  (!da_bf16 || aligned16(da_bf16)),
+              MOE_ERR_ALIGNMENT, "moe_grouped_fc2_dgrad_dswiglu: tensors must be 16-byte aligned");
+  if (rows == 0) return MOE_OK;
+  const int bits = elem_bits(fmt);
+  Args g{};
+  g.a = static_cast<const uint8_t*>(dy);
+  g.a_row_bytes = static_cast<int64_t>(H) * bits / 8;
+  g.a_sc = dy_scales;
+  g.a_sc_row_bytes = H / 32;
+  g.b = static_cast<const uint8_t*>(w2t);
+  g.b_row_bytes = g.a_row_bytes;
+  g.b_exp_bytes = static_cast<int64_t>(F) * g.b_row_bytes;
+  g.b_sc = w2t_scales;
+  g.b_sc_row_bytes = H / 32;
+  g.b_sc_exp_bytes = static_cast<int64_t>(F) * (H / 32);
+  g.up_row = F;
+  g.offsets = offsets;
+  g.E = E;
+  g.rows = rows;
+  g.n_blocks = F / 128;
+  g.out = static_cast<uint8_t*>(da);
+  g.out_row_bytes = 2ll * F * bits / 8;
+  g.out_sc = da_scales;
+  g.out_sc_row_bytes = 2 * F / 32;
+  g.a_saved = static_cast<const uint16_t*>(act_save);
+  g.da_bf16 = static_cast<uint16_t*>(da_bf16);
+  const bool wide = F % 256 == 0;
+  if (fmt == MOE_BF16)
+    return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_BF16, EPI_DSWIGLU, MOE_BF16>(g, stream)
+                : launch_gemm<256, 3, 1, 2, 1, 128, OP_BF16, EPI_DSWIGLU, MOE_BF16>(g, stream);
+  if (fmt == MOE_MXFP8_E4M3)
+    return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP8, EPI_DSWIGLU, MOE_MXFP8_E4M3>(g, stream)
+                : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP8, EPI_DSWIGLU, MOE_MXFP8_E4M3>(g, stream);
+  return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP4, EPI_DSWIGLU, MOE_MXFP4_E2M1>(g, stream)
+              : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP4, EPI_DSWIGLU, MOE_MXFP4_E2M1>(g, stream);
+}
+
+extern "C" int moe_grouped_fc1_dgrad(const void* da, const uint8_t* da_scales, int fmt,
+                                     const void* w1t, const uint8_t* w1t_scales,
+                                     const int32_t* offsets, int E, int H, int F, int64_t rows,
+                                     void* dx_perm, hipStream_t stream) {
+  // dX rows = dA . W1 with W1 stored transposed [E, H, 2F] (contraction over
+  // 2F contiguous): the fc2 kernel with 2F in place of F.
+  clear_error();
+  MOE_REQUIRE(E >= 1 && E <= kMaxGroups && H > 0 && F > 0 && rows >= 0, MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc1_dgrad: need 1 <= E <= 1024, H > 0, F > 0, rows >= 0");
+  MOE_REQUIRE(fmt == MOE_BF16 || fmt == MOE_MXFP8_E4M3 || fmt == MOE_MXFP4_E2M1, MOE_ERR_UNSUPPORTED,
+              "moe_grouped_fc1_dgrad: fmt must be BF16, MXFP8 or MXFP4");
+  int st = check_formats("moe_grouped_fc1_dgrad", fmt, fmt, MOE_BF16, H, 2 * F);
+  if (st) return st;
+  MOE_REQUIRE(offsets && w1t && dx_perm && (rows == 0 || da), MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc1_dgrad: null pointer");
+  if (is_mx(fmt))
+    MOE_REQUIRE(da_scales && w1t_scales && scale_aligned(da_scales) && scale_aligned(w1t_scales),
+                MOE_ERR_INVALID_ARG, "moe_grouped_fc1_dgrad: MX needs 4-byte aligned scales");
+  MOE_REQUIRE(aligned16(da) && aligned16(w1t) && aligned16(dx_perm), MOE_ERR_ALIGNMENT,
+              "moe_grouped_fc1_dgrad: tensors must be 16-byte aligned");
+  if (rows == 0) return MOE_OK;
+  return fc2_impl(da, da_scales, fmt, w1t, w1t_scales, offsets, E, H, 2 * F, rows, dx_perm, stream);
+}
+
+extern "C" int moe_grouped_wgrad(const void* at, const uint8_t* at_scales, const void* bt,
+                                 const uint8_t* bt_scales, int fmt, const int32_t* kofs, int E,
+                                 int M, int N, int64_t kstride, void* dw, hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(E >= 1 && E <= kMaxGroups && M > 0 && N > 0 && kstride > 0 && kstride % 128 == 0,
+              MOE_ERR_INVALID_ARG,
+              "moe_grouped_wgrad: need 1 <= E <= 1024, M, N > 0, kstride a positive multiple of 128");
+  MOE_REQUIRE(fmt == MOE_MXFP8_E4M3, MOE_ERR_UNSUPPORTED, "moe_grouped_wgrad: fmt must be MXFP8");
+  const bool wide = M % 128 == 0 && N % 256 == 0;
+  MOE_REQUIRE(wide || (M % 256 == 0 && N % 128 == 0), MOE_ERR_INVALID_ARG,
+              "moe_grouped_wgrad: need M % 128 == 0 and N % 256 == 0, or M % 256 == 0 and N % 128 == 0");
+  MOE_REQUIRE(at && bt && at_scales && bt_scales && kofs && dw, MOE_ERR_INVALID_ARG,
+              "moe_grouped_wgrad: null pointer");
+  MOE_REQUIRE(aligned16(at) && aligned16(bt) && aligned16(dw) && scale_aligned(at_scales) &&
+                  scale_aligned(bt_scales),
+              MOE_ERR_ALIGNMENT, "moe_grouped_wgrad: tensors must be 16-byte aligned");
+  const int bits = elem_bits(fmt);
+  Args g{};
+  g.a = static_cast<const uint8_t*>(at);
+  g.a_row_bytes = kstride * bits / 8;
+  g.a_sc = at_scales;
+  g.a_sc_row_bytes = kstride / 32;
+  g.b = static_cast<const uint8_t*>(bt);
+  g.b_row_bytes = g.a_row_bytes;
+  g.b_sc = bt_scales;
+  g.b_sc_row_bytes = kstride / 32;
+  g.kofs = kofs;
+  g.bits = bits;
+  g.E = E;
+  g.rows = M;
+  g.m_blocks = M / 32;
+  g.n_blocks = N / 128;
+  g.out = static_cast<uint8_t*>(dw);
+  g.out_row_bytes = 2ll * N;
+  g.out_exp_bytes = 2ll * M * N;
+  // segments are padded to 128 elements = one 128-byte stage of E4M3
+  return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP8, EPI_PLAIN, MOE_BF16, MODE_K>(g, stream)
+              : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP8, EPI_PLAIN, MOE_BF16, MODE_K>(g, stream);
 }

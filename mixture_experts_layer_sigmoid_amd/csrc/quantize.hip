@@ -13,6 +13,8 @@
 #include "mx_codec.h"
 
 namespace moe {
+int quantize_mx_columns(const void* in, int64_t rows, int K, int out_fmt, uint8_t* codes,
+                        uint8_t* scales, hipStream_t stream);
 namespace {
 
 template <int IN_FMT, bool FP4>
@@ -76,11 +78,16 @@ extern "C" int moe_quantize_mx(const void* in, int in_fmt, int64_t rows, int K, 
               "moe_quantize_mx: in_fmt must be MOE_F32 or MOE_BF16");
   MOE_REQUIRE(out_fmt == MOE_MXFP8_E4M3 || out_fmt == MOE_MXFP4_E2M1, MOE_ERR_UNSUPPORTED,
               "moe_quantize_mx: out_fmt must be an MX format");
-  MOE_REQUIRE(axis == 0, MOE_ERR_UNSUPPORTED, "moe_quantize_mx: only axis 0 (along K)");
+  MOE_REQUIRE(axis == 0 || axis == 1, MOE_ERR_INVALID_ARG, "moe_quantize_mx: axis must be 0 or 1");
+  MOE_REQUIRE(axis == 0 || in_fmt == MOE_BF16, MOE_ERR_UNSUPPORTED,
+              "moe_quantize_mx: axis 1 takes bf16 input");
+  MOE_REQUIRE(axis == 0 || rows % 32 == 0, MOE_ERR_INVALID_ARG,
+              "moe_quantize_mx: axis 1 needs rows % 32 == 0");
   if (rows == 0) return MOE_OK;
   MOE_REQUIRE(in && codes && scales, MOE_ERR_INVALID_ARG, "moe_quantize_mx: null pointer");
   MOE_REQUIRE(aligned16(in) && aligned16(codes), MOE_ERR_ALIGNMENT,
               "moe_quantize_mx: in and codes must be 16-byte aligned");
+  if (axis == 1) return quantize_mx_columns(in, rows, K, out_fmt, codes, scales, stream);
   const int64_t nblocks = rows * (K / 32);
   const int64_t want = (nblocks + 255) / 256;
   const int grid = static_cast<int>(want < 65536 ? want : 65536);

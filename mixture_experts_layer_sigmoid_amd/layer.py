@@ -8,6 +8,13 @@ and then issues, on one stream:
       -> [moe_grouped_mlp_fwd for the shared expert, E = 1]
       -> moe_combine
 
+MoEBackward runs the backward of the routed expert path (MXFP8), reusing
+the forward's routing and maps:
+
+    moe_combine_bwd -> moe_quantize_mx (dY) -> moe_grouped_fc2_dgrad_dswiglu
+      -> moe_grouped_fc1_dgrad -> moe_unpermute
+      -> moe_quantize_mx_segments (dY, h, dA, x) -> moe_grouped_wgrad (dW2, dW1)
+
 Only marshalling happens here; every step of the layer runs in the HIP
 library.
 """
@@ -43,27 +50,56 @@ def quantize_mx(t: torch.Tensor, fmt: str, stream=None):
     return codes, scales
 
 
+def quantize_mx_t(t: torch.Tensor, fmt: str, stream=None):
+    """MX-quantize each [R, K] bf16 matrix of a [..., R, K] tensor along R
+    (moe_quantize_mx with axis 1), giving the transposed K-major copy:
+    codes [..., K, R or R/2], scales [..., K, R/32]."""
+    R, K = t.shape[-2], t.shape[-1]
+    lead = t.shape[:-2]
+    codes = torch.empty(lead + (K, code_cols(R, fmt)), dtype=torch.uint8, device=t.device)
+    scales = torch.empty(lead + (K, R // 32), dtype=torch.uint8, device=t.device)
+    flat_t, flat_c, flat_s = t.reshape(-1, R, K), codes.view(-1, K, codes.shape[-1]), \
+        scales.view(-1, K, R // 32)
+    for i in range(flat_t.shape[0]):
+        L.moe_quantize_mx(flat_t[i], L.MOE_BF16, R, K, 1, FMT[fmt], flat_c[i], flat_s[i], stream)
+    return codes, scales
+
+
 @dataclass
 class ExpertWeights:
     """Stored expert weights: w1 [E, 2F, H], w2 [E, H, F] in the layer
-    format (MX: codes, with scales w1_sc [E, 2F, H/32], w2_sc [E, H, F/32])."""
+    format (MX: codes, with scales w1_sc [E, 2F, H/32], w2_sc [E, H, F/32]).
+    With `transposed`, also the copies the backward's data-gradient GEMMs
+    contract over: w1t [E, H, 2F] (blocks along 2F), w2t [E, F, H] (blocks
+    along H), quantized from the same masters."""
     w1: torch.Tensor
     w2: torch.Tensor
     w1_sc: torch.Tensor | None = None
     w2_sc: torch.Tensor | None = None
+    w1t: torch.Tensor | None = None
+    w2t: torch.Tensor | None = None
+    w1t_sc: torch.Tensor | None = None
+    w2t_sc: torch.Tensor | None = None
 
     @staticmethod
-    def from_dense(w1: torch.Tensor, w2: torch.Tensor, fmt: str, stream=None) -> "ExpertWeights":
+    def from_dense(w1: torch.Tensor, w2: torch.Tensor, fmt: str, stream=None,
+                   transposed: bool = False) -> "ExpertWeights":
         if not is_mx(fmt):
+            if transposed:
+                raise ValueError("transposed weight copies are built for MX formats only")
             return ExpertWeights(w1, w2)
         c1, s1 = quantize_mx(w1, fmt, stream)
         c2, s2 = quantize_mx(w2, fmt, stream)
-        return ExpertWeights(c1, c2, s1, s2)
+        ew = ExpertWeights(c1, c2, s1, s2)
+        if transposed:
+            ew.w1t, ew.w1t_sc = quantize_mx_t(w1, fmt, stream)
+            ew.w2t, ew.w2t_sc = quantize_mx_t(w2, fmt, stream)
+        return ew
 
 
 class MoEForward:
     def __init__(self, *, T, H, F, E, n_group, topk_group, k, routed_scale, fmt,
-                 F_shared=0, align=1, device="cuda", keep_logits=False):
+                 F_shared=0, align=1, device="cuda", keep_logits=False, save_act=False):
         self.T, self.H, self.F, self.E = T, H, F, E
         self.n_group, self.topk_group, self.k = n_group, topk_group, k
         self.routed_scale, self.fmt, self.F_shared, self.align = routed_scale, fmt, F_shared, align
@@ -88,6 +124,9 @@ class MoEForward:
             self.xq = self.xq_sc = None
         self.y_rows = torch.empty((max(1, self.bound), H), dtype=act, device=dev)
         self.h, self.h_sc = self._h_buffers(max(1, self.bound), F, dev)
+        # fc1 output (gate | up) per expert row, kept for the backward
+        self.act_save = (torch.empty((max(1, self.bound), 2 * F), dtype=torch.bfloat16, device=dev)
+                         if save_act else None)
         if F_shared:
             self.shared_offsets = torch.tensor([0, T], **i32)
             self.y_shared = torch.empty((T, H), dtype=act, device=dev)
@@ -122,7 +161,7 @@ class MoEForward:
         a, a_sc = (self.xq, self.xq_sc) if is_mx(self.fmt) else (x, None)
         f = FMT[self.fmt]
         L.moe_grouped_fc1_swiglu(a, a_sc, f, self.src_row, ew.w1, ew.w1_sc, f, self.offsets, self.E,
-                                 self.H, self.F, self.bound, None, self.h, self.h_sc, stream)
+                                 self.H, self.F, self.bound, self.act_save, self.h, self.h_sc, stream)
 
     def experts_fc2(self, ew: ExpertWeights, stream=None):
         f = FMT[self.fmt]
@@ -158,8 +197,78 @@ class MoEForward:
         return self.out
 
     @classmethod
-    def for_config(cls, cfg, device="cuda", keep_logits=False, T=None):
+    def for_config(cls, cfg, device="cuda", keep_logits=False, T=None, save_act=False):
         return cls(T=cfg.T if T is None else T, H=cfg.H, F=cfg.F, E=cfg.E, n_group=cfg.n_group,
                    topk_group=cfg.topk_group, k=cfg.k, routed_scale=cfg.routed_scale, fmt=cfg.fmt,
                    F_shared=cfg.F_shared if cfg.n_shared else 0, align=cfg.align, device=device,
-                   keep_logits=keep_logits)
+                   keep_logits=keep_logits, save_act=save_act)
+
+
+class MoEBackward:
+    """Backward of the routed experts of one MoEForward pass (built with
+    save_act=True, MXFP8). Produces dx [T, H] (gradient through the routed
+    experts) and the weight gradients dw1 [E, 2F, H], dw2 [E, H, F] (bf16).
+    Routing weights are constants and the quantizers pass gradients straight
+    through."""
+
+    def __init__(self, fwd: MoEForward):
+        if fwd.fmt != "mxfp8":
+            raise ValueError("the backward runs in MXFP8")
+        if fwd.act_save is None:
+            raise ValueError("the forward must keep its fc1 output (save_act=True)")
+        self.fwd = fwd
+        T, H, F, E, bound = fwd.T, fwd.H, fwd.F, fwd.E, max(1, fwd.bound)
+        dev = fwd.topk_idx.device
+        u8, bf = dict(dtype=torch.uint8, device=dev), dict(dtype=torch.bfloat16, device=dev)
+        self.dy = torch.empty((bound, H), **bf)
+        self.dy_q = torch.empty((bound, H), **u8)
+        self.dy_sc = torch.empty((bound, H // 32), **u8)
+        self.da = torch.empty((bound, 2 * F), **u8)
+        self.da_sc = torch.empty((bound, 2 * F // 32), **u8)
+        self.da_bf16 = torch.empty((bound, 2 * F), **bf)
+        self.dx_perm = torch.empty((bound, H), **bf)
+        self.dx = torch.empty((T, H), **bf)
+        ks = L.moe_segments_kstride(fwd.bound, E)
+        self.kstride = ks
+        self.kofs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        self.dyT, self.dyT_sc = torch.empty((H, ks), **u8), torch.empty((H, ks // 32), **u8)
+        self.hT, self.hT_sc = torch.empty((F, ks), **u8), torch.empty((F, ks // 32), **u8)
+        self.daT, self.daT_sc = torch.empty((2 * F, ks), **u8), torch.empty((2 * F, ks // 32), **u8)
+        self.xT, self.xT_sc = torch.empty((H, ks), **u8), torch.empty((H, ks // 32), **u8)
+        self.dw1 = torch.empty((E, 2 * F, H), **bf)
+        self.dw2 = torch.empty((E, H, F), **bf)
+
+    def data_grad(self, dout, ew: ExpertWeights, stream=None):
+        """dY rows -> dA (SwiGLU backward fused) -> dX rows -> dx."""
+        f, fw = FMT["mxfp8"], self.fwd
+        T, H, F, E, k, rows = fw.T, fw.H, fw.F, fw.E, fw.k, fw.bound
+        L.moe_combine_bwd(dout, fw.act_fmt, fw.row_map, fw.src_row, fw.topk_w, T, k, H, rows,
+                          self.dy, stream)
+        L.moe_quantize_mx(self.dy, L.MOE_BF16, rows, H, 0, f, self.dy_q, self.dy_sc, stream)
+        L.moe_grouped_fc2_dgrad_dswiglu(self.dy_q, self.dy_sc, f, ew.w2t, ew.w2t_sc, fw.offsets,
+                                        E, H, F, rows, fw.act_save, self.da, self.da_sc,
+                                        self.da_bf16, stream)
+        L.moe_grouped_fc1_dgrad(self.da, self.da_sc, f, ew.w1t, ew.w1t_sc, fw.offsets, E, H, F,
+                                rows, self.dx_perm, stream)
+        L.moe_unpermute(self.dx_perm, L.MOE_BF16, fw.row_map, T, k, H, self.dx, L.MOE_BF16, stream)
+
+    def weight_grad(self, x, stream=None):
+        """dW2 = dY^T h and dW1 = dA^T x per expert, contracting over the
+        expert's rows (MX blocks of 32 rows of the segment)."""
+        f, fw = FMT["mxfp8"], self.fwd
+        H, F, E, rows, ks = fw.H, fw.F, fw.E, fw.bound, self.kstride
+        seg = lambda src, mode, C, c, s: L.moe_quantize_mx_segments(
+            src, mode, fw.src_row, fw.offsets, E, rows, C, ks, f, c, s, self.kofs, stream)
+        seg(self.dy, 0, H, self.dyT, self.dyT_sc)
+        seg(fw.act_save, 2, F, self.hT, self.hT_sc)
+        L.moe_grouped_wgrad(self.dyT, self.dyT_sc, self.hT, self.hT_sc, f, self.kofs, E, H, F, ks,
+                            self.dw2, stream)
+        seg(self.da_bf16, 0, 2 * F, self.daT, self.daT_sc)
+        seg(x, 1, H, self.xT, self.xT_sc)
+        L.moe_grouped_wgrad(self.daT, self.daT_sc, self.xT, self.xT_sc, f, self.kofs, E, 2 * F, H,
+                            ks, self.dw1, stream)
+
+    def __call__(self, dout, x, ew: ExpertWeights, stream=None):
+        self.data_grad(dout, ew, stream)
+        self.weight_grad(x, stream)
+        return self.dx, self.dw1, self.dw2

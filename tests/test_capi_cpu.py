@@ -75,7 +75,9 @@ def test_quantize_validation(lib):
                                         k.get("K", 64), k.get("axis", 0), k.get("fo", 2),
                                         k.get("c", A), k.get("s", A), None)
     assert q(K=48) == INVALID
-    assert q(axis=1) == UNSUPPORTED
+    assert q(axis=2) == INVALID
+    assert q(axis=1, fi=0) == UNSUPPORTED       # axis 1 takes bf16 only
+    assert q(axis=1, rows=40) == INVALID        # axis 1 needs rows % 32 == 0
     assert q(fo=1) == UNSUPPORTED
     assert q(fi=2) == UNSUPPORTED
     assert q(c=A + 4) == ALIGN
@@ -129,3 +131,39 @@ def test_binding_raises_with_message(lib):
     with pytest.raises(moe.MoEError) as ei:
         L._check("moe_route", _route(lib, E=0))
     assert "E must be" in str(ei.value)
+
+
+def test_backward_validation(lib):
+    assert lib.moe_segments_kstride(1000, 8) == ((1000 + 8 * 127 + 127) // 128) * 128
+    assert lib.moe_segments_kstride(-1, 8) == -1
+    assert lib.moe_segments_kstride(0, 0) == -1
+    # combine backward: bad k, unsupported dout format, alignment
+    cb = lambda **k: lib.moe_combine_bwd(k.get("d", A), k.get("df", 1), A, A, A, 4, k.get("k", 2),
+                                         64, 32, k.get("dy", A), None)
+    assert cb(k=0) == INVALID
+    assert cb(df=2) == UNSUPPORTED
+    assert cb(dy=A + 2) == ALIGN
+    un = lambda **k: lib.moe_unpermute(A, k.get("f", 1), A, 4, 2, k.get("H", 64), A,
+                                       k.get("of", 1), None)
+    assert un(H=60) == INVALID
+    assert un(of=3) == UNSUPPORTED
+    qs = lambda **k: lib.moe_quantize_mx_segments(
+        A, k.get("mode", 0), A, A, 4, k.get("rows", 128), 64, k.get("ks", 1024), k.get("fo", 2),
+        A, A, A, None)
+    assert qs(mode=3) == INVALID
+    assert qs(fo=1) == UNSUPPORTED
+    assert qs(ks=256) == INVALID                  # below moe_segments_kstride(128, 4)
+    assert lib.moe_quantize_mx_segments(A, 0, None, A, 4, 128, 64, 1024, 2, A, A, A, None) == INVALID
+    # grouped GEMMs: bad shapes and formats are rejected before any launch
+    d2 = lambda **k: lib.moe_grouped_fc2_dgrad_dswiglu(
+        A, A, k.get("f", 2), A, A, A, 4, k.get("H", 256), k.get("F", 128), 64, A, A, A, None, None)
+    assert d2(H=200) == INVALID
+    assert d2(f=0) == UNSUPPORTED
+    d1 = lambda **k: lib.moe_grouped_fc1_dgrad(A, A, k.get("f", 2), A, A, A, 4, k.get("H", 256),
+                                               k.get("F", 128), 64, A, None)
+    assert d1(F=100) == INVALID
+    wg = lambda **k: lib.moe_grouped_wgrad(A, A, A, A, k.get("f", 2), A, 4, k.get("M", 256),
+                                           k.get("N", 256), k.get("ks", 1024), A, None)
+    assert wg(f=3) == UNSUPPORTED
+    assert wg(M=96) == INVALID
+    assert wg(ks=1000) == INVALID

@@ -1,0 +1,276 @@
+"""GPU parity of the MXFP8 backward of the routed expert path against the
+oracle (oracle.backward), stage by stage and end to end.
+
+Stages get the same seeded synthetic inputs on both sides:
+* combine backward (dY rows) and the summing un-permute: bit-exact;
+* the transposed (axis 1) weight quantization and the segment-transposed
+  activation quantization (rows / gathered tokens): bit-exact codes and
+  scales; the recomputed-SwiGLU mode within rounding of silu;
+* the grouped weight-gradient GEMM on ragged segments (empty, shorter than
+  one 128-row stage, several stages): relative L2 within the MXFP8 bar.
+End to end: the reduced skewed config (every expert, zero-row experts give
+exact zeros) and the full-size one on a sampled light expert plus the
+zero-row experts, with a property check of the un-permute on sampled
+tokens."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_sigmoid_amd as moe
+from moe_synth import configs, gen
+from oracle import backward as obw, mx as omx, permute as pm, routing as rt
+from tests.gpu_util import certified_tie_mismatches, dev, device_inputs, host, log, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+I32 = dict(dtype=torch.int32, device="cuda")
+
+
+def _bf16(a):
+    return gen.round_to_storage(np.asarray(a, np.float32), "bf16")
+
+
+def _maps(T, E, k, align, seed, n_empty=3):
+    """Seeded routing with distinct experts per token, the last n_empty
+    experts unused and expert 0 heavy (several 128-row stages)."""
+    g = np.random.default_rng(seed)
+    idx = np.stack([g.permutation(E - n_empty)[:k] for _ in range(T)]).astype(np.int32)
+    for t in g.permutation(T)[: (2 * T) // 3]:
+        if 0 not in idx[t]:
+            idx[t, 0] = 0
+    counts, offsets, row_map, src = pm.permute_maps(idx, E, align)
+    return idx, counts, offsets, row_map, src
+
+
+def test_combine_bwd_and_unpermute(gpu_lib):
+    T, E, k, H = 211, 16, 4, 384
+    log(f"combine backward / unpermute T={T} E={E} k={k} H={H}")
+    idx, counts, offsets, row_map, src = _maps(T, E, k, 32, 1)
+    bound = len(src)
+    g = np.random.default_rng(2)
+    dout = _bf16(g.standard_normal((T, H)))
+    w = g.uniform(0.05, 1.0, (T, k)).astype(np.float32)
+    dy = torch.full((bound, H), 3.0, dtype=torch.bfloat16, device="cuda")
+    rm, sr = torch.from_numpy(row_map.astype(np.int32)).cuda(), torch.from_numpy(src.astype(np.int32)).cuda()
+    moe.moe_combine_bwd(dev(dout, "bf16"), moe.MOE_BF16, rm, sr, dev(w), T, k, H, bound, dy)
+    torch.cuda.synchronize()
+    ref = np.zeros((bound, H), np.float32)
+    for t in range(T):
+        for j in range(k):
+            ref[row_map[t, j]] = w[t, j] * dout[t]
+    assert np.array_equal(host(dy), _bf16(ref))
+    # un-permute of random expert rows: fp32 sums in slot order, bf16 out
+    rows = _bf16(g.standard_normal((bound, H)))
+    dx = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_unpermute(dev(rows, "bf16"), moe.MOE_BF16, rm, T, k, H, dx, moe.MOE_BF16)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dx), _bf16(pm.unpermute_sum(rows, row_map)))
+    dxf = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    moe.moe_unpermute(dev(rows, "bf16"), moe.MOE_BF16, rm, T, k, H, dxf, moe.MOE_F32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dxf), pm.unpermute_sum(rows, row_map))
+
+
+@pytest.mark.parametrize("fmt,R,K", [("mxfp8", 96, 160), ("mxfp8", 512, 384), ("mxfp4", 256, 96)])
+def test_quantize_axis1_transposed(gpu_lib, fmt, R, K):
+    log(f"axis-1 quantize {fmt} R={R} K={K}")
+    g = np.random.default_rng(R + K)
+    v = _bf16(g.standard_normal((R, K)) * np.exp2(g.integers(-6, 6, (R, 1))))
+    v[:32, 5] = 0.0                       # an all-zero block
+    codes, scales = moe.quantize_mx_t(dev(v, "bf16"), fmt)
+    torch.cuda.synchronize()
+    ec, es = omx.quantize(v, omx.fmt_of(fmt), axis=0)
+    ec, es = ec.T, es.T                   # K-major
+    if fmt == "mxfp4":
+        ec = omx.pack_fp4(ec)
+    assert np.array_equal(host(codes), ec)
+    assert np.array_equal(host(scales), es)
+
+
+def _segments_expected(vals, src, offsets, E, fmt, pad=128):
+    """Oracle side of the segment-transposed quantization: per expert the
+    segment's rows (zero where src < 0) padded with zero rows to a multiple
+    of `pad`, MX-quantized along the rows; returns K-major codes, scales and
+    the segment starts."""
+    C = vals.shape[1]
+    cols, scs, kofs = [], [], [0]
+    for e in range(E):
+        seg = vals[offsets[e]:offsets[e + 1]].copy()
+        seg[src[offsets[e]:offsets[e + 1]] < 0] = 0
+        n = (len(seg) + pad - 1) // pad * pad
+        seg = np.concatenate([seg, np.zeros((n - len(seg), C), np.float32)])
+        kofs.append(kofs[-1] + n)
+        if n:
+            c, s = omx.quantize(seg, omx.fmt_of(fmt), axis=0)
+            cols.append(c.T)
+            scs.append(s.T)
+    return np.concatenate(cols, axis=1), np.concatenate(scs, axis=1), np.array(kofs)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_quantize_segments(gpu_lib, mode):
+    T, E, k, C = 173, 12, 3, 320
+    log(f"segment quantize mode {mode} T={T} E={E} C={C}")
+    idx, counts, offsets, row_map, src = _maps(T, E, k, 32, 7)
+    bound = len(src)
+    g = np.random.default_rng(8 + mode)
+    if mode == 0:
+        inp = _bf16(g.standard_normal((bound, C)))
+        vals = inp
+    elif mode == 1:
+        inp = _bf16(g.standard_normal((T, C)))
+        vals = pm.permute_rows(inp, src)
+    else:
+        inp = _bf16(g.standard_normal((bound, 2 * C)) * 2)
+        from oracle import mlp as omlp
+        vals = omlp.swiglu(inp, C)
+    ks = moe.moe_segments_kstride(bound, E)
+    codes = torch.zeros((C, ks), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((C, ks // 32), dtype=torch.uint8, device="cuda")
+    kofs = torch.empty((E + 1,), **I32)
+    moe.moe_quantize_mx_segments(dev(inp, "bf16"), mode, torch.from_numpy(src.astype(np.int32)).cuda(),
+                                 torch.from_numpy(offsets.astype(np.int32)).cuda(), E, bound, C, ks,
+                                 moe.MOE_MXFP8_E4M3, codes, scales, kofs)
+    torch.cuda.synchronize()
+    ec, es, ekofs = _segments_expected(vals, src, offsets, E, "mxfp8")
+    assert np.array_equal(host(kofs), ekofs)
+    n = ekofs[-1]
+    gc, gs = host(codes)[:, :n], host(scales)[:, : n // 32]
+    if mode < 2:
+        assert np.array_equal(gc, ec) and np.array_equal(gs, es)
+    else:
+        # silu in fp32 on the device vs the oracle's: codes may differ at a
+        # rounding boundary, never by more than one grid step
+        assert (gs == es).mean() > 0.999
+        a = omx.dequantize(gc, gs, "e4m3", axis=1)
+        b = omx.dequantize(ec, es, "e4m3", axis=1)
+        assert rel_l2(a, b) < 1e-3
+
+
+@pytest.mark.parametrize("M,N", [(256, 384), (384, 256)])
+def test_wgrad_ragged_segments(gpu_lib, M, N):
+    T, E, k = 400, 16, 4
+    log(f"grouped wgrad M={M} N={N} T={T} E={E}")
+    idx, counts, offsets, row_map, src = _maps(T, E, k, 32, 9)
+    assert counts[0] > 256 and (counts[-3:] == 0).all()
+    bound = len(src)
+    g = np.random.default_rng(10)
+    A = _bf16(g.standard_normal((bound, M)))
+    B = _bf16(g.standard_normal((bound, N)))
+    ks = moe.moe_segments_kstride(bound, E)
+    src_d = torch.from_numpy(src.astype(np.int32)).cuda()
+    off_d = torch.from_numpy(offsets.astype(np.int32)).cuda()
+    kofs = torch.empty((E + 1,), **I32)
+    bufs = []
+    for vals, C in ((A, M), (B, N)):
+        c = torch.empty((C, ks), dtype=torch.uint8, device="cuda")
+        s = torch.empty((C, ks // 32), dtype=torch.uint8, device="cuda")
+        moe.moe_quantize_mx_segments(dev(vals, "bf16"), 0, src_d, off_d, E, bound, C, ks,
+                                     moe.MOE_MXFP8_E4M3, c, s, kofs)
+        bufs += [c, s]
+    dw = torch.full((E, M, N), 5.0, dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_wgrad(bufs[0], bufs[1], bufs[2], bufs[3], moe.MOE_MXFP8_E4M3, kofs, E, M, N, ks, dw)
+    torch.cuda.synchronize()
+    got = host(dw)
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        live = src[lo:hi] >= 0
+        a = np.where(live[:, None], A[lo:hi], 0)
+        b = np.where(live[:, None], B[lo:hi], 0)
+        if hi == lo:
+            assert (got[e] == 0).all(), f"expert {e} has no rows: gradient must be exactly zero"
+            continue
+        ref = (omx.fake_quant(obw._pad_rows(a, 32), "e4m3", axis=0).T
+               @ omx.fake_quant(obw._pad_rows(b, 32), "e4m3", axis=0))
+        assert rel_l2(got[e], ref) < TOL, e
+
+
+def _gpu_backward(cfg, x_d, wr_d, b_d, w1, w2, dout_d):
+    ew = moe.ExpertWeights.from_dense(w1, w2, cfg.fmt, transposed=True)
+    fw = moe.MoEForward.for_config(cfg, save_act=True)
+    fw(x_d, wr_d, b_d, ew)
+    bw = moe.MoEBackward(fw)
+    bw(dout_d, x_d, ew)
+    torch.cuda.synchronize()
+    return fw, bw
+
+
+def test_backward_reduced_skewed(gpu_lib):
+    cfg = configs.get("mini_skew_mxfp8")
+    log(f"backward end to end {cfg.name}")
+    h, d = device_inputs(cfg)
+    fw, bw = _gpu_backward(cfg, d["x"], d["w_router"], d["bias"], d["w1"], d["w2"], d["dout"])
+    olog = rt.router_logits(h["x"], h["w_router"])
+    oidx, ow, _, _ = rt.route(olog, h["bias"], cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
+    assert np.array_equal(host(fw.topk_idx), oidx)
+    ref = obw.moe_backward(h["x"], h["dout"], oidx, ow, lambda e: h["w1"][e], lambda e: h["w2"][e],
+                           E=cfg.E, fmt=cfg.fmt)
+    dx = host(bw.dx)
+    err = rel_l2(dx, ref["dx"])
+    log(f"  dx rel L2 {err:.2e}")
+    assert err < TOL
+    counts = np.bincount(oidx.ravel(), minlength=cfg.E)
+    assert (counts == 0).sum() >= 1, "the skewed routing leaves some experts without rows"
+    dw1, dw2 = host(bw.dw1), host(bw.dw2)
+    for e in range(cfg.E):
+        if counts[e] == 0:
+            assert (dw1[e] == 0).all() and (dw2[e] == 0).all()
+    e1 = rel_l2(dw1, np.stack([ref["dw1"][e] for e in range(cfg.E)]))
+    e2 = rel_l2(dw2, np.stack([ref["dw2"][e] for e in range(cfg.E)]))
+    log(f"  dW1 rel L2 {e1:.2e}, dW2 rel L2 {e2:.2e}")
+    assert e1 < TOL and e2 < TOL
+    # per-expert bar for every expert with rows
+    for e in np.nonzero(counts)[0]:
+        assert rel_l2(dw1[e], ref["dw1"][e]) < TOL and rel_l2(dw2[e], ref["dw2"][e]) < TOL, e
+
+
+@pytest.mark.timeout(900)
+def test_backward_full_size_sampled(gpu_lib):
+    cfg = configs.get("dsv4_skew_mxfp8_t8192")
+    log(f"full-size backward {cfg.name}: generating weights on the device")
+    x, wr, b = gen.host_x(cfg), gen.host_router(cfg), gen.host_bias(cfg)
+    dout = gen.host_dout(cfg)
+    wts = gen.device_expert_weights(cfg, "cuda")
+    x_d = dev(x, "bf16")
+    fw, bw = _gpu_backward(cfg, x_d, dev(wr, "bf16"), dev(b), wts["w1"], wts["w2"], dev(dout, "bf16"))
+    log("  forward + backward done; oracle routing of all tokens")
+    olog = rt.router_logits(x, wr)
+    oidx, ow, _, osel = rt.route(olog, b, cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
+    idx = host(fw.topk_idx)
+    nbad, unc = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group)
+    assert unc == 0 and nbad <= max(2, cfg.T // 1000)
+    bad_tok = np.nonzero((idx != oidx).any(axis=1))[0]
+    counts = np.bincount(oidx.ravel(), minlength=cfg.E)
+    touched = set(int(e) for t in bad_tok for e in np.concatenate([idx[t], oidx[t]]))
+    dw1_d, dw2_d = bw.dw1, bw.dw2
+    zero = [e for e in range(cfg.E) if counts[e] == 0 and e not in touched]
+    assert len(zero) >= 1
+    for e in zero:
+        assert not dw1_d[e].any().item() and not dw2_d[e].any().item(), e
+    # a light expert (one or two 32-row blocks): oracle backward of all its rows
+    cand = [e for e in range(cfg.E) if 20 <= counts[e] <= 60 and e not in touched]
+    e = cand[0]
+    tj = np.argwhere(oidx == e)
+    t, j = tj[:, 0], tj[:, 1]
+    log(f"  oracle backward of expert {e} ({len(t)} rows)")
+    w1 = wts["w1"][e].float().cpu().numpy()
+    w2 = wts["w2"][e].float().cpu().numpy()
+    dy = (ow[t, j][:, None].astype(np.float32) * dout[t]).astype(np.float32)
+    dx_e, dw1_e, dw2_e = obw.expert_backward(x[t], dy, w1, w2, cfg.fmt)
+    rows = host(fw.row_map)[t, j]
+    e_dx = rel_l2(host(bw.dx_perm[torch.from_numpy(rows).cuda()]), dx_e)
+    e_w1 = rel_l2(host(dw1_d[e]), dw1_e)
+    e_w2 = rel_l2(host(dw2_d[e]), dw2_e)
+    log(f"  expert {e}: dX rows {e_dx:.2e}, dW1 {e_w1:.2e}, dW2 {e_w2:.2e}")
+    assert e_dx < TOL and e_w1 < TOL and e_w2 < TOL
+    # un-permute property on sampled tokens: dx[t] = bf16(sum_j dX_rows[row_map[t, j]])
+    g = np.random.default_rng(3)
+    toks = g.choice(cfg.T, 64, replace=False)
+    rm = host(fw.row_map)[toks]
+    rows_h = host(bw.dx_perm[torch.from_numpy(rm.ravel()).cuda()]).reshape(len(toks), cfg.k, cfg.H)
+    acc = np.zeros((len(toks), cfg.H), np.float32)
+    for jj in range(cfg.k):
+        acc = (acc + rows_h[:, jj]).astype(np.float32)
+    assert np.array_equal(host(bw.dx[torch.from_numpy(toks).cuda()]), _bf16(acc))
+    assert np.isfinite(host(bw.dx)).all()
