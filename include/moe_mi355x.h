@@ -208,7 +208,8 @@ size_t moe_grouped_mlp_workspace(int E, int H, int F, int64_t rows, int a_fmt,
  *          (MXFP8, MXFP8, BF16), (MXFP4, MXFP4, BF16).
  * offsets  [E+1] int32 device array (as moe_permute writes it);
  *          offsets[E] <= rows.
- * act_save optional [rows, 2F] bf16: receives A (for the backward).
+ * act_save optional [rows, 2F] fp32: receives A = (gate | up) unrounded,
+ *          for the backward (rows of a padding slot hold unspecified values).
  * y        [rows, H] in y_fmt; rows outside every segment are not written.
  * ws       moe_grouped_mlp_workspace(E, H, F, rows, a_fmt, w_fmt) bytes.
  * Limits: 1 <= E <= 1024; BF16: H % 128 == 0, F % 64 == 0; MXFP8:
@@ -220,7 +221,7 @@ int moe_grouped_mlp_fwd(const void* a, const uint8_t* a_scales, int a_fmt,
                         const uint8_t* w1_scales, const void* w2,
                         const uint8_t* w2_scales, int w_fmt,
                         const int32_t* offsets, int E, int H, int F,
-                        int64_t rows, void* act_save, void* y, int y_fmt,
+                        int64_t rows, float* act_save, void* y, int y_fmt,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
@@ -236,7 +237,7 @@ int moe_grouped_fc1_swiglu(const void* a, const uint8_t* a_scales, int a_fmt,
                            const int32_t* src_row, const void* w1,
                            const uint8_t* w1_scales, int w_fmt,
                            const int32_t* offsets, int E, int H, int F,
-                           int64_t rows, void* act_save, void* h,
+                           int64_t rows, float* act_save, void* h,
                            uint8_t* h_scales, hipStream_t stream);
 
 /*
@@ -274,13 +275,21 @@ int moe_combine(const void* y, int y_fmt, const int32_t* row_map,
  */
 
 /*
- * moe_combine_bwd — dy[r] = topk_w[t, j] * dout[t] for the expert-major row
- * r = row_map[t, j]; every row with src_row[r] == -1 is zero.
- * dout [T, H] in dout_fmt (MOE_BF16 or MOE_F32); dy [rows, H] bf16 out.
+ * moe_combine_bwd — dY rows of the expert-major layout:
+ *   dy[r] = topk_w[t, j] * dout[t]   for r = row_map[t, j]
+ * formed in fp32; every row with src_row[r] == -1 is zero.
+ * dout    [T, H] in dout_fmt (MOE_BF16 or MOE_F32).
+ * dy      [rows, H] out in dy_fmt: MOE_F32, MOE_BF16, or an MX format (codes
+ *         [rows, H] / [rows, H/2] encoded from the fp32 products, with
+ *         dy_scales [rows, H/32]; needs H % 32 == 0).
+ * row_w   optional [rows] fp32 out: the routing weight of each row (0 for a
+ *         padding row), the row scale moe_quantize_mx_segments takes to form
+ *         the same dY rows from dout.
  */
 int moe_combine_bwd(const void* dout, int dout_fmt, const int32_t* row_map,
                     const int32_t* src_row, const float* topk_w, int T, int k,
-                    int H, int64_t rows, void* dy, hipStream_t stream);
+                    int H, int64_t rows, void* dy, int dy_fmt,
+                    uint8_t* dy_scales, float* row_w, hipStream_t stream);
 
 /*
  * moe_unpermute — dx[t] = sum_j dx_perm[row_map[t, j]], fp32 accumulation
@@ -302,16 +311,21 @@ int64_t moe_segments_kstride(int64_t rows, int E);
  * with align 32 writes them); column c of segment e becomes K-major codes
  * codes[c, kofs[e] .. kofs[e] + len_e) in blocks of 32 rows, the segment
  * padded with zeros to a multiple of 128, kofs[e] the sum of the padded
- * lengths before e (written to kofs [E+1]).
- * mode 0: in [rows, C] bf16, row r used as is (zero where src_row[r] < 0)
- * mode 1: in [T, C] bf16 token rows gathered through src_row (zero for -1)
- * mode 2: in [rows, 2C] bf16 = the saved fc1 output (gate | up); the value
+ * lengths before e (written to kofs [E+1]). Values are formed in fp32:
+ * mode 0: in [rows, C], row r used as is (zero where src_row[r] < 0)
+ * mode 1: in [T, C] token rows gathered through src_row (zero for -1)
+ * mode 2: in [rows, 2C] = the saved fc1 output (gate | up); the value
  *         is silu(gate) * up (h recomputed), zero where src_row[r] < 0
+ * in_fmt  MOE_BF16 or MOE_F32.
+ * row_scale optional [rows] fp32: row r's values are multiplied by
+ *         row_scale[r] (mode 1 with moe_combine_bwd's row_w gives dY).
  * codes [C, kstride] (E4M3) or [C, kstride/2] (E2M1), scales [C, kstride/32];
- * kstride >= moe_segments_kstride(rows, E), a multiple of 128.
+ * kstride >= moe_segments_kstride(rows, E), a multiple of 128. Columns past
+ * kofs[E] are not written.
  */
-int moe_quantize_mx_segments(const void* in, int mode, const int32_t* src_row,
-                             const int32_t* offsets, int E, int64_t rows,
+int moe_quantize_mx_segments(const void* in, int in_fmt, int mode,
+                             const int32_t* src_row, const int32_t* offsets,
+                             const float* row_scale, int E, int64_t rows,
                              int C, int64_t kstride, int out_fmt,
                              uint8_t* codes, uint8_t* scales, int32_t* kofs,
                              hipStream_t stream);
@@ -322,17 +336,18 @@ int moe_quantize_mx_segments(const void* in, int mode, const int32_t* src_row,
  * SwiGLU backward with the saved fc1 output A = (g | u):
  *   dgate = dH * u * sig(g) * (1 + g * (1 - sig(g))),  dup = dH * silu(g)
  * dy      [rows, H] in fmt (MX: codes + dy_scales [rows, H/32]).
- * act_save [rows, 2F] bf16 (moe_grouped_fc1_swiglu's act_save).
+ * act_save [rows, 2F] fp32 (moe_grouped_fc1_swiglu's act_save).
  * da      [rows, 2F] out: MX codes (+ da_scales [rows, 2F/32], blocks along
- *         2F) or bf16 when fmt is MOE_BF16; da_bf16 optional bf16 copy.
+ *         2F) or bf16 when fmt is MOE_BF16; da_f32 optional fp32 copy of the
+ *         unrounded dA (the weight gradient's operand).
  * Limits: H % 128 == 0 (256 for MXFP4), F % 128 == 0.
  */
 int moe_grouped_fc2_dgrad_dswiglu(const void* dy, const uint8_t* dy_scales,
                                   int fmt, const void* w2t,
                                   const uint8_t* w2t_scales,
                                   const int32_t* offsets, int E, int H, int F,
-                                  int64_t rows, const void* act_save, void* da,
-                                  uint8_t* da_scales, void* da_bf16,
+                                  int64_t rows, const float* act_save, void* da,
+                                  uint8_t* da_scales, float* da_f32,
                                   hipStream_t stream);
 
 /*

@@ -34,10 +34,10 @@ SIGNATURES = {
     "moe_grouped_fc1_swiglu": (_I, [_P, _P, _I, _P, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _P, _P, _P]),
     "moe_grouped_fc2": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _I, _P]),
     "moe_combine": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _P, _I, _P]),
-    "moe_combine_bwd": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _I64, _P, _P]),
+    "moe_combine_bwd": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _I64, _P, _I, _P, _P, _P]),
     "moe_unpermute": (_I, [_P, _I, _P, _I, _I, _I, _P, _I, _P]),
     "moe_segments_kstride": (_I64, [_I64, _I]),
-    "moe_quantize_mx_segments": (_I, [_P, _I, _P, _P, _I, _I64, _I, _I64, _I, _P, _P, _P, _P]),
+    "moe_quantize_mx_segments": (_I, [_P, _I, _I, _P, _P, _P, _I, _I64, _I, _I64, _I, _P, _P, _P, _P]),
     "moe_grouped_fc2_dgrad_dswiglu": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I64, _P, _P, _P, _P, _P]),
     "moe_grouped_fc1_dgrad": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I64, _P, _P]),
     "moe_grouped_wgrad": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _P]),
@@ -159,10 +159,11 @@ def moe_combine(y, y_fmt, row_map, topk_w, shared, T, k, H, out, out_fmt, stream
         _stream(stream)))
 
 
-def moe_combine_bwd(dout, dout_fmt, row_map, src_row, topk_w, T, k, H, rows, dy, stream=None):
+def moe_combine_bwd(dout, dout_fmt, row_map, src_row, topk_w, T, k, H, rows, dy, dy_fmt, dy_scales,
+                    row_w, stream=None):
     _check("moe_combine_bwd", load().moe_combine_bwd(
         _ptr(dout), dout_fmt, _ptr(row_map), _ptr(src_row), _ptr(topk_w), T, k, H, rows, _ptr(dy),
-        _stream(stream)))
+        dy_fmt, _ptr(dy_scales), _ptr(row_w), _stream(stream)))
 
 
 def moe_unpermute(dx_perm, fmt, row_map, T, k, H, dx, out_fmt, stream=None):
@@ -174,18 +175,18 @@ def moe_segments_kstride(rows, E) -> int:
     return load().moe_segments_kstride(rows, E)
 
 
-def moe_quantize_mx_segments(inp, mode, src_row, offsets, E, rows, C, kstride, out_fmt, codes,
-                             scales, kofs, stream=None):
+def moe_quantize_mx_segments(inp, in_fmt, mode, src_row, offsets, row_scale, E, rows, C, kstride,
+                             out_fmt, codes, scales, kofs, stream=None):
     _check("moe_quantize_mx_segments", load().moe_quantize_mx_segments(
-        _ptr(inp), mode, _ptr(src_row), _ptr(offsets), E, rows, C, kstride, out_fmt, _ptr(codes),
-        _ptr(scales), _ptr(kofs), _stream(stream)))
+        _ptr(inp), in_fmt, mode, _ptr(src_row), _ptr(offsets), _ptr(row_scale), E, rows, C, kstride,
+        out_fmt, _ptr(codes), _ptr(scales), _ptr(kofs), _stream(stream)))
 
 
 def moe_grouped_fc2_dgrad_dswiglu(dy, dy_scales, fmt, w2t, w2t_scales, offsets, E, H, F, rows,
-                                  act_save, da, da_scales, da_bf16, stream=None):
+                                  act_save, da, da_scales, da_f32, stream=None):
     _check("moe_grouped_fc2_dgrad_dswiglu", load().moe_grouped_fc2_dgrad_dswiglu(
         _ptr(dy), _ptr(dy_scales), fmt, _ptr(w2t), _ptr(w2t_scales), _ptr(offsets), E, H, F, rows,
-        _ptr(act_save), _ptr(da), _ptr(da_scales), _ptr(da_bf16), _stream(stream)))
+        _ptr(act_save), _ptr(da), _ptr(da_scales), _ptr(da_f32), _stream(stream)))
 
 
 def moe_grouped_fc1_dgrad(da, da_scales, fmt, w1t, w1t_scales, offsets, E, H, F, rows, dx_perm,

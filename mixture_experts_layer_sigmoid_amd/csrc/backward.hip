@@ -16,52 +16,97 @@
 #include "mx_codec.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace moe {
 namespace {
 
 constexpr int kMaxE = 1024;
 
-// dy[r] = w[t, j] * dout[t] for the row r = row_map[t, j]; padding rows
-// (src_row -1) are zero. One workgroup per row.
 template <int DF>
+__device__ __forceinline__ void load_row8(const void* base, int64_t off, float* v) {
+  if (DF == MOE_BF16) {
+    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(base) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(q[i] << 16);
+      v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+    }
+  } else {
+    load8_f32(static_cast<const float*>(base) + off, v);
+  }
+}
+
+// Routing weight of expert-major row r (0 for a padding row): the slot j of
+// token src_row[r] whose row_map entry is r.
+__device__ __forceinline__ float row_weight(const int32_t* row_map, const float* w, int t, int k,
+                                            int64_t r) {
+  float wj = 0.f;
+  if (t >= 0)
+    for (int j = 0; j < k; ++j)
+      if (row_map[static_cast<int64_t>(t) * k + j] == r) wj = w[static_cast<int64_t>(t) * k + j];
+  return wj;
+}
+
+// dy[r] = w[t, j] * dout[t] for the row r = row_map[t, j], formed in fp32;
+// padding rows (src_row -1) are zero. One workgroup per row. Plain output
+// (OF = MOE_F32 / MOE_BF16): 8 columns per thread. MX output: one 32-column
+// block per thread, encoded from the fp32 products (no intermediate
+// rounding), codes and one scale byte per block.
+template <int DF, int OF>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const void* __restrict__ dout,
                                                           const int32_t* __restrict__ row_map,
                                                           const int32_t* __restrict__ src_row,
                                                           const float* __restrict__ w, int k, int H,
-                                                          int64_t rows, uint16_t* __restrict__ dy) {
+                                                          int64_t rows, void* __restrict__ dy,
+                                                          uint8_t* __restrict__ dy_scales,
+                                                          float* __restrict__ row_w) {
+  constexpr bool kMx = OF == MOE_MXFP8_E4M3 || OF == MOE_MXFP4_E2M1;
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
     const int t = src_row[r];
-    float wj = 0.f;
-    if (t >= 0) {
-      for (int j = 0; j < k; ++j)
-        if (row_map[static_cast<int64_t>(t) * k + j] == r) wj = w[static_cast<int64_t>(t) * k + j];
-    }
-    uint16_t* o = dy + r * H;
-    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
-      float v[8];
-      if (t >= 0) {
-        if (DF == MOE_BF16) {
-          const u32x4_t q = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(dout) +
-                                                              static_cast<int64_t>(t) * H + c);
+    const float wj = row_weight(row_map, w, t, k, r);
+    if (row_w && threadIdx.x == 0) row_w[r] = wj;
+    if constexpr (kMx) {
+      constexpr bool fp4 = OF == MOE_MXFP4_E2M1;
+      for (int b = threadIdx.x; b < H / 32; b += 256) {
+        float v[32];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(q[i] << 16);
-            v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+        for (int q = 0; q < 4; ++q) {
+          if (t >= 0) {
+            load_row8<DF>(dout, static_cast<int64_t>(t) * H + b * 32 + q * 8, v + q * 8);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[q * 8 + i] *= wj;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[q * 8 + i] = 0.f;
           }
-        } else {
-          const float* s = static_cast<const float*>(dout) + static_cast<int64_t>(t) * H + c;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = s[i];
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] *= wj;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+        uint32_t words[8];
+        const uint32_t sb = mx_encode_block<fp4>(v, words);
+        uint8_t* o = static_cast<uint8_t*>(dy) + r * (fp4 ? H / 2 : H) + b * (fp4 ? 16 : 32);
+        reinterpret_cast<u32x4_t*>(o)[0] = u32x4_t{words[0], words[1], words[2], words[3]};
+        if (!fp4) reinterpret_cast<u32x4_t*>(o)[1] = u32x4_t{words[4], words[5], words[6], words[7]};
+        dy_scales[r * (H / 32) + b] = static_cast<uint8_t>(sb);
       }
-      *reinterpret_cast<u32x4_t*>(o + c) = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    } else {
+      for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+        float v[8];
+        if (t >= 0) {
+          load_row8<DF>(dout, static_cast<int64_t>(t) * H + c, v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] *= wj;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = 0.f;
+        }
+        if (OF == MOE_BF16) {
+          *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(dy) + r * H + c) =
+              u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7])};
+        } else {
+          store8_f32(static_cast<float*>(dy) + r * H + c, v);
+        }
+      }
     }
   }
 }
@@ -70,21 +115,30 @@ enum { SEG_ROWS = 0, SEG_GATHER = 1, SEG_SWIGLU = 2 };
 
 // Segment-transposed MX quantization. Input rows r (expert-major, segments
 // [offsets[e], offsets[e+1]) with lengths multiple of 32) of C columns:
-//   SEG_ROWS:   in[r, c] (bf16), zero where src_row[r] < 0
-//   SEG_GATHER: in[src_row[r], c] (bf16 token rows), zero where src_row < 0
-//   SEG_SWIGLU: silu(in[r, c]) * in[r, C + c] (in is [rows, 2C] bf16),
+//   SEG_ROWS:   in[r, c], zero where src_row[r] < 0
+//   SEG_GATHER: in[src_row[r], c] (token rows), zero where src_row < 0
+//   SEG_SWIGLU: silu(in[r, c]) * in[r, C + c] (in is [rows, 2C]),
 //               zero where src_row[r] < 0
+// in is bf16 (IN = MOE_BF16) or fp32; with row_scale the value of row r is
+// multiplied by row_scale[r] in fp32 before encoding.
 // Output K-major: codes[c, kofs[e] + i] for the segment's rows i, each
 // segment padded with zeros to a multiple of `pad` columns; scales
 // [c, kstride/32], one per 32 columns. kofs[e] = sum over e' < e of the
 // padded lengths (written to kofs_out when given, kofs_out[E] = total).
 // offsets == nullptr means one segment [0, rows); src_row == nullptr means
 // every row is live (SEG_ROWS / SEG_SWIGLU only).
-template <int MODE, bool FP4>
+template <int IN>
+__device__ __forceinline__ float ld_in(const void* in, int64_t i) {
+  if (IN == MOE_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(in)[i]);
+  return static_cast<const float*>(in)[i];
+}
+
+template <int MODE, bool FP4, int IN>
 __global__ __launch_bounds__(256) void quantize_segments_kernel(
-    const uint16_t* __restrict__ in, const int32_t* __restrict__ src_row,
-    const int32_t* __restrict__ offsets, int E, int64_t rows, int C, int64_t kstride, int pad,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int32_t* __restrict__ kofs_out) {
+    const void* __restrict__ in, const int32_t* __restrict__ src_row,
+    const int32_t* __restrict__ offsets, const float* __restrict__ row_scale, int E, int64_t rows,
+    int C, int64_t kstride, int pad, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    int32_t* __restrict__ kofs_out) {
   __shared__ int32_t s_kofs[kMaxE + 1];
   __shared__ int32_t part[256];
   const int tid = threadIdx.x;
@@ -141,14 +195,15 @@ __global__ __launch_bounds__(256) void quantize_segments_kernel(
         const int src = src_row ? src_row[r] : static_cast<int>(r);
         if (src >= 0) {
           if (MODE == SEG_ROWS) {
-            x = bf16_bits_to_f32(in[r * C + c]);
+            x = ld_in<IN>(in, r * C + c);
           } else if (MODE == SEG_GATHER) {
-            x = bf16_bits_to_f32(in[static_cast<int64_t>(src) * C + c]);
+            x = ld_in<IN>(in, static_cast<int64_t>(src) * C + c);
           } else {
-            const float g = bf16_bits_to_f32(in[r * 2 * C + c]);
-            const float u = bf16_bits_to_f32(in[r * 2 * C + C + c]);
+            const float g = ld_in<IN>(in, r * 2 * C + c);
+            const float u = ld_in<IN>(in, r * 2 * C + C + c);
             x = g * (1.f / (1.f + expf(-g))) * u;
           }
+          if (row_scale) x *= row_scale[r];
         }
       }
       v[i] = x;
@@ -174,24 +229,38 @@ using namespace moe;
 
 extern "C" int moe_combine_bwd(const void* dout, int dout_fmt, const int32_t* row_map,
                                const int32_t* src_row, const float* topk_w, int T, int k, int H,
-                               int64_t rows, void* dy, hipStream_t stream) {
+                               int64_t rows, void* dy, int dy_fmt, uint8_t* dy_scales,
+                               float* row_w, hipStream_t stream) {
   clear_error();
   MOE_REQUIRE(T >= 0 && k >= 1 && H > 0 && H % 8 == 0 && rows >= 0, MOE_ERR_INVALID_ARG,
               "moe_combine_bwd: need T >= 0, k >= 1, H a positive multiple of 8, rows >= 0");
   MOE_REQUIRE(dout_fmt == MOE_BF16 || dout_fmt == MOE_F32, MOE_ERR_UNSUPPORTED,
               "moe_combine_bwd: dout_fmt must be MOE_BF16 or MOE_F32");
+  const bool mx = dy_fmt == MOE_MXFP8_E4M3 || dy_fmt == MOE_MXFP4_E2M1;
+  MOE_REQUIRE(mx || dy_fmt == MOE_BF16 || dy_fmt == MOE_F32, MOE_ERR_UNSUPPORTED,
+              "moe_combine_bwd: dy_fmt must be MOE_F32, MOE_BF16 or an MX format");
+  MOE_REQUIRE(!mx || H % 32 == 0, MOE_ERR_INVALID_ARG, "moe_combine_bwd: MX dy needs H % 32 == 0");
   if (rows == 0) return MOE_OK;
-  MOE_REQUIRE(dy && src_row && (T == 0 || (dout && row_map && topk_w)), MOE_ERR_INVALID_ARG,
-              "moe_combine_bwd: null pointer");
+  MOE_REQUIRE(dy && src_row && (!mx || dy_scales) && (T == 0 || (dout && row_map && topk_w)),
+              MOE_ERR_INVALID_ARG, "moe_combine_bwd: null pointer");
   MOE_REQUIRE(aligned16(dy) && (!dout || aligned16(dout)), MOE_ERR_ALIGNMENT,
               "moe_combine_bwd: dout and dy must be 16-byte aligned");
   const unsigned grid = static_cast<unsigned>(std::min<int64_t>(rows, 16384));
-  if (dout_fmt == MOE_BF16)
-    hipLaunchKernelGGL(combine_bwd_kernel<MOE_BF16>, dim3(grid), dim3(256), 0, stream, dout, row_map,
-                       src_row, topk_w, k, H, rows, static_cast<uint16_t*>(dy));
-  else
-    hipLaunchKernelGGL(combine_bwd_kernel<MOE_F32>, dim3(grid), dim3(256), 0, stream, dout, row_map,
-                       src_row, topk_w, k, H, rows, static_cast<uint16_t*>(dy));
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, dout, row_map, src_row, topk_w, k, H,
+                       rows, dy, dy_scales, row_w);
+  };
+  auto by_out = [&](auto df) {
+    constexpr int DF = decltype(df)::value;
+    switch (dy_fmt) {
+      case MOE_F32: go(combine_bwd_kernel<DF, MOE_F32>); break;
+      case MOE_BF16: go(combine_bwd_kernel<DF, MOE_BF16>); break;
+      case MOE_MXFP8_E4M3: go(combine_bwd_kernel<DF, MOE_MXFP8_E4M3>); break;
+      default: go(combine_bwd_kernel<DF, MOE_MXFP4_E2M1>); break;
+    }
+  };
+  if (dout_fmt == MOE_BF16) by_out(std::integral_constant<int, MOE_BF16>{});
+  else by_out(std::integral_constant<int, MOE_F32>{});
   return check_launch("moe_combine_bwd");
 }
 
@@ -200,8 +269,9 @@ extern "C" int64_t moe_segments_kstride(int64_t rows, int E) {
   return (rows + static_cast<int64_t>(E) * 127 + 127) / 128 * 128;
 }
 
-extern "C" int moe_quantize_mx_segments(const void* in, int mode, const int32_t* src_row,
-                                        const int32_t* offsets, int E, int64_t rows, int C,
+extern "C" int moe_quantize_mx_segments(const void* in, int in_fmt, int mode,
+                                        const int32_t* src_row, const int32_t* offsets,
+                                        const float* row_scale, int E, int64_t rows, int C,
                                         int64_t kstride, int out_fmt, uint8_t* codes,
                                         uint8_t* scales, int32_t* kofs, hipStream_t stream) {
   clear_error();
@@ -209,6 +279,8 @@ extern "C" int moe_quantize_mx_segments(const void* in, int mode, const int32_t*
               "moe_quantize_mx_segments: need 1 <= E <= 1024, C > 0, rows >= 0");
   MOE_REQUIRE(mode >= SEG_ROWS && mode <= SEG_SWIGLU, MOE_ERR_INVALID_ARG,
               "moe_quantize_mx_segments: mode must be 0 (rows), 1 (gather) or 2 (swiglu)");
+  MOE_REQUIRE(in_fmt == MOE_BF16 || in_fmt == MOE_F32, MOE_ERR_UNSUPPORTED,
+              "moe_quantize_mx_segments: in_fmt must be MOE_BF16 or MOE_F32");
   MOE_REQUIRE(out_fmt == MOE_MXFP8_E4M3 || out_fmt == MOE_MXFP4_E2M1, MOE_ERR_UNSUPPORTED,
               "moe_quantize_mx_segments: out_fmt must be an MX format");
   MOE_REQUIRE(kstride >= moe_segments_kstride(rows, E) && kstride % 128 == 0, MOE_ERR_INVALID_ARG,
@@ -219,14 +291,23 @@ extern "C" int moe_quantize_mx_segments(const void* in, int mode, const int32_t*
   MOE_REQUIRE(aligned16(codes), MOE_ERR_ALIGNMENT, "moe_quantize_mx_segments: codes not 16-byte aligned");
   const int64_t work = (kstride / 32) * ((C + 255) / 256);
   const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>(work, 16384)));
-  const bool fp4 = out_fmt == MOE_MXFP4_E2M1;
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, static_cast<const uint16_t*>(in),
-                       src_row, offsets, E, rows, C, kstride, 128, codes, scales, kofs);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, in, src_row, offsets, row_scale, E,
+                       rows, C, kstride, 128, codes, scales, kofs);
   };
-  if (mode == SEG_ROWS) fp4 ? go(quantize_segments_kernel<SEG_ROWS, true>) : go(quantize_segments_kernel<SEG_ROWS, false>);
-  else if (mode == SEG_GATHER) fp4 ? go(quantize_segments_kernel<SEG_GATHER, true>) : go(quantize_segments_kernel<SEG_GATHER, false>);
-  else fp4 ? go(quantize_segments_kernel<SEG_SWIGLU, true>) : go(quantize_segments_kernel<SEG_SWIGLU, false>);
+  auto by_mode = [&](auto fp4_c, auto in_c) {
+    constexpr bool FP4 = decltype(fp4_c)::value;
+    constexpr int IN = decltype(in_c)::value;
+    if (mode == SEG_ROWS) go(quantize_segments_kernel<SEG_ROWS, FP4, IN>);
+    else if (mode == SEG_GATHER) go(quantize_segments_kernel<SEG_GATHER, FP4, IN>);
+    else go(quantize_segments_kernel<SEG_SWIGLU, FP4, IN>);
+  };
+  auto by_in = [&](auto fp4_c) {
+    if (in_fmt == MOE_BF16) by_mode(fp4_c, std::integral_constant<int, MOE_BF16>{});
+    else by_mode(fp4_c, std::integral_constant<int, MOE_F32>{});
+  };
+  if (out_fmt == MOE_MXFP4_E2M1) by_in(std::true_type{});
+  else by_in(std::false_type{});
   return check_launch("moe_quantize_mx_segments");
 }
 
@@ -238,13 +319,13 @@ int quantize_mx_columns(const void* in, int64_t rows, int K, int out_fmt, uint8_
   const int64_t work = (rows / 32) * ((K + 255) / 256);
   const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>(work, 16384)));
   if (out_fmt == MOE_MXFP4_E2M1)
-    hipLaunchKernelGGL((quantize_segments_kernel<SEG_ROWS, true>), dim3(grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(in), nullptr, nullptr, 1, rows, K, rows, 32,
-                       codes, scales, nullptr);
+    hipLaunchKernelGGL((quantize_segments_kernel<SEG_ROWS, true, MOE_BF16>), dim3(grid), dim3(256), 0,
+                       stream, in, nullptr, nullptr, nullptr, 1, rows, K, rows, 32, codes, scales,
+                       nullptr);
   else
-    hipLaunchKernelGGL((quantize_segments_kernel<SEG_ROWS, false>), dim3(grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(in), nullptr, nullptr, 1, rows, K, rows, 32,
-                       codes, scales, nullptr);
+    hipLaunchKernelGGL((quantize_segments_kernel<SEG_ROWS, false, MOE_BF16>), dim3(grid), dim3(256), 0,
+                       stream, in, nullptr, nullptr, nullptr, 1, rows, K, rows, 32, codes, scales,
+                       nullptr);
   return check_launch("moe_quantize_mx");
 }
 }  // namespace moe

@@ -53,6 +53,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
 }
 
+// Eight consecutive fp32 values as two 16-byte accesses (p 16-byte aligned).
+__device__ __forceinline__ void load8_f32(const float* p, float* v) {
+  const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0];
+  const f32x4_t b = reinterpret_cast<const f32x4_t*>(p)[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+  }
+}
+__device__ __forceinline__ void store8_f32(float* p, const float* v) {
+  reinterpret_cast<f32x4_t*>(p)[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+  reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+}
+
 // s_waitcnt that waits until at most n vector-memory operations are
 // outstanding (gfx9 encoding: vmcnt in bits [3:0] and [15:14]; expcnt and
 // lgkmcnt left at their no-wait maxima).

@@ -90,7 +90,7 @@ struct Args {
   int64_t out_row_bytes;
   uint8_t* out_sc;
   int64_t out_sc_row_bytes;
-  uint16_t* act_save;      // optional [rows, 2F] bf16 (fc1 only)
+  float* act_save;         // optional [rows, 2F] fp32 (fc1 only)
   int act_cols;            // 2F
   // MODE_K
   const int32_t* kofs;     // [E+1] K offsets (elements) of the groups
@@ -98,8 +98,8 @@ struct Args {
   int64_t out_exp_bytes;   // bytes of one group's output matrix
   int bits;                // bits per element of A and B
   // EPI_DSWIGLU
-  const uint16_t* a_saved; // saved fc1 output A [rows, 2F] bf16 (gate | up)
-  uint16_t* da_bf16;       // optional bf16 copy of dA [rows, 2F]
+  const float* a_saved;    // saved fc1 output A [rows, 2F] fp32 (gate | up)
+  float* da_f32;           // optional fp32 copy of dA [rows, 2F]
 };
 
 template <int MMAX, int STAGES, int NCB, int OP, int RB>
@@ -552,13 +552,9 @@ void grouped_gemm_kernel(Args p) {
               u32x4_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
                       pack_bf16x2(h[6], h[7])};
           if (p.act_save) {
-            uint16_t* ar = p.act_save + grow * p.act_cols + nblk * kHc + c0;
-            *reinterpret_cast<u32x4_t*>(ar) =
-                u32x4_t{pack_bf16x2(gp[0], gp[1]), pack_bf16x2(gp[2], gp[3]),
-                        pack_bf16x2(gp[4], gp[5]), pack_bf16x2(gp[6], gp[7])};
-            *reinterpret_cast<u32x4_t*>(ar + p.up_row) =
-                u32x4_t{pack_bf16x2(up[0], up[1]), pack_bf16x2(up[2], up[3]),
-                        pack_bf16x2(up[4], up[5]), pack_bf16x2(up[6], up[7])};
+            float* ar = p.act_save + grow * p.act_cols + nblk * kHc + c0;
+            store8_f32(ar, gp);
+            store8_f32(ar + p.up_row, up);
           }
         }
       } else {
@@ -591,13 +587,9 @@ void grouped_gemm_kernel(Args p) {
             for (int q = 0; q < 32; q += 8) {
               const int c = blk * 32 + q;
               const float* gp = cs + row * kCs + 32 * (c >> 4) + (c & 15);
-              uint16_t* ar = p.act_save + r * p.act_cols + nblk * kHc + c;
-              *reinterpret_cast<u32x4_t*>(ar) =
-                  u32x4_t{pack_bf16x2(gp[0], gp[1]), pack_bf16x2(gp[2], gp[3]),
-                          pack_bf16x2(gp[4], gp[5]), pack_bf16x2(gp[6], gp[7])};
-              *reinterpret_cast<u32x4_t*>(ar + p.up_row) =
-                  u32x4_t{pack_bf16x2(gp[16], gp[17]), pack_bf16x2(gp[18], gp[19]),
-                          pack_bf16x2(gp[20], gp[21]), pack_bf16x2(gp[22], gp[23])};
+              float* ar = p.act_save + r * p.act_cols + nblk * kHc + c;
+              store8_f32(ar, gp);
+              store8_f32(ar + p.up_row, gp + 16);
             }
           }
         }
@@ -623,14 +615,12 @@ void grouped_gemm_kernel(Args p) {
           const int row = i / (kBR / 8), c0 = (i % (kBR / 8)) * 8;
           const int col = nblk * kBR + c0;
           const int64_t grow = row0 + row;
-          const u32x4_t gw = *reinterpret_cast<const u32x4_t*>(p.a_saved + grow * a2 + col);
-          const u32x4_t uw = *reinterpret_cast<const u32x4_t*>(p.a_saved + grow * a2 + F + col);
-          float dg[8], du[8];
+          float gv[8], uv[8], dg[8], du[8];
+          load8_f32(p.a_saved + grow * a2 + col, gv);
+          load8_f32(p.a_saved + grow * a2 + F + col, uv);
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
-            const uint32_t gb = (q & 1) ? (gw[q >> 1] & 0xFFFF0000u) : (gw[q >> 1] << 16);
-            const uint32_t ub = (q & 1) ? (uw[q >> 1] & 0xFFFF0000u) : (uw[q >> 1] << 16);
-            const float g = __uint_as_float(gb), u = __uint_as_float(ub);
+            const float g = gv[q], u = uv[q];
             const float dh = cs[row * kCs + c0 + q];
             const float sig = 1.f / (1.f + expf(-g));
             dg[q] = dh * u * sig * (1.f + g * (1.f - sig));
@@ -654,13 +644,12 @@ void grouped_gemm_kernel(Args p) {
           float dg[32], du[32];
 #pragma unroll
           for (int w8 = 0; w8 < 4; ++w8) {
-            const u32x4_t gw = *reinterpret_cast<const u32x4_t*>(p.a_saved + grow * a2 + col + w8 * 8);
-            const u32x4_t uw = *reinterpret_cast<const u32x4_t*>(p.a_saved + grow * a2 + F + col + w8 * 8);
+            float gv[8], uv[8];
+            load8_f32(p.a_saved + grow * a2 + col + w8 * 8, gv);
+            load8_f32(p.a_saved + grow * a2 + F + col + w8 * 8, uv);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-              const uint32_t gb = (q & 1) ? (gw[q >> 1] & 0xFFFF0000u) : (gw[q >> 1] << 16);
-              const uint32_t ub = (q & 1) ? (uw[q >> 1] & 0xFFFF0000u) : (uw[q >> 1] << 16);
-              const float g = __uint_as_float(gb), u = __uint_as_float(ub);
+              const float g = gv[q], u = uv[q];
               const float dh = cs[row * kCs + blk * 32 + w8 * 8 + q];
               const float sig = 1.f / (1.f + expf(-g));
               dg[w8 * 8 + q] = dh * u * sig * (1.f + g * (1.f - sig));
@@ -679,13 +668,10 @@ void grouped_gemm_kernel(Args p) {
             o[0] = u32x4_t{words[0], words[1], words[2], words[3]};
             if (!fp4) o[1] = u32x4_t{words[4], words[5], words[6], words[7]};
             srow[c / 32] = static_cast<uint8_t>(sb);
-            if (p.da_bf16) {
-              uint16_t* ob = p.da_bf16 + grow * a2 + c;
+            if (p.da_f32) {
+              float* ob = p.da_f32 + grow * a2 + c;
 #pragma unroll
-              for (int w8 = 0; w8 < 4; ++w8)
-                *reinterpret_cast<u32x4_t*>(ob + w8 * 8) =
-                    u32x4_t{pack_bf16x2(v[w8 * 8 + 0], v[w8 * 8 + 1]), pack_bf16x2(v[w8 * 8 + 2], v[w8 * 8 + 3]),
-                            pack_bf16x2(v[w8 * 8 + 4], v[w8 * 8 + 5]), pack_bf16x2(v[w8 * 8 + 6], v[w8 * 8 + 7])};
+              for (int w8 = 0; w8 < 4; ++w8) store8_f32(ob + w8 * 8, v + w8 * 8);
             }
           }
         }
@@ -703,7 +689,7 @@ __global__ __launch_bounds__(256) void fc1_swiglu_f32_kernel(const float* __rest
                                                              const int32_t* __restrict__ offsets,
                                                              int E, int H, int F, int64_t rows,
                                                              float* __restrict__ h,
-                                                             uint16_t* __restrict__ act_save) {
+                                                             float* __restrict__ act_save) {
   const int64_t used = min(static_cast<int64_t>(offsets[E]), rows);
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < used * F; i += 256ll * gridDim.x) {
     const int64_t r = i / F;
@@ -729,8 +715,8 @@ __global__ __launch_bounds__(256) void fc1_swiglu_f32_kernel(const float* __rest
       u = fmaf(x[k], wu[k], u);
     }
     if (act_save) {
-      act_save[r * 2 * F + c] = f32_to_bf16_bits(g);
-      act_save[r * 2 * F + F + c] = f32_to_bf16_bits(u);
+      act_save[r * 2 * F + c] = g;
+      act_save[r * 2 * F + F + c] = u;
     }
     h[r * F + c] = silu_mul(g, u);
   }
@@ -815,7 +801,7 @@ static bool scale_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p
 
 static int fc1_impl(const void* a, const uint8_t* a_scales, int a_fmt, const int32_t* src_row,
                     const void* w1, const uint8_t* w1_scales, const int32_t* offsets, int E, int H,
-                    int F, int64_t rows, void* act_save, void* h, uint8_t* h_scales,
+                    int F, int64_t rows, float* act_save, void* h, uint8_t* h_scales,
                     hipStream_t stream) {
   const int bits = elem_bits(a_fmt);
   if (a_fmt == MOE_F32) {
@@ -823,7 +809,7 @@ static int fc1_impl(const void* a, const uint8_t* a_scales, int a_fmt, const int
     hipLaunchKernelGGL(fc1_swiglu_f32_kernel, dim3(g1), dim3(256), 0, stream,
                        static_cast<const float*>(a), src_row, static_cast<const float*>(w1),
                        offsets, E, H, F, rows, static_cast<float*>(h),
-                       static_cast<uint16_t*>(act_save));
+                       static_cast<float*>(act_save));
     return check_launch("moe_grouped_fc1_swiglu");
   }
   Args f1{};
@@ -847,7 +833,7 @@ static int fc1_impl(const void* a, const uint8_t* a_scales, int a_fmt, const int
   f1.out_row_bytes = static_cast<int64_t>(F) * bits / 8;
   f1.out_sc = h_scales;
   f1.out_sc_row_bytes = F / 32;
-  f1.act_save = static_cast<uint16_t*>(act_save);
+  f1.act_save = static_cast<float*>(act_save);
   f1.act_cols = 2 * F;
   // 128-row tiles of 256 weight rows (two 32-column MFMA blocks per wave, 8
   // waves) for routed experts; 256-row tiles of 128 weight rows for a single
@@ -925,7 +911,7 @@ extern "C" int moe_grouped_fc1_swiglu(const void* a, const uint8_t* a_scales, in
                                       const int32_t* src_row, const void* w1,
                                       const uint8_t* w1_scales, int w_fmt,
                                       const int32_t* offsets, int E, int H, int F, int64_t rows,
-                                      void* act_save, void* h, uint8_t* h_scales,
+                                      float* act_save, void* h, uint8_t* h_scales,
                                       hipStream_t stream) {
   clear_error();
   MOE_REQUIRE(E >= 1 && E <= kMaxGroups && H > 0 && F > 0 && rows >= 0, MOE_ERR_INVALID_ARG,
@@ -975,7 +961,7 @@ extern "C" int moe_grouped_mlp_fwd(const void* a, const uint8_t* a_scales, int a
                                    const int32_t* src_row, const void* w1,
                                    const uint8_t* w1_scales, const void* w2,
                                    const uint8_t* w2_scales, int w_fmt, const int32_t* offsets,
-                                   int E, int H, int F, int64_t rows, void* act_save, void* y,
+                                   int E, int H, int F, int64_t rows, float* act_save, void* y,
                                    int y_fmt, void* ws, size_t ws_bytes, hipStream_t stream) {
   clear_error();
   MOE_REQUIRE(E >= 1 && E <= kMaxGroups && H > 0 && F > 0 && rows >= 0, MOE_ERR_INVALID_ARG,
@@ -1013,8 +999,8 @@ extern "C" int moe_grouped_mlp_fwd(const void* a, const uint8_t* a_scales, int a
 extern "C" int moe_grouped_fc2_dgrad_dswiglu(const void* dy, const uint8_t* dy_scales, int fmt,
                                              const void* w2t, const uint8_t* w2t_scales,
                                              const int32_t* offsets, int E, int H, int F,
-                                             int64_t rows, const void* act_save, void* da,
-                                             uint8_t* da_scales, void* da_bf16,
+                                             int64_t rows, const float* act_save, void* da,
+                                             uint8_t* da_scales, float* da_f32,
                                              hipStream_t stream) {
   clear_error();
   MOE_REQUIRE(E >= 1 && E <= kMaxGroups && H > 0 && F > 0 && rows >= 0, MOE_ERR_INVALID_ARG,
@@ -1031,7 +1017,7 @@ extern "C" int moe_grouped_fc2_dgrad_dswiglu(const void* dy, const uint8_t* dy_s
                     scale_aligned(w2t_scales),
                 MOE_ERR_INVALID_ARG, "moe_grouped_fc2_dgrad_dswiglu: MX needs 4-byte aligned scales");
   MOE_REQUIRE(aligned16(dy) && aligned16(w2t) && aligned16(act_save) && aligned16(da) &&
-                  (!da_bf16 || aligned16(da_bf16)),
+                  (!da_f32 || aligned16(da_f32)),
               MOE_ERR_ALIGNMENT, "moe_grouped_fc2_dgrad_dswiglu: tensors must be 16-byte aligned");
   if (rows == 0) return MOE_OK;
   const int bits = elem_bits(fmt);
@@ -1055,8 +1041,8 @@ extern "C" int moe_grouped_fc2_dgrad_dswiglu(const void* dy, const uint8_t* dy_s
   g.out_row_bytes = 2ll * F * bits / 8;
   g.out_sc = da_scales;
   g.out_sc_row_bytes = 2 * F / 32;
-  g.a_saved = static_cast<const uint16_t*>(act_save);
-  g.da_bf16 = static_cast<uint16_t*>(da_bf16);
+  g.a_saved = static_cast<const float*>(act_save);
+  g.da_f32 = da_f32;
   const bool wide = F % 256 == 0;
   if (fmt == MOE_BF16)
     return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_BF16, EPI_DSWIGLU, MOE_BF16>(g, stream)

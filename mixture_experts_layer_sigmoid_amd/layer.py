@@ -11,9 +11,13 @@ and then issues, on one stream:
 MoEBackward runs the backward of the routed expert path (MXFP8), reusing
 the forward's routing and maps:
 
-    moe_combine_bwd -> moe_quantize_mx (dY) -> moe_grouped_fc2_dgrad_dswiglu
+    moe_combine_bwd (dY rows, MX) -> moe_grouped_fc2_dgrad_dswiglu
       -> moe_grouped_fc1_dgrad -> moe_unpermute
       -> moe_quantize_mx_segments (dY, h, dA, x) -> moe_grouped_wgrad (dW2, dW1)
+
+Intermediates that feed an MX quantization stay in fp32 (the saved fc1
+output, dA, the dY products), so rounding happens only where the MX
+operands are formed.
 
 Only marshalling happens here; every step of the layer runs in the HIP
 library.
@@ -124,8 +128,8 @@ class MoEForward:
             self.xq = self.xq_sc = None
         self.y_rows = torch.empty((max(1, self.bound), H), dtype=act, device=dev)
         self.h, self.h_sc = self._h_buffers(max(1, self.bound), F, dev)
-        # fc1 output (gate | up) per expert row, kept for the backward
-        self.act_save = (torch.empty((max(1, self.bound), 2 * F), dtype=torch.bfloat16, device=dev)
+        # fc1 output (gate | up) per expert row in fp32, kept for the backward
+        self.act_save = (torch.empty((max(1, self.bound), 2 * F), dtype=torch.float32, device=dev)
                          if save_act else None)
         if F_shared:
             self.shared_offsets = torch.tensor([0, T], **i32)
@@ -220,12 +224,13 @@ class MoEBackward:
         T, H, F, E, bound = fwd.T, fwd.H, fwd.F, fwd.E, max(1, fwd.bound)
         dev = fwd.topk_idx.device
         u8, bf = dict(dtype=torch.uint8, device=dev), dict(dtype=torch.bfloat16, device=dev)
-        self.dy = torch.empty((bound, H), **bf)
+        f32 = dict(dtype=torch.float32, device=dev)
         self.dy_q = torch.empty((bound, H), **u8)
         self.dy_sc = torch.empty((bound, H // 32), **u8)
+        self.row_w = torch.empty((bound,), **f32)
         self.da = torch.empty((bound, 2 * F), **u8)
         self.da_sc = torch.empty((bound, 2 * F // 32), **u8)
-        self.da_bf16 = torch.empty((bound, 2 * F), **bf)
+        self.da_f32 = torch.empty((bound, 2 * F), **f32)
         self.dx_perm = torch.empty((bound, H), **bf)
         self.dx = torch.empty((T, H), **bf)
         ks = L.moe_segments_kstride(fwd.bound, E)
@@ -243,32 +248,32 @@ class MoEBackward:
         f, fw = FMT["mxfp8"], self.fwd
         T, H, F, E, k, rows = fw.T, fw.H, fw.F, fw.E, fw.k, fw.bound
         L.moe_combine_bwd(dout, fw.act_fmt, fw.row_map, fw.src_row, fw.topk_w, T, k, H, rows,
-                          self.dy, stream)
-        L.moe_quantize_mx(self.dy, L.MOE_BF16, rows, H, 0, f, self.dy_q, self.dy_sc, stream)
+                          self.dy_q, f, self.dy_sc, self.row_w, stream)
         L.moe_grouped_fc2_dgrad_dswiglu(self.dy_q, self.dy_sc, f, ew.w2t, ew.w2t_sc, fw.offsets,
                                         E, H, F, rows, fw.act_save, self.da, self.da_sc,
-                                        self.da_bf16, stream)
+                                        self.da_f32, stream)
         L.moe_grouped_fc1_dgrad(self.da, self.da_sc, f, ew.w1t, ew.w1t_sc, fw.offsets, E, H, F,
                                 rows, self.dx_perm, stream)
         L.moe_unpermute(self.dx_perm, L.MOE_BF16, fw.row_map, T, k, H, self.dx, L.MOE_BF16, stream)
 
-    def weight_grad(self, x, stream=None):
+    def weight_grad(self, dout, x, stream=None):
         """dW2 = dY^T h and dW1 = dA^T x per expert, contracting over the
         expert's rows (MX blocks of 32 rows of the segment)."""
         f, fw = FMT["mxfp8"], self.fwd
         H, F, E, rows, ks = fw.H, fw.F, fw.E, fw.bound, self.kstride
-        seg = lambda src, mode, C, c, s: L.moe_quantize_mx_segments(
-            src, mode, fw.src_row, fw.offsets, E, rows, C, ks, f, c, s, self.kofs, stream)
-        seg(self.dy, 0, H, self.dyT, self.dyT_sc)
-        seg(fw.act_save, 2, F, self.hT, self.hT_sc)
+        seg = lambda src, in_fmt, mode, scale, C, c, s: L.moe_quantize_mx_segments(
+            src, in_fmt, mode, fw.src_row, fw.offsets, scale, E, rows, C, ks, f, c, s, self.kofs,
+            stream)
+        seg(dout, fw.act_fmt, 1, self.row_w, H, self.dyT, self.dyT_sc)       # w * dout rows
+        seg(fw.act_save, L.MOE_F32, 2, None, F, self.hT, self.hT_sc)         # h recomputed
         L.moe_grouped_wgrad(self.dyT, self.dyT_sc, self.hT, self.hT_sc, f, self.kofs, E, H, F, ks,
                             self.dw2, stream)
-        seg(self.da_bf16, 0, 2 * F, self.daT, self.daT_sc)
-        seg(x, 1, H, self.xT, self.xT_sc)
+        seg(self.da_f32, L.MOE_F32, 0, None, 2 * F, self.daT, self.daT_sc)
+        seg(x, fw.act_fmt, 1, None, H, self.xT, self.xT_sc)
         L.moe_grouped_wgrad(self.daT, self.daT_sc, self.xT, self.xT_sc, f, self.kofs, E, 2 * F, H,
                             ks, self.dw1, stream)
 
     def __call__(self, dout, x, ew: ExpertWeights, stream=None):
         self.data_grad(dout, ew, stream)
-        self.weight_grad(x, stream)
+        self.weight_grad(dout, x, stream)
         return self.dx, self.dw1, self.dw2

@@ -139,21 +139,26 @@ def test_backward_validation(lib):
     assert lib.moe_segments_kstride(0, 0) == -1
     # combine backward: bad k, unsupported dout format, alignment
     cb = lambda **k: lib.moe_combine_bwd(k.get("d", A), k.get("df", 1), A, A, A, 4, k.get("k", 2),
-                                         64, 32, k.get("dy", A), None)
+                                         k.get("H", 64), 32, k.get("dy", A), k.get("of", 1),
+                                         k.get("ds", A), None, None)
     assert cb(k=0) == INVALID
     assert cb(df=2) == UNSUPPORTED
+    assert cb(of=7) == UNSUPPORTED
+    assert cb(of=2, H=72) == INVALID              # MX dy needs H % 32 == 0
+    assert cb(of=2, ds=None) == INVALID           # MX dy needs its scales
     assert cb(dy=A + 2) == ALIGN
     un = lambda **k: lib.moe_unpermute(A, k.get("f", 1), A, 4, 2, k.get("H", 64), A,
                                        k.get("of", 1), None)
     assert un(H=60) == INVALID
     assert un(of=3) == UNSUPPORTED
     qs = lambda **k: lib.moe_quantize_mx_segments(
-        A, k.get("mode", 0), A, A, 4, k.get("rows", 128), 64, k.get("ks", 1024), k.get("fo", 2),
-        A, A, A, None)
+        A, k.get("fi", 1), k.get("mode", 0), k.get("src", A), A, None, 4, k.get("rows", 128), 64,
+        k.get("ks", 1024), k.get("fo", 2), A, A, A, None)
     assert qs(mode=3) == INVALID
     assert qs(fo=1) == UNSUPPORTED
+    assert qs(fi=2) == UNSUPPORTED
     assert qs(ks=256) == INVALID                  # below moe_segments_kstride(128, 4)
-    assert lib.moe_quantize_mx_segments(A, 0, None, A, 4, 128, 64, 1024, 2, A, A, A, None) == INVALID
+    assert qs(src=None) == INVALID
     # grouped GEMMs: bad shapes and formats are rejected before any launch
     d2 = lambda **k: lib.moe_grouped_fc2_dgrad_dswiglu(
         A, A, k.get("f", 2), A, A, A, 4, k.get("H", 256), k.get("F", 128), 64, A, A, A, None, None)

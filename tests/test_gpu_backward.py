@@ -52,14 +52,28 @@ def test_combine_bwd_and_unpermute(gpu_lib):
     dout = _bf16(g.standard_normal((T, H)))
     w = g.uniform(0.05, 1.0, (T, k)).astype(np.float32)
     dy = torch.full((bound, H), 3.0, dtype=torch.bfloat16, device="cuda")
+    dyf = torch.full((bound, H), 3.0, dtype=torch.float32, device="cuda")
+    dyq = torch.full((bound, H), 3, dtype=torch.uint8, device="cuda")
+    dys = torch.full((bound, H // 32), 3, dtype=torch.uint8, device="cuda")
+    row_w = torch.full((bound,), 3.0, dtype=torch.float32, device="cuda")
     rm, sr = torch.from_numpy(row_map.astype(np.int32)).cuda(), torch.from_numpy(src.astype(np.int32)).cuda()
-    moe.moe_combine_bwd(dev(dout, "bf16"), moe.MOE_BF16, rm, sr, dev(w), T, k, H, bound, dy)
+    d_dout, d_w = dev(dout, "bf16"), dev(w)
+    moe.moe_combine_bwd(d_dout, moe.MOE_BF16, rm, sr, d_w, T, k, H, bound, dy, moe.MOE_BF16, None, None)
+    moe.moe_combine_bwd(d_dout, moe.MOE_BF16, rm, sr, d_w, T, k, H, bound, dyf, moe.MOE_F32, None, None)
+    moe.moe_combine_bwd(d_dout, moe.MOE_BF16, rm, sr, d_w, T, k, H, bound, dyq, moe.MOE_MXFP8_E4M3, dys,
+                        row_w)
     torch.cuda.synchronize()
     ref = np.zeros((bound, H), np.float32)
+    ref_w = np.zeros(bound, np.float32)
     for t in range(T):
         for j in range(k):
             ref[row_map[t, j]] = w[t, j] * dout[t]
+            ref_w[row_map[t, j]] = w[t, j]
     assert np.array_equal(host(dy), _bf16(ref))
+    assert np.array_equal(host(dyf), ref)
+    assert np.array_equal(host(row_w), ref_w)
+    qc, qs = omx.quantize(ref, "e4m3", axis=-1)
+    assert np.array_equal(host(dyq), qc) and np.array_equal(host(dys), qs)
     # un-permute of random expert rows: fp32 sums in slot order, bf16 out
     rows = _bf16(g.standard_normal((bound, H)))
     dx = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
@@ -108,30 +122,39 @@ def _segments_expected(vals, src, offsets, E, fmt, pad=128):
     return np.concatenate(cols, axis=1), np.concatenate(scs, axis=1), np.array(kofs)
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2])
-def test_quantize_segments(gpu_lib, mode):
+@pytest.mark.parametrize("mode,in_fmt,scaled", [(0, "bf16", False), (0, "fp32", False),
+                                                (1, "bf16", False), (1, "bf16", True),
+                                                (2, "fp32", False)])
+def test_quantize_segments(gpu_lib, mode, in_fmt, scaled):
     T, E, k, C = 173, 12, 3, 320
-    log(f"segment quantize mode {mode} T={T} E={E} C={C}")
+    log(f"segment quantize mode {mode} {in_fmt} scaled={scaled} T={T} E={E} C={C}")
     idx, counts, offsets, row_map, src = _maps(T, E, k, 32, 7)
     bound = len(src)
     g = np.random.default_rng(8 + mode)
+    rnd = (lambda a: _bf16(a)) if in_fmt == "bf16" else (lambda a: np.asarray(a, np.float32))
     if mode == 0:
-        inp = _bf16(g.standard_normal((bound, C)))
+        inp = rnd(g.standard_normal((bound, C)))
         vals = inp
     elif mode == 1:
-        inp = _bf16(g.standard_normal((T, C)))
+        inp = rnd(g.standard_normal((T, C)))
         vals = pm.permute_rows(inp, src)
     else:
-        inp = _bf16(g.standard_normal((bound, 2 * C)) * 2)
+        inp = rnd(g.standard_normal((bound, 2 * C)) * 2)
         from oracle import mlp as omlp
         vals = omlp.swiglu(inp, C)
+    scale = None
+    if scaled:
+        rs = g.uniform(0.05, 1.0, bound).astype(np.float32)
+        vals = (vals * rs[:, None]).astype(np.float32)
+        scale = dev(rs)
     ks = moe.moe_segments_kstride(bound, E)
     codes = torch.zeros((C, ks), dtype=torch.uint8, device="cuda")
     scales = torch.zeros((C, ks // 32), dtype=torch.uint8, device="cuda")
     kofs = torch.empty((E + 1,), **I32)
-    moe.moe_quantize_mx_segments(dev(inp, "bf16"), mode, torch.from_numpy(src.astype(np.int32)).cuda(),
-                                 torch.from_numpy(offsets.astype(np.int32)).cuda(), E, bound, C, ks,
-                                 moe.MOE_MXFP8_E4M3, codes, scales, kofs)
+    moe.moe_quantize_mx_segments(dev(inp, in_fmt), moe.FMT[in_fmt], mode,
+                                 torch.from_numpy(src.astype(np.int32)).cuda(),
+                                 torch.from_numpy(offsets.astype(np.int32)).cuda(), scale, E, bound, C,
+                                 ks, moe.MOE_MXFP8_E4M3, codes, scales, kofs)
     torch.cuda.synchronize()
     ec, es, ekofs = _segments_expected(vals, src, offsets, E, "mxfp8")
     assert np.array_equal(host(kofs), ekofs)
@@ -166,8 +189,8 @@ def test_wgrad_ragged_segments(gpu_lib, M, N):
     for vals, C in ((A, M), (B, N)):
         c = torch.empty((C, ks), dtype=torch.uint8, device="cuda")
         s = torch.empty((C, ks // 32), dtype=torch.uint8, device="cuda")
-        moe.moe_quantize_mx_segments(dev(vals, "bf16"), 0, src_d, off_d, E, bound, C, ks,
-                                     moe.MOE_MXFP8_E4M3, c, s, kofs)
+        moe.moe_quantize_mx_segments(dev(vals, "bf16"), moe.MOE_BF16, 0, src_d, off_d, None, E, bound,
+                                     C, ks, moe.MOE_MXFP8_E4M3, c, s, kofs)
         bufs += [c, s]
     dw = torch.full((E, M, N), 5.0, dtype=torch.bfloat16, device="cuda")
     moe.moe_grouped_wgrad(bufs[0], bufs[1], bufs[2], bufs[3], moe.MOE_MXFP8_E4M3, kofs, E, M, N, ks, dw)

@@ -51,7 +51,7 @@ def _run(cfg, x_d, ew, offsets, src, bound, T, act_save=False, direct_rows=None)
         a, a_sc = (x_d if direct_rows is None else direct_rows), None
     act = x_d.dtype
     y = torch.full((bound, cfg.H), 7.0, dtype=act, device="cuda")
-    save = torch.zeros((bound, 2 * cfg.F), dtype=torch.bfloat16, device="cuda") if act_save else None
+    save = torch.zeros((bound, 2 * cfg.F), dtype=torch.float32, device="cuda") if act_save else None
     ws = torch.empty(max(1, moe.moe_grouped_mlp_workspace(ew.w1.shape[0], cfg.H, cfg.F, bound, f, f)),
                      dtype=torch.uint8, device="cuda")
     off_d = torch.from_numpy(offsets.astype(np.int32)).cuda()
@@ -107,7 +107,8 @@ def test_stage_parity(gpu_lib, name, T, k, heavy, align):
     assert err < TOL[cfg.fmt]
     assert (y[:used][~live] == 0).all(), "padding rows must be zero"
     assert (y[used:] == 7.0).all(), "rows past the segments are not written"
-    assert rel_l2(save[:used][live], a_ref[:used][live]) < 1e-2
+    # the saved fc1 output is the fp32 accumulator (summation order aside)
+    assert rel_l2(save[:used][live], a_ref[:used][live]) < 1e-5
 
 
 def test_fallback_tiles_bf16(gpu_lib):
