@@ -107,8 +107,10 @@ def test_stage_parity(gpu_lib, name, T, k, heavy, align):
     assert err < TOL[cfg.fmt]
     assert (y[:used][~live] == 0).all(), "padding rows must be zero"
     assert (y[used:] == 7.0).all(), "rows past the segments are not written"
-    # the saved fc1 output is the fp32 accumulator (summation order aside)
-    assert rel_l2(save[:used][live], a_ref[:used][live]) < 1e-5
+    # the saved fc1 output is the unrounded accumulator: equal to the oracle's
+    # fp32 product up to summation order (the MX matrix instructions add each
+    # 64-element block product at their own internal precision: ~1e-5)
+    assert rel_l2(save[:used][live], a_ref[:used][live]) < (1e-5 if cfg.fmt == "fp32" else 1e-4)
 
 
 def test_fallback_tiles_bf16(gpu_lib):
