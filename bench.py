@@ -1,24 +1,31 @@
-"""Throughput of the routed MoE layer forward on one MI355X.
+"""Throughput of the routed MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--cpu-tokens N]
 
-A step is one whole forward pass (router GEMM + grouped top-k, permute maps,
-grouped fc1 + SwiGLU, grouped fc2, shared expert, combine) over one batch of
-synthetic inputs that are resident in HBM before timing starts. W untimed
+A step is one whole pass of the layer over one batch of synthetic inputs
+that are resident in HBM before timing starts: router GEMM + grouped top-k,
+MX quantization of the hidden states (MX workloads), permute maps, grouped
+fc1 + SwiGLU, grouped fc2, shared expert, combine; for the workload with a
+backward also the whole backward (combine backward with the dY quantization,
+fc2 data gradient fused with the SwiGLU backward, fc1 data gradient,
+un-permute, segment quantizations and both weight-gradient GEMMs). W untimed
 warm-up steps, then exactly K timed steps bracketed by device
 synchronization. One JSON line is printed.
 
 The default workload is DeepSeek-V3 dims at 4096 tokens, bf16 (hidden 7168,
 expert FFN 2048, 256 experts in 8 groups, top-4 groups, top-8, routed scale
-2.5, one shared expert).
-Other workloads of the same family can be chosen with --workload for study;
-their lines carry their own name in config.workload.
+2.5, one shared expert). --workload picks another configuration of the
+layer; its line carries its own name in config.workload.
 
-Inside the timed region the dominant kernel (grouped fc1 + SwiGLU) is
-bracketed by HIP events on the stream it is launched on; its average
-duration gives the roofline entry. The CPU baseline times the oracle (plain
-numpy) on the first --cpu-tokens tokens of the same batch.
+Inside the timed region every stage is bracketed by HIP events on the stream
+its kernels are launched on. The stage with the largest average duration is
+the dominant kernel of the roofline entry: its algorithmic bytes and flops
+per launch (weights of the experts that received rows read once, activation
+rows read or written once, in their storage formats) decide the bound
+(arithmetic intensity against the ridge of the format's MFMA peak over the
+8 TB/s HBM peak) and the achieved rate. The CPU baseline times the oracle
+(plain numpy) on the first --cpu-tokens tokens of the same batch.
 """
 from __future__ import annotations
 
@@ -33,37 +40,79 @@ import numpy as np
 METRIC = "MoE layer tokens/s + TFLOP/s (% MFMA peak) at DSV3 dims, 4096 tok, 1 GPU"
 PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
+# bytes per stored element (MX: code + one scale byte per 32 elements)
+ELEM_BYTES = {"bf16": 2.0, "fp32": 4.0, "mxfp8": 1 + 1 / 32, "mxfp4": 0.5 + 1 / 32}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def fc1_algorithmic_bytes(cfg, counts: np.ndarray) -> float:
-    """Bytes fc1 + SwiGLU must move: the fc1 weights of every expert that
-    received rows (read once), the token rows (read once), and h (written
-    once), in the layer's storage formats."""
+def stage_work(cfg, counts: np.ndarray, backward: bool):
+    """Algorithmic (bytes, flops) per launch of each timed stage."""
+    T, H, F, E, k = cfg.T, cfg.H, cfg.F, cfg.E, cfg.k
+    R = T * k                                   # token-expert rows
     touched = int((counts > 0).sum())
-    if cfg.fmt == "bf16":
-        wbytes, xbytes, hbytes = 2.0, 2.0, 2.0
-    elif cfg.fmt == "mxfp8":
-        wbytes, xbytes, hbytes = 1 + 1 / 32, 1 + 1 / 32, 1 + 1 / 32
-    elif cfg.fmt == "mxfp4":
-        wbytes, xbytes, hbytes = 0.5 + 1 / 32, 0.5 + 1 / 32, 0.5 + 1 / 32
-    else:
-        wbytes, xbytes, hbytes = 4.0, 4.0, 4.0
-    w = touched * 2 * cfg.F * cfg.H * wbytes
-    x = cfg.T * cfg.H * xbytes
-    h = cfg.rows * cfg.F * hbytes
-    return w + x + h
+    wb = ELEM_BYTES[cfg.fmt]
+    ab = ELEM_BYTES[cfg.act_dtype]              # bf16 / fp32 activations
+    qb = wb                                     # layer-format activation rows
+    work = {}
+    work["route"] = (T * H * ab + E * H * ab + T * k * 8, 2.0 * T * H * E)
+    if cfg.fmt in ("mxfp8", "mxfp4"):
+        work["quantize_x"] = (T * H * ab + T * H * qb, 0.0)
+    work["permute"] = (T * k * 4 * 3 + E * 8, 0.0)
+    save = R * 2 * F * 4 if backward else 0
+    work["fc1_swiglu"] = (touched * 2 * F * H * wb + T * H * qb + R * F * qb + save,
+                          2.0 * R * H * 2 * F)
+    work["fc2"] = (touched * H * F * wb + R * F * qb + R * H * ab, 2.0 * R * F * H)
+    if cfg.n_shared:
+        Fs = cfg.F_shared
+        work["shared"] = (2 * Fs * H * wb + H * Fs * wb + T * H * qb + T * H * ab,
+                          2.0 * T * H * 2 * Fs + 2.0 * T * Fs * H)
+    work["combine"] = (R * H * ab + T * H * ab * (2 if cfg.n_shared else 1), 0.0)
+    if backward:
+        work["combine_bwd"] = (R * H * ab + R * H * qb, 0.0)
+        work["fc2_dgrad_dswiglu"] = (touched * F * H * wb + R * H * qb + R * 2 * F * 4
+                                     + R * 2 * F * (qb + 4), 2.0 * R * H * F)
+        work["fc1_dgrad"] = (touched * H * 2 * F * wb + R * 2 * F * qb + R * H * 2,
+                             2.0 * R * 2 * F * H)
+        work["unpermute"] = (R * H * 2 + T * H * 2, 0.0)
+        work["wgrad_dw2"] = (R * H * ab + R * 2 * F * 4 + R * (H + F) * qb * 2
+                             + E * H * F * 2, 2.0 * R * H * F)
+        work["wgrad_dw1"] = (R * 2 * F * 4 + R * H * ab + R * (2 * F + H) * qb * 2
+                             + E * 2 * F * H * 2, 2.0 * R * 2 * F * H)
+    return work
 
 
-def cpu_baseline(cfg, x, wr, b, wts, sh, n_tokens: int):
-    """Time the oracle forward on the first n_tokens tokens (weights held on
-    the host in their bf16 storage type and widened to fp32 by the oracle's
-    weight accessors, as the oracle consumes them)."""
+def roofline_entry(name, nbytes, flops, ms, fmt):
+    peak_f = PEAK_TFLOPS[fmt]
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)     # flop per byte
+    if flops > 0 and flops / nbytes >= ridge:
+        ach = flops / (ms * 1e-3) / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": round(ach, 1), "peak": peak_f,
+                "unit": "TFLOP/s", "frac": round(ach / peak_f, 4), "traffic": None,
+                "flops_per_launch": flops, "bytes_per_launch": nbytes,
+                "avg_launch_ms": round(ms, 4)}
+    ach = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+            "bytes_per_launch": nbytes, "flops_per_launch": flops, "avg_launch_ms": round(ms, 4)}
+
+
+def _host_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(cfg, x, wr, b, wts, sh, dout, n_tokens: int, backward: bool):
+    """Time the oracle on the first n_tokens tokens (weights held on the host
+    in their bf16 storage type and widened to fp32 by the oracle's weight
+    accessors, as the oracle consumes them)."""
     import torch
-    from oracle import mlp as omlp
+    from oracle import backward as obw, mlp as omlp, routing as rt
     log(f"cpu baseline: copying weights to the host for {n_tokens} tokens")
     w1h = wts["w1"].view(torch.int16).cpu().numpy().view(np.uint16)
     w2h = wts["w2"].view(torch.int16).cpu().numpy().view(np.uint16)
@@ -72,20 +121,24 @@ def cpu_baseline(cfg, x, wr, b, wts, sh, n_tokens: int):
         shared = (sh["w1s"].float().cpu().numpy(), sh["w2s"].float().cpu().numpy())
     widen = lambda u: (u.astype(np.uint32) << 16).view(np.float32)
     xs = x[:n_tokens]
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    log(f"cpu baseline: oracle forward on {n_tokens} tokens, {threads} BLAS threads")
+    threads = _host_threads()
+    log(f"cpu baseline: oracle on {n_tokens} tokens, {threads} BLAS threads")
     t0 = time.perf_counter()
-    omlp.moe_forward(xs, wr, b, lambda e: widen(w1h[e]), lambda e: widen(w2h[e]), E=cfg.E,
-                     n_group=cfg.n_group, topk_group=cfg.topk_group, k=cfg.k,
-                     routed_scale=cfg.routed_scale, fmt=cfg.fmt, shared_w=shared)
+    ref = omlp.moe_forward(xs, wr, b, lambda e: widen(w1h[e]), lambda e: widen(w2h[e]), E=cfg.E,
+                           n_group=cfg.n_group, topk_group=cfg.topk_group, k=cfg.k,
+                           routed_scale=cfg.routed_scale, fmt=cfg.fmt, align=cfg.align,
+                           shared_w=shared)
+    what = f"oracle forward (routing, {cfg.k} routed experts"
+    what += " + shared expert" if shared else ""
+    what += ", combine)"
+    if backward:
+        obw.moe_backward(xs, dout[:n_tokens], ref["idx"], ref["w"], lambda e: widen(w1h[e]),
+                         lambda e: widen(w2h[e]), E=cfg.E, fmt=cfg.fmt)
+        what += " and backward (dX and every touched expert's dW)"
     dt = time.perf_counter() - t0
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle forward (routing, {cfg.k} routed experts + shared expert, combine) "
-                      f"of the first {n_tokens} tokens of the {cfg.T}-token batch; {dt:.1f} s"}
+            "sample": f"{what} of the first {n_tokens} tokens of the {cfg.T}-token batch; "
+                      f"{dt:.1f} s"}
 
 
 def main():
@@ -95,7 +148,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_bf16_t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=96)
+    ap.add_argument("--cpu-tokens", type=int, default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the layer runs on a single MI355X with no "
@@ -107,6 +160,7 @@ def main():
     from moe_synth import configs, gen
 
     cfg = configs.get(args.workload)
+    backward = bool(cfg.backward)
     moe.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -114,56 +168,107 @@ def main():
     x = gen.host_x(cfg)
     wr = gen.host_router(cfg)
     b = gen.host_bias(cfg)
+    dout = gen.host_dout(cfg) if backward else None
     act = torch.float32 if cfg.act_dtype == "fp32" else torch.bfloat16
     x_d = torch.from_numpy(x).to(dev).to(act)
     wr_d = torch.from_numpy(wr).to(dev).to(act)
     b_d = torch.from_numpy(b).to(dev)
+    dout_d = torch.from_numpy(dout).to(dev).to(act) if backward else None
     wts = gen.device_expert_weights(cfg, dev)
     sh = gen.device_shared_weights(cfg, dev) if cfg.n_shared else None
-    ew = moe.ExpertWeights.from_dense(wts["w1"], wts["w2"], cfg.fmt)
+    # weight preparation (MX quantization, transposed copies for the
+    # backward) happens once per weight update, outside the timed step
+    ew = moe.ExpertWeights.from_dense(wts["w1"], wts["w2"], cfg.fmt, transposed=backward)
     sw = moe.ExpertWeights.from_dense(sh["w1s"], sh["w2s"], cfg.fmt) if sh else None
-    if moe.layer.is_mx(cfg.fmt):
+    want_cpu = not args.no_cpu_baseline
+    if moe.layer.is_mx(cfg.fmt) and not want_cpu:
         del wts["w1"], wts["w2"]
-    fw = moe.MoEForward.for_config(cfg, device=dev)
+    fw = moe.MoEForward.for_config(cfg, device=dev, save_act=backward)
+    bw = moe.MoEBackward(fw) if backward else None
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 
-    def step(ev=None):
-        fw.route(x_d, wr_d, b_d)
-        fw.quantize_x(x_d)
-        fw.permute()
-        if ev is not None:
-            ev[0].record(stream)
-        fw.experts_fc1(x_d, ew)
-        if ev is not None:
-            ev[1].record(stream)
-        fw.experts_fc2(ew)
-        if cfg.n_shared:
+    names = ["route", "quantize_x", "permute", "fc1_swiglu", "fc2", "shared", "combine"]
+    if backward:
+        names += ["combine_bwd", "fc2_dgrad_dswiglu", "fc1_dgrad", "unpermute", "wgrad_dw2",
+                  "wgrad_dw1"]
+    if not moe.layer.is_mx(cfg.fmt):
+        names.remove("quantize_x")
+    if not cfg.n_shared:
+        names.remove("shared")
+    f8 = moe.FMT["mxfp8"]
+
+    def run_stage(name):
+        if name == "route":
+            fw.route(x_d, wr_d, b_d)
+        elif name == "quantize_x":
+            fw.quantize_x(x_d)
+        elif name == "permute":
+            fw.permute()
+        elif name == "fc1_swiglu":
+            fw.experts_fc1(x_d, ew)
+        elif name == "fc2":
+            fw.experts_fc2(ew)
+        elif name == "shared":
             fw.shared(x_d, sw)
-        fw.combine()
+        elif name == "combine":
+            fw.combine()
+        elif name == "combine_bwd":
+            moe.moe_combine_bwd(dout_d, fw.act_fmt, fw.row_map, fw.src_row, fw.topk_w, fw.T, fw.k,
+                                fw.H, fw.bound, bw.dy_q, f8, bw.dy_sc, bw.row_w)
+        elif name == "fc2_dgrad_dswiglu":
+            moe.moe_grouped_fc2_dgrad_dswiglu(bw.dy_q, bw.dy_sc, f8, ew.w2t, ew.w2t_sc, fw.offsets,
+                                              fw.E, fw.H, fw.F, fw.bound, fw.act_save, bw.da,
+                                              bw.da_sc, bw.da_f32)
+        elif name == "fc1_dgrad":
+            moe.moe_grouped_fc1_dgrad(bw.da, bw.da_sc, f8, ew.w1t, ew.w1t_sc, fw.offsets, fw.E,
+                                      fw.H, fw.F, fw.bound, bw.dx_perm)
+        elif name == "unpermute":
+            moe.moe_unpermute(bw.dx_perm, moe.MOE_BF16, fw.row_map, fw.T, fw.k, fw.H, bw.dx,
+                              moe.MOE_BF16)
+        elif name == "wgrad_dw2":
+            bw.weight_grad_dw2(dout_d)
+        elif name == "wgrad_dw1":
+            bw.weight_grad_dw1(x_d)
+
+    def step(evs=None):
+        for i, n in enumerate(names):
+            if evs is not None:
+                evs[i][0].record(stream)
+            run_stage(n)
+            if evs is not None:
+                evs[i][1].record(stream)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in names] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps of {len(names)} stages")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    fc1_ms = float(np.mean([a.elapsed_time(c) for a, c in evs]))
+    stage_ms = {n: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1])
+                                  for s in range(args.steps)])) for i, n in enumerate(names)}
     ms_per_step = elapsed * 1e3 / args.steps
     counts = fw.counts.cpu().numpy()
+    work = stage_work(cfg, counts, backward)
 
     tokens_per_s = cfg.T * args.steps / elapsed
-    tflops = cfg.flops_forward() / (ms_per_step * 1e-3) / 1e12
+    flops = cfg.flops_forward() + (cfg.flops_backward() if backward else 0.0)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[cfg.fmt]
-    fc1_bytes = fc1_algorithmic_bytes(cfg, counts)
-    achieved = fc1_bytes / (fc1_ms * 1e-3) / 1e9
+    dom = max(names, key=lambda n: stage_ms[n])
+    roof = roofline_entry(dom, work[dom][0], work[dom][1], stage_ms[dom], cfg.fmt)
+    stages = {n: {"ms": round(stage_ms[n], 4),
+                  **({"gbs": round(work[n][0] / (stage_ms[n] * 1e-3) / 1e9, 1)} if n in work else {}),
+                  **({"tflops": round(work[n][1] / (stage_ms[n] * 1e-3) / 1e12, 1)}
+                     if n in work and work[n][1] else {})}
+              for n in names}
     rec = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -177,19 +282,19 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.fmt,
         "data": "synthetic (seeded; random-init weights of the layer's shapes)",
-        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "expert_ffn": cfg.F,
-                   "experts": cfg.E, "n_group": cfg.n_group, "topk_group": cfg.topk_group,
-                   "top_k": cfg.k, "routed_scale": cfg.routed_scale,
-                   "shared_experts": cfg.n_shared, "parallelism": "single GPU"},
+        "config": {"workload": cfg.name, "pass": "forward+backward" if backward else "forward",
+                   "tokens": cfg.T, "hidden": cfg.H, "expert_ffn": cfg.F, "experts": cfg.E,
+                   "n_group": cfg.n_group, "topk_group": cfg.topk_group, "top_k": cfg.k,
+                   "routed_scale": cfg.routed_scale, "shared_experts": cfg.n_shared,
+                   "experts_with_rows": int((counts > 0).sum()), "parallelism": "single GPU"},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / peak, 4),
-        "roofline": {"kernel": "grouped fc1 + SwiGLU", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "bytes_per_launch": fc1_bytes, "avg_launch_ms": round(fc1_ms, 4)},
+        "roofline": roof,
+        "stages": stages,
     }
-    if not args.no_cpu_baseline and cfg.fmt == "bf16":
-        rec["cpu_baseline"] = cpu_baseline(cfg, x, wr, b, wts, sh, args.cpu_tokens)
+    if want_cpu:
+        n = args.cpu_tokens or (1 if backward else (96 if cfg.fmt == "bf16" else 2))
+        rec["cpu_baseline"] = cpu_baseline(cfg, x, wr, b, wts, sh, dout, min(n, cfg.T), backward)
     print(json.dumps(rec), flush=True)
 
 

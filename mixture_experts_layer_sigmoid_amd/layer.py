@@ -256,22 +256,33 @@ class MoEBackward:
                                 rows, self.dx_perm, stream)
         L.moe_unpermute(self.dx_perm, L.MOE_BF16, fw.row_map, T, k, H, self.dx, L.MOE_BF16, stream)
 
+    def _seg(self, src, in_fmt, mode, scale, C, codes, scales, stream):
+        fw = self.fwd
+        L.moe_quantize_mx_segments(src, in_fmt, mode, fw.src_row, fw.offsets, scale, fw.E,
+                                   fw.bound, C, self.kstride, FMT["mxfp8"], codes, scales,
+                                   self.kofs, stream)
+
+    def weight_grad_dw2(self, dout, stream=None):
+        """dW2 = dY^T h per expert, contracting over the expert's rows (MX
+        blocks of 32 rows of the segment): dY rows formed as w * dout, h
+        recomputed from the saved fc1 output."""
+        fw = self.fwd
+        self._seg(dout, fw.act_fmt, 1, self.row_w, fw.H, self.dyT, self.dyT_sc, stream)
+        self._seg(fw.act_save, L.MOE_F32, 2, None, fw.F, self.hT, self.hT_sc, stream)
+        L.moe_grouped_wgrad(self.dyT, self.dyT_sc, self.hT, self.hT_sc, FMT["mxfp8"], self.kofs,
+                            fw.E, fw.H, fw.F, self.kstride, self.dw2, stream)
+
+    def weight_grad_dw1(self, x, stream=None):
+        """dW1 = dA^T x per expert, contracting over the expert's rows."""
+        fw = self.fwd
+        self._seg(self.da_f32, L.MOE_F32, 0, None, 2 * fw.F, self.daT, self.daT_sc, stream)
+        self._seg(x, fw.act_fmt, 1, None, fw.H, self.xT, self.xT_sc, stream)
+        L.moe_grouped_wgrad(self.daT, self.daT_sc, self.xT, self.xT_sc, FMT["mxfp8"], self.kofs,
+                            fw.E, 2 * fw.F, fw.H, self.kstride, self.dw1, stream)
+
     def weight_grad(self, dout, x, stream=None):
-        """dW2 = dY^T h and dW1 = dA^T x per expert, contracting over the
-        expert's rows (MX blocks of 32 rows of the segment)."""
-        f, fw = FMT["mxfp8"], self.fwd
-        H, F, E, rows, ks = fw.H, fw.F, fw.E, fw.bound, self.kstride
-        seg = lambda src, in_fmt, mode, scale, C, c, s: L.moe_quantize_mx_segments(
-            src, in_fmt, mode, fw.src_row, fw.offsets, scale, E, rows, C, ks, f, c, s, self.kofs,
-            stream)
-        seg(dout, fw.act_fmt, 1, self.row_w, H, self.dyT, self.dyT_sc)       # w * dout rows
-        seg(fw.act_save, L.MOE_F32, 2, None, F, self.hT, self.hT_sc)         # h recomputed
-        L.moe_grouped_wgrad(self.dyT, self.dyT_sc, self.hT, self.hT_sc, f, self.kofs, E, H, F, ks,
-                            self.dw2, stream)
-        seg(self.da_f32, L.MOE_F32, 0, None, 2 * F, self.daT, self.daT_sc)
-        seg(x, fw.act_fmt, 1, None, H, self.xT, self.xT_sc)
-        L.moe_grouped_wgrad(self.daT, self.daT_sc, self.xT, self.xT_sc, f, self.kofs, E, 2 * F, H,
-                            ks, self.dw1, stream)
+        self.weight_grad_dw2(dout, stream)
+        self.weight_grad_dw1(x, stream)
 
     def __call__(self, dout, x, ew: ExpertWeights, stream=None):
         self.data_grad(dout, ew, stream)
