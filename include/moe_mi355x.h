@@ -103,6 +103,11 @@ const char* moe_last_error(void);
  *            selection starts from these logits.
  * logits_out optional [T, E] fp32: receives the logits used.
  * topk_idx   [T, k] int32 out; topk_w [T, k] fp32 out.
+ * ws         device workspace of at least moe_route_workspace(T, H, E)
+ *            bytes for the router GEMM's partial sums (the GEMM is split
+ *            along H when T is small; the partials are added in chunk
+ *            order); may be NULL when logits_in is given. Otherwise
+ *            MOE_ERR_WORKSPACE.
  * Limits: 1 <= E <= 512, E % n_group == 0, E / n_group >= 2 when
  * n_group > 1, 1 <= topk_group <= n_group, 1 <= k <= min(16,
  * topk_group * E / n_group), H % 32 == 0 (bf16) when the GEMM runs.
@@ -111,7 +116,11 @@ const char* moe_last_error(void);
 int moe_route(const void* x, int x_fmt, const void* w_router, const float* bias,
               const float* logits_in, int T, int H, int E, int n_group,
               int topk_group, int k, float routed_scale, float* logits_out,
-              int32_t* topk_idx, float* topk_w, hipStream_t stream);
+              int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+              hipStream_t stream);
+
+/* moe_route_workspace — bytes of moe_route's workspace (0 for bad sizes). */
+size_t moe_route_workspace(int T, int H, int E);
 
 /*
  * moe_quantize_mx — MX block quantization of a [rows, K] tensor along K

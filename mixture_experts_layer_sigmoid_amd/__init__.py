@@ -10,7 +10,7 @@ loads the built library and raises when it is missing.
 """
 from ._lib import (  # noqa: F401
     load, MoEError, MOE_F32, MOE_BF16, MOE_MXFP8_E4M3, MOE_MXFP4_E2M1,
-    moe_abi_version, moe_route, moe_quantize_mx, moe_permute_rows_bound,
+    moe_abi_version, moe_route, moe_route_workspace, moe_quantize_mx, moe_permute_rows_bound,
     moe_permute_workspace, moe_permute, moe_grouped_mlp_workspace,
     moe_grouped_mlp_fwd, moe_grouped_fc1_swiglu, moe_grouped_fc2, moe_combine,
     moe_combine_bwd, moe_unpermute, moe_segments_kstride, moe_quantize_mx_segments,

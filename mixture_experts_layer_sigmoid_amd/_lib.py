@@ -23,7 +23,8 @@ SIGNATURES = {
     "moe_abi_version": (_I, []),
     "moe_status_str": (ctypes.c_char_p, [_I]),
     "moe_last_error": (ctypes.c_char_p, []),
-    "moe_route": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P]),
+    "moe_route": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_workspace": (_SZ, [_I, _I, _I]),
     "moe_quantize_mx": (_I, [_P, _I, _I64, _I, _I, _I, _P, _P, _P]),
     "moe_permute_rows_bound": (_I64, [_I, _I, _I, _I]),
     "moe_permute_workspace": (_SZ, [_I, _I, _I]),
@@ -98,11 +99,15 @@ def moe_abi_version() -> int:
 
 
 def moe_route(x, x_fmt, w_router, bias, logits_in, T, H, E, n_group, topk_group, k,
-              routed_scale, logits_out, topk_idx, topk_w, stream=None):
+              routed_scale, logits_out, topk_idx, topk_w, ws, stream=None):
     _check("moe_route", load().moe_route(
         _ptr(x), x_fmt, _ptr(w_router), _ptr(bias), _ptr(logits_in), T, H, E, n_group,
         topk_group, k, float(routed_scale), _ptr(logits_out), _ptr(topk_idx), _ptr(topk_w),
-        _stream(stream)))
+        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_route_workspace(T, H, E) -> int:
+    return load().moe_route_workspace(T, H, E)
 
 
 def moe_quantize_mx(inp, in_fmt, rows, K, axis, out_fmt, codes, scales, stream=None):

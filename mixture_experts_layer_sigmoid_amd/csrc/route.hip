@@ -10,25 +10,32 @@
 // use the unbiased scores, normalized then scaled; the sigmoid is evaluated
 // in fp64 and rounded once to fp32.
 //
-// Layout of the work: one workgroup of 4 wavefronts handles 16 tokens. The
-// logits tile [16, E] is produced by MFMA (bf16 16x16x32, tokens in M,
-// experts in N, each wave owning every 4th 16-expert block) or by fp32 FMA,
-// and kept in LDS. Selection then runs one wavefront per token with the E
-// scores spread over the 64 lanes (expert e on lane e % 64); every argmax is
-// a 64-lane max-reduction of a 64-bit key (order-preserving score bits in
-// the high word, the complemented index in the low word, which turns "ties
-// to the lower index" into a plain max).
+// Layout of the work, two kernels:
+//  * router GEMM: logits = x . W_r^T over tiles of 64 tokens x 64 experts,
+//    optionally split along H into S chunks so that small token counts still
+//    spread over the chip; partial sums go to a workspace [S, T, E] fp32.
+//    bf16: MFMA 16x16x32 with each wave owning 16 tokens and the tile's 64
+//    experts; fp32: plain FMA.
+//  * selection: one wavefront per token sums the S partials in chunk order
+//    and spreads the E scores over the 64 lanes (expert e on lane e % 64);
+//    every argmax is a 64-lane max-reduction of a 64-bit key
+//    (order-preserving score bits in the high word, the complemented index
+//    in the low word, which turns "ties to the lower index" into a plain
+//    max).
 #include "common.h"
 
+#include <algorithm>
 #include <cmath>
 
 namespace moe {
 namespace {
 
-constexpr int kTokPerBlock = 16;
 constexpr int kThreads = 256;
 constexpr int kMaxE = 512;
 constexpr int kMaxPerLane = kMaxE / 64;
+constexpr int kTile = 64;       // tokens and experts per router GEMM tile
+constexpr int kMinChunk = 128;  // smallest H chunk of the split
+constexpr int kTargetWgs = 512;
 
 __device__ __forceinline__ uint32_t orderable(float f) {
   uint32_t u = __float_as_uint(f);
@@ -53,169 +60,176 @@ __device__ __forceinline__ int key_index(unsigned long long key) {
   return static_cast<int>(~static_cast<uint32_t>(key & 0xFFFFFFFFull));
 }
 
-// Logits of 16 tokens x E experts, bf16 inputs, fp32 MFMA accumulation.
-__device__ void logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-                            int T, int H, int E, int t0, float* lg /* LDS [16][E] */) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nblk = (E + 15) / 16;
-  const int row = lane & 15;
-  const int kq = (lane >> 4) * 8;  // k offset of this lane inside a 32-wide step
-  const int tok = min(t0 + row, T - 1);
-  const uint16_t* xa = x + static_cast<int64_t>(tok) * H + kq;
-  constexpr int kMaxBlkPerWave = kMaxE / 16 / 4;
-  f32x4_t acc[kMaxBlkPerWave];
-  const uint16_t* wb[kMaxBlkPerWave];
-  int myblk = 0;
-#pragma unroll
-  for (int i = 0; i < kMaxBlkPerWave; ++i) {
-    acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    int nb = wave + 4 * i;
-    int ex = min(nb * 16 + row, E - 1);
-    wb[i] = wr + static_cast<int64_t>(ex) * H + kq;
-    if (nb < nblk) myblk = i + 1;
-  }
-  for (int k0 = 0; k0 < H; k0 += 32) {
-    bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(xa + k0);
-#pragma unroll
-    for (int i = 0; i < kMaxBlkPerWave; ++i) {
-      if (i < myblk) {
-        bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(wb[i] + k0);
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
-      }
-    }
-  }
-  // C layout of 16x16 MFMA: lane l, element r -> row 4*(l/16)+r, column l%16
-#pragma unroll
-  for (int i = 0; i < kMaxBlkPerWave; ++i) {
-    if (i < myblk) {
-      int col = (wave + 4 * i) * 16 + (lane & 15);
-      if (col < E) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lg[(4 * (lane >> 4) + r) * E + col] = acc[i][r];
-      }
-    }
-  }
-}
-
-// Logits with fp32 inputs by plain FMA (the small fp32 layer).
-__device__ void logits_f32(const float* __restrict__ x, const float* __restrict__ wr, int T,
-                           int H, int E, int t0, float* lg) {
-  for (int o = threadIdx.x; o < kTokPerBlock * E; o += kThreads) {
-    int r = o / E, e = o % E;
-    int tok = min(t0 + r, T - 1);
-    const float* xp = x + static_cast<int64_t>(tok) * H;
-    const float* wp = wr + static_cast<int64_t>(e) * H;
-    float acc = 0.f;
-    for (int h = 0; h < H; ++h) acc = fmaf(xp[h], wp[h], acc);
-    lg[r * E + e] = acc;
-  }
-}
-
+// Partial logits of one tile over H chunk [k0, k1):
+// part[s, t, e] = sum_{h in chunk} x[t, h] * w[e, h].
 template <int XFMT>
-__global__ __launch_bounds__(kThreads) void route_kernel(
-    const void* __restrict__ x, const void* __restrict__ wr, const float* __restrict__ bias,
-    const float* __restrict__ logits_in, int T, int H, int E, int n_group, int topk_group,
-    int k, float routed_scale, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w) {
-  __shared__ float lg[kTokPerBlock * kMaxE];
+__global__ __launch_bounds__(kThreads) void router_gemm_kernel(const void* __restrict__ x,
+                                                               const void* __restrict__ wr, int T,
+                                                               int H, int E, int chunk, int S,
+                                                               float* __restrict__ part) {
+  const int ne = (E + kTile - 1) / kTile;
+  int b = blockIdx.x;
+  const int s = b % S;
+  b /= S;
+  const int t0 = (b / ne) * kTile, e0 = (b % ne) * kTile;
+  const int k0 = s * chunk, k1 = min(H, k0 + chunk);
+  float* out = part + static_cast<int64_t>(s) * T * E;
+  if constexpr (XFMT == MOE_BF16) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kq = (lane >> 4) * 8;  // k offset of this lane inside a 32-wide step
+    const int tok = min(t0 + 16 * wave + (lane & 15), T - 1);
+    const uint16_t* xa = static_cast<const uint16_t*>(x) + static_cast<int64_t>(tok) * H + kq;
+    const uint16_t* wb[4];
+    f32x4_t acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ex = min(e0 + 16 * j + (lane & 15), E - 1);
+      wb[j] = static_cast<const uint16_t*>(wr) + static_cast<int64_t>(ex) * H + kq;
+      acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll 4
+    for (int k = k0; k < k1; k += 32) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(xa + k);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t w = *reinterpret_cast<const bf16x8_t*>(wb[j] + k);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, acc[j], 0, 0, 0);
+      }
+    }
+    // C layout of 16x16 MFMA: lane l, element r -> row 4*(l/16)+r, column l%16
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + 16 * j + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 16 * wave + 4 * (lane >> 4) + r;
+        if (t < T && e < E) out[static_cast<int64_t>(t) * E + e] = acc[j][r];
+      }
+    }
+  } else {
+    const float* xf = static_cast<const float*>(x);
+    const float* wf = static_cast<const float*>(wr);
+    for (int o = threadIdx.x; o < kTile * kTile; o += kThreads) {
+      const int t = t0 + o / kTile, e = e0 + o % kTile;
+      if (t >= T || e >= E) continue;
+      const float* xp = xf + static_cast<int64_t>(t) * H;
+      const float* wp = wf + static_cast<int64_t>(e) * H;
+      float acc = 0.f;
+      for (int h = k0; h < k1; ++h) acc = fmaf(xp[h], wp[h], acc);
+      out[static_cast<int64_t>(t) * E + e] = acc;
+    }
+  }
+}
+
+// One wavefront per token: logits (sum of S partials, or logits_in), then
+// sigmoid, bias, group limit, top-k and the combine weights.
+__global__ __launch_bounds__(kThreads) void select_kernel(
+    const float* __restrict__ part, int S, const float* __restrict__ bias, int T, int E,
+    int n_group, int topk_group, int k, float routed_scale, float* __restrict__ logits_out,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   __shared__ float s_sc[4][kMaxE];   // per wave: sigmoid scores of its token
   __shared__ float s_sel[4][kMaxE];  // per wave: biased scores of its token
-  const int t0 = blockIdx.x * kTokPerBlock;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-
-  if (logits_in == nullptr) {
-    if (XFMT == MOE_BF16)
-      logits_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr), T, H, E, t0, lg);
-    else
-      logits_f32(static_cast<const float*>(x), static_cast<const float*>(wr), T, H, E, t0, lg);
-    __syncthreads();
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;  // no block-level barrier below
+  // scores of this token, expert e on lane e % 64
+  float val[kMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + 64 * i;
+    val[i] = -INFINITY;
+    if (e < E) {
+      float l = 0.f;
+      for (int s = 0; s < S; ++s) l += part[(static_cast<int64_t>(s) * T + t) * E + e];
+      if (logits_out) logits_out[static_cast<int64_t>(t) * E + e] = l;
+      const float sc = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(l))));
+      const float sel = sc + bias[e];
+      s_sc[wave][e] = sc;
+      s_sel[wave][e] = sel;
+      val[i] = sel;
+    }
   }
-
-  const int G = E / n_group;
-  for (int r = wave; r < kTokPerBlock; r += 4) {
-    const int t = t0 + r;
-    if (t >= T) break;
-    // scores of this token, expert e on lane e % 64
-    float val[kMaxPerLane];
+  __builtin_amdgcn_wave_barrier();
+  if (n_group > 1) {
+    const int G = E / n_group;
+    // group q on lane q: the two largest biased scores of the group
+    float gscore = -INFINITY;
+    if (lane < n_group) {
+      float m1 = -INFINITY, m2 = -INFINITY;
+      for (int e = lane * G; e < (lane + 1) * G; ++e) {
+        const float v = s_sel[wave][e];
+        if (v > m1) {
+          m2 = m1;
+          m1 = v;
+        } else if (v > m2) {
+          m2 = v;
+        }
+      }
+      gscore = m1 + m2;
+    }
+    unsigned long long kept = 0;  // bit q set: group q kept
+    for (int i = 0; i < topk_group; ++i) {
+      const unsigned long long key = lane < n_group ? make_key(gscore, lane) : 0ull;
+      const int q = key_index(wave_max_u64(key));
+      kept |= 1ull << q;
+      if (lane == q) gscore = -INFINITY;
+    }
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
-      int e = lane + 64 * i;
-      val[i] = -INFINITY;
-      if (e < E) {
-        float l = logits_in ? logits_in[static_cast<int64_t>(t) * E + e] : lg[r * E + e];
-        if (logits_out) logits_out[static_cast<int64_t>(t) * E + e] = l;
-        float s = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(l))));
-        float sel = s + bias[e];
-        s_sc[wave][e] = s;
-        s_sel[wave][e] = sel;
-        val[i] = sel;
-      }
+      const int e = lane + 64 * i;
+      if (e < E && !((kept >> (e / G)) & 1ull)) val[i] = -INFINITY;
     }
-    if (n_group > 1) {
-      __builtin_amdgcn_wave_barrier();
-      // group q on lane q: the two largest biased scores of the group
-      float gscore = -INFINITY;
-      if (lane < n_group) {
-        float m1 = -INFINITY, m2 = -INFINITY;
-        for (int e = lane * G; e < (lane + 1) * G; ++e) {
-          float v = s_sel[wave][e];
-          if (v > m1) {
-            m2 = m1;
-            m1 = v;
-          } else if (v > m2) {
-            m2 = v;
-          }
-        }
-        gscore = m1 + m2;
-      }
-      unsigned long long kept = 0;  // bit q set: group q kept
-      for (int i = 0; i < topk_group; ++i) {
-        unsigned long long key = lane < n_group ? make_key(gscore, lane) : 0ull;
-        int q = key_index(wave_max_u64(key));
-        kept |= 1ull << q;
-        if (lane == q) gscore = -INFINITY;
-      }
-#pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
-        int e = lane + 64 * i;
-        if (e < E && !((kept >> (e / G)) & 1ull)) val[i] = -INFINITY;
-      }
-    }
-    // top-k by repeated 64-lane argmax
-    int my_idx = 0;
-    for (int j = 0; j < k; ++j) {
-      unsigned long long best = 0;
-#pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
-        int e = lane + 64 * i;
-        if (e < E) {
-          unsigned long long key = make_key(val[i], e);
-          best = key > best ? key : best;
-        }
-      }
-      int e = key_index(wave_max_u64(best));
-      if (lane == j) my_idx = e;
-      if (lane == (e & 63)) {
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-          if (i == (e >> 6)) val[i] = -INFINITY;
-      }
-    }
-    // normalize the unbiased scores of the chosen experts, then scale
-    float S = 0.f;
-    for (int j = 0; j < k; ++j) {
-      int e = __shfl(my_idx, j, 64);
-      S += s_sc[wave][e];
-    }
-    if (lane < k) {
-      float w = s_sc[wave][my_idx] / S;
-      topk_idx[static_cast<int64_t>(t) * k + lane] = my_idx;
-      topk_w[static_cast<int64_t>(t) * k + lane] = w * routed_scale;
-    }
-    __builtin_amdgcn_wave_barrier();
   }
+  // top-k by repeated 64-lane argmax
+  int my_idx = 0;
+  for (int j = 0; j < k; ++j) {
+    unsigned long long best = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) {
+        const unsigned long long key = make_key(val[i], e);
+        best = key > best ? key : best;
+      }
+    }
+    const int e = key_index(wave_max_u64(best));
+    if (lane == j) my_idx = e;
+    if (lane == (e & 63)) {
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i)
+        if (i == (e >> 6)) val[i] = -INFINITY;
+    }
+  }
+  // normalize the unbiased scores of the chosen experts, then scale
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int e = __shfl(my_idx, j, 64);
+    sum += s_sc[wave][e];
+  }
+  if (lane < k) {
+    const float w = s_sc[wave][my_idx] / sum;
+    topk_idx[static_cast<int64_t>(t) * k + lane] = my_idx;
+    topk_w[static_cast<int64_t>(t) * k + lane] = w * routed_scale;
+  }
+}
+
+// H split of the router GEMM: S chunks of `chunk` columns (a multiple of 32).
+struct Split {
+  int S, chunk;
+};
+Split router_split(int T, int H, int E) {
+  const int64_t tiles = static_cast<int64_t>((T + kTile - 1) / kTile) * ((E + kTile - 1) / kTile);
+  int S = 1;
+  if (tiles < kTargetWgs) {
+    const int64_t want = (kTargetWgs + tiles - 1) / tiles;
+    const int most = std::max(1, H / kMinChunk);
+    S = static_cast<int>(std::min<int64_t>(want, most));
+  }
+  int chunk = (H + S - 1) / S;
+  chunk = (chunk + 31) / 32 * 32;
+  S = (H + chunk - 1) / chunk;
+  return {S, chunk};
 }
 
 }  // namespace
@@ -223,10 +237,17 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 
 using namespace moe;
 
+extern "C" size_t moe_route_workspace(int T, int H, int E) {
+  if (T <= 0 || H <= 0 || E <= 0) return 0;
+  const Split sp = router_split(T, H, E);
+  return static_cast<size_t>(sp.S) * T * E * sizeof(float);
+}
+
 extern "C" int moe_route(const void* x, int x_fmt, const void* w_router, const float* bias,
                          const float* logits_in, int T, int H, int E, int n_group,
                          int topk_group, int k, float routed_scale, float* logits_out,
-                         int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+                         int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
   clear_error();
   MOE_REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "moe_route: T < 0");
   MOE_REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "moe_route: E must be in [1, 512]");
@@ -253,13 +274,26 @@ extern "C" int moe_route(const void* x, int x_fmt, const void* w_router, const f
     }
   }
   if (T == 0) return MOE_OK;
-  dim3 grid((T + kTokPerBlock - 1) / kTokPerBlock), block(kThreads);
-  if (logits_in || x_fmt == MOE_F32)
-    hipLaunchKernelGGL(route_kernel<MOE_F32>, grid, block, 0, stream, x, w_router, bias, logits_in,
-                       T, H, E, n_group, topk_group, k, routed_scale, logits_out, topk_idx, topk_w);
+  const dim3 sel_grid((T + 3) / 4), block(kThreads);
+  if (logits_in) {
+    hipLaunchKernelGGL(select_kernel, sel_grid, block, 0, stream, logits_in, 1, bias, T, E,
+                       n_group, topk_group, k, routed_scale, logits_out, topk_idx, topk_w);
+    return check_launch("moe_route");
+  }
+  const Split sp = router_split(T, H, E);
+  const size_t need = static_cast<size_t>(sp.S) * T * E * sizeof(float);
+  MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE,
+              "moe_route: workspace smaller than moe_route_workspace(T, H, E)");
+  const int tiles = ((T + kTile - 1) / kTile) * ((E + kTile - 1) / kTile);
+  const dim3 grid(static_cast<unsigned>(tiles * sp.S));
+  float* part = static_cast<float*>(ws);
+  if (x_fmt == MOE_BF16)
+    hipLaunchKernelGGL(router_gemm_kernel<MOE_BF16>, grid, block, 0, stream, x, w_router, T, H, E,
+                       sp.chunk, sp.S, part);
   else
-    hipLaunchKernelGGL(route_kernel<MOE_BF16>, grid, block, 0, stream, x, w_router, bias,
-                       logits_in, T, H, E, n_group, topk_group, k, routed_scale, logits_out,
-                       topk_idx, topk_w);
+    hipLaunchKernelGGL(router_gemm_kernel<MOE_F32>, grid, block, 0, stream, x, w_router, T, H, E,
+                       sp.chunk, sp.S, part);
+  hipLaunchKernelGGL(select_kernel, sel_grid, block, 0, stream, part, sp.S, bias, T, E, n_group,
+                     topk_group, k, routed_scale, logits_out, topk_idx, topk_w);
   return check_launch("moe_route");
 }

@@ -113,6 +113,8 @@ class MoEForward:
         self.act_fmt = FMT["fp32"] if fmt == "fp32" else FMT["bf16"]
         i32 = dict(dtype=torch.int32, device=dev)
         self.logits = torch.empty((T, E), dtype=torch.float32, device=dev) if keep_logits else None
+        self.route_ws = torch.empty((max(1, L.moe_route_workspace(T, H, E)),), dtype=torch.uint8,
+                                    device=dev)
         self.topk_idx = torch.empty((T, k), **i32)
         self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
         self.counts = torch.empty((E,), **i32)
@@ -149,7 +151,7 @@ class MoEForward:
     def route(self, x, w_router, bias, logits_in=None, stream=None):
         L.moe_route(x, self.act_fmt, w_router, bias, logits_in, self.T, self.H, self.E, self.n_group,
                     self.topk_group, self.k, self.routed_scale, self.logits, self.topk_idx,
-                    self.topk_w, stream)
+                    self.topk_w, None if logits_in is not None else self.route_ws, stream)
 
     def quantize_x(self, x, stream=None):
         if is_mx(self.fmt):

@@ -50,7 +50,8 @@ def _route(lib, **kw):
              lout=None, idx=A, w_out=A)
     a.update(kw)
     return lib.moe_route(a["x"], a["x_fmt"], a["w"], a["bias"], a["lin"], a["T"], a["H"], a["E"],
-                         a["ng"], a["tg"], a["k"], a["scale"], a["lout"], a["idx"], a["w_out"], None)
+                         a["ng"], a["tg"], a["k"], a["scale"], a["lout"], a["idx"], a["w_out"],
+                         a.get("ws"), a.get("wsb", 0), None)
 
 
 def test_route_validation(lib):
@@ -68,6 +69,11 @@ def test_route_validation(lib):
     assert b"aligned" in lib.moe_last_error()
     assert _route(lib, T=0) == OK                       # nothing to do, nothing launched
     assert _route(lib, T=0, x=None, w=None, lin=A) == OK
+    assert _route(lib) == WS                            # the GEMM needs its workspace
+    need = lib.moe_route_workspace(4, 64, 16)
+    assert need >= 4 * 16 * 4
+    assert _route(lib, ws=A, wsb=need - 1) == WS
+    assert lib.moe_route_workspace(0, 64, 16) == 0
 
 
 def test_quantize_validation(lib):

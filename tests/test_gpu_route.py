@@ -4,7 +4,9 @@
   indices must match bit for bit and weights within 2 fp32 ulps (both
   evaluate the sigmoid in fp64 and round once).
 * GEMM path: logits match the oracle's fp64 logits within fp32 accumulation
-  error; expert lists match except certified near ties.
+  error; expert lists match except certified near ties. Covered at small
+  sizes and at the full hidden size with few tokens (the router GEMM split
+  along H into many chunks) and with 4096 tokens.
 """
 import numpy as np
 import pytest
@@ -21,7 +23,10 @@ def _route_dev(gpu_lib, T, H, E, ng, tg, k, scale, bias, logits=None, x=None, w=
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
     wt = torch.empty((T, k), dtype=torch.float32, device="cuda")
     lo = torch.empty((T, E), dtype=torch.float32, device="cuda")
-    gpu_lib.moe_route(x, fmt, w, bias, logits, T, H, E, ng, tg, k, scale, lo, idx, wt)
+    ws = None
+    if logits is None:
+        ws = torch.empty(max(1, gpu_lib.moe_route_workspace(T, H, E)), dtype=torch.uint8, device="cuda")
+    gpu_lib.moe_route(x, fmt, w, bias, logits, T, H, E, ng, tg, k, scale, lo, idx, wt, ws)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), wt.cpu().numpy(), lo.cpu().numpy()
 
@@ -79,3 +84,21 @@ def test_gemm_path_full_size(gpu_lib, name):
     assert unc == 0 and nbad <= max(2, cfg.T // 1000)
     same = (idx == oidx).all(axis=1)
     assert rel_l2(w[same], ow[same]) < 1e-5
+
+
+@pytest.mark.parametrize("name", ["dsv3_mxfp8_decode_t64", "dsv3_bf16_t4096", "dsv4_skew_mxfp8_t8192"])
+def test_gemm_path_full_hidden(gpu_lib, name):
+    cfg = configs.get(name)
+    log(f"route with router GEMM at full hidden size, {name} (H split {gpu_lib.moe_route_workspace(cfg.T, cfg.H, cfg.E) // (4 * cfg.T * cfg.E)} ways)")
+    x = gen.host_x(cfg)
+    wr = gen.host_router(cfg)
+    b = gen.host_bias(cfg)
+    idx, w, lo = _route_dev(gpu_lib, cfg.T, cfg.H, cfg.E, cfg.n_group, cfg.topk_group, cfg.k,
+                            cfg.routed_scale, dev(b), x=dev(x, "bf16"), w=dev(wr, "bf16"))
+    olog = rt.router_logits(x, wr)
+    assert rel_l2(lo, olog) < 1e-6
+    oidx, ow, _, osel = rt.route(olog, b, cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
+    nbad, unc = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group)
+    assert unc == 0 and nbad <= max(1, cfg.T // 1000)
+    same = (idx == oidx).all(axis=1)
+    assert ulp_diff_f32(w[same], ow[same]).max() <= 64     # fp32 logits vs fp64 logits
