@@ -196,6 +196,29 @@ size_t moe_grouped_mlp_workspace(int E, int H, int F, int64_t rows, int a_fmt,
                                  int w_fmt);
 
 /*
+ * moe_pack_weights — one-time preparation of expert weights for the grouped
+ * GEMMs (done when the weights change, not per step): reorders each
+ * expert's [N, K] matrix so that a wavefront streams exactly the bytes its
+ * 32x32 matrix instructions consume, contiguously. (TE DeepSeekV3Layer
+ * page, Description and Performance section: the experts' GroupedLinear
+ * weights of the fused grouped MLP; MX scales one per 32 values along K.)
+ * Layout: for expert e, 32-row column block cb, 128-byte K stage s, piece
+ * q < 4 and lane l < 64, 16 bytes = bytes [128 s + 32 q + 16 (l / 32), +16)
+ * of row R(cb, l): R = 32 cb + l % 32, or with half = F > 0 (fc1, N = 2F)
+ * gate row 32 (cb / 2) + l % 32 for even cb and up row F + 32 (cb / 2) +
+ * l % 32 for odd cb. MX scales: for (e, cb, s, l), kSub bytes (2 for
+ * E4M3, 4 for E2M1): byte j is the scale of stage-local 32-block
+ * 2 j + l / 32 of row R(cb, l).
+ * w        [E, N, K] in fmt (BF16 values, or MX codes with w_scales
+ *          [E, N, K/32]); out (and out_scales) the same number of bytes.
+ * Limits: N % 64 == 0; K a multiple of 64 (BF16), 128 (E4M3), 256 (E2M1);
+ * half == 0 or N == 2 * half with half % 32 == 0.
+ */
+int moe_pack_weights(const void* w, const uint8_t* w_scales, int fmt, int E,
+                     int N, int K, int half, void* out, uint8_t* out_scales,
+                     hipStream_t stream);
+
+/*
  * moe_grouped_mlp_fwd — per expert e, on rows [offsets[e], offsets[e+1]):
  *   A = X_e . W1_e^T          [n_e, 2F], fp32 accumulate
  *   h = silu(A[:, :F]) * A[:, F:]   (W1 rows [0, F) gate, [F, 2F) up)
@@ -211,8 +234,10 @@ size_t moe_grouped_mlp_workspace(int E, int H, int F, int64_t rows, int a_fmt,
  *          [T, H] gathered through src_row (row r reads a[src_row[r]]; a
  *          row with src_row -1 produces zero h).
  * a_scales MX scales of a ([rows or T, H/32]), NULL for F32/BF16.
- * w1       [E, 2F, H] and w2 [E, H, F] in w_fmt, with MX scales
- *          w1_scales [E, 2F, H/32], w2_scales [E, H, F/32] (NULL otherwise).
+ * w1       [E, 2F, H] and w2 [E, H, F] in w_fmt: for BF16 and MX formats
+ *          packed by moe_pack_weights (w1 with half = F, w2 with half = 0),
+ *          with their packed MX scales w1_scales / w2_scales (NULL for BF16);
+ *          for F32 plain row-major, no scales.
  * Supported (a_fmt, w_fmt, y_fmt): (F32, F32, F32), (BF16, BF16, BF16),
  *          (MXFP8, MXFP8, BF16), (MXFP4, MXFP4, BF16).
  * offsets  [E+1] int32 device array (as moe_permute writes it);
@@ -341,7 +366,8 @@ int moe_quantize_mx_segments(const void* in, int in_fmt, int mode,
 
 /*
  * moe_grouped_fc2_dgrad_dswiglu — per expert segment, dH = dY . W2 with W2
- * given transposed w2t [E, F, H] (contraction over H contiguous), then the
+ * given transposed w2t [E, F, H] (contraction over H contiguous, packed by
+ * moe_pack_weights with half = 0, scales packed alongside), then the
  * SwiGLU backward with the saved fc1 output A = (g | u):
  *   dgate = dH * u * sig(g) * (1 + g * (1 - sig(g))),  dup = dH * silu(g)
  * dy      [rows, H] in fmt (MX: codes + dy_scales [rows, H/32]).
@@ -361,7 +387,8 @@ int moe_grouped_fc2_dgrad_dswiglu(const void* dy, const uint8_t* dy_scales,
 
 /*
  * moe_grouped_fc1_dgrad — per expert segment dX_rows = dA . W1 with W1 given
- * transposed w1t [E, H, 2F] (contraction over 2F contiguous).
+ * transposed w1t [E, H, 2F] (contraction over 2F contiguous, packed by
+ * moe_pack_weights with half = 0).
  * da [rows, 2F] in fmt (MX codes + da_scales); dx_perm [rows, H] bf16 out.
  */
 int moe_grouped_fc1_dgrad(const void* da, const uint8_t* da_scales, int fmt,

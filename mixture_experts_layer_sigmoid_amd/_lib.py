@@ -35,6 +35,7 @@ SIGNATURES = {
     "moe_grouped_fc1_swiglu": (_I, [_P, _P, _I, _P, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _P, _P, _P]),
     "moe_grouped_fc2": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _I, _P]),
     "moe_combine": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _P, _I, _P]),
+    "moe_pack_weights": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moe_combine_bwd": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _I64, _P, _I, _P, _P, _P]),
     "moe_unpermute": (_I, [_P, _I, _P, _I, _I, _I, _P, _I, _P]),
     "moe_segments_kstride": (_I64, [_I64, _I]),
@@ -205,3 +206,8 @@ def moe_grouped_wgrad(at, at_scales, bt, bt_scales, fmt, kofs, E, M, N, kstride,
     _check("moe_grouped_wgrad", load().moe_grouped_wgrad(
         _ptr(at), _ptr(at_scales), _ptr(bt), _ptr(bt_scales), fmt, _ptr(kofs), E, M, N, kstride,
         _ptr(dw), _stream(stream)))
+
+
+def moe_pack_weights(w, w_scales, fmt, E, N, K, half, out, out_scales, stream=None):
+    _check("moe_pack_weights", load().moe_pack_weights(
+        _ptr(w), _ptr(w_scales), fmt, E, N, K, half, _ptr(out), _ptr(out_scales), _stream(stream)))

@@ -1,0 +1,724 @@
+// Grouped expert GEMMs over expert-major row segments with weights streamed
+// straight into registers: routed fc1 + SwiGLU, fc2, and the data-gradient
+// GEMMs of the backward (fc2 dgrad fused with the SwiGLU backward, fc1
+// dgrad).
+//
+// Page "[PyTorch] DeepSeekV3Layer: full MoE transformer layer (MLA +
+// DeepSeek MoE)": Description (experts as GroupedLinear -> ScaledSwiGLU ->
+// GroupedLinear, fused into one grouped MLP) and Performance section ("Where
+// the time goes": fc1+SwiGLU fwd, fc2 fwd and dGLU bwd of the fused grouped
+// MLP, MXFP8). Page "Mistral Large 3 NVFP4 TRTLLM MoE support", Highlights:
+// fc1's weight holds the w1 (gate) and w3 (up) halves; here rows [0, F) gate,
+// [F, 2F) up.
+//
+// Design (gfx950). At the shapes of these layers the grouped GEMMs stream
+// far more weight bytes than activation bytes (a few hundred rows per expert
+// against 2F x H weights), so the kernel is built around reading every
+// weight byte from HBM once, contiguously, with as much in flight as
+// possible:
+//   * Weights are packed once (moe_pack_weights) into the order the 32x32
+//     MFMA consumes them: for every 32-row column block and every 128 bytes
+//     of K ("stage"), 4 KB holding, piece by piece, exactly the 16 bytes
+//     each of the 64 lanes feeds its matrix instruction. A wavefront streams
+//     its column blocks with plain 16-byte-per-lane loads of contiguous
+//     1 KB pieces into a ring of P stages of registers; no LDS, no barrier
+//     and no sharing is involved on the weight side. MX block scales are
+//     packed the same way (the bytes of one lane's scales for one stage are
+//     adjacent).
+//   * A tile is (expert e, column tile of 256 weight rows, up to 256 rows of
+//     the expert's segment): an expert with at most 256 rows reads its
+//     weights exactly once; longer segments are cut into balanced row tiles
+//     that run side by side on one XCD, so the second read hits L2. Four
+//     wavefronts, one per SIMD; wavefront w owns two column blocks (64
+//     weight rows) and every row block of the tile: 16 accumulators of
+//     32x32 fp32 in the accumulation registers.
+//   * Activation rows are shared by the four wavefronts: they go through a
+//     ring of P LDS stages with direct global->LDS 16-byte loads (row
+//     gather through src_row for fc1), XOR-swizzled so the MFMA operand
+//     reads are free of bank conflicts; the MX scales of the rows ride in
+//     small per-stage arrays.
+//   * The tile list (experts x column tiles x row tiles) is built in LDS
+//     from `offsets` by every workgroup, cut into 8 contiguous chunks, one
+//     per XCD; consecutive tiles are the row tiles of one weight tile, then
+//     the column tiles of one expert, so concurrent workgroups of an XCD
+//     share activation rows and weight tiles in its L2.
+//   * Epilogues go through LDS in passes of 128 rows to row-major 16-byte
+//     stores: SwiGLU (bf16 h or MX-encoded 32-column blocks, optional fp32
+//     save of the fc1 output), plain bf16 y, or the SwiGLU backward (dA in
+//     MX or bf16, optional fp32 copy).
+#include "common.h"
+#include "gemm_util.h"
+#include "mx_codec.h"
+
+#include <algorithm>
+#include <string>
+#include <type_traits>
+
+namespace moe {
+namespace {
+
+constexpr int kMaxGroups = 1024;
+constexpr int kStageBytes = 128;        // bytes of K per row per stage
+constexpr int kChunk = 4096;            // packed bytes per (column block, stage)
+constexpr int kTileCols = 256;          // weight rows per tile (8 column blocks)
+constexpr int kPassRows = 128;          // epilogue rows per LDS pass
+constexpr int kCs = kTileCols + 4;      // padded fp32 row stride of the epilogue tile
+
+enum { XOP_BF16 = 0, XOP_FP8 = 1, XOP_FP4 = 2 };
+enum { XEPI_SWIGLU = 0, XEPI_PLAIN = 1, XEPI_DSWIGLU = 2 };
+
+// k-steps of one stage and MX scale bytes per row per stage
+template <int OP>
+struct XOp {
+  static constexpr int kSub = OP == XOP_FP8 ? 2 : 4;
+  static constexpr int kScaleBytes = OP == XOP_BF16 ? 0 : (OP == XOP_FP8 ? 4 : 8);
+  static constexpr int kPackedScaleBytes = OP == XOP_BF16 ? 0 : 64 * kSub;  // per (cb, stage)
+};
+
+struct XArgs {
+  const uint8_t* a;          // activation rows [rows, K] (or token rows with gather)
+  int64_t a_row_bytes;
+  const uint8_t* a_sc;       // their MX scales [rows, K/32]
+  int64_t a_sc_row_bytes;
+  const int32_t* gather;     // optional row -> token row (-1: padding row)
+  const uint8_t* b;          // packed weights of expert 0
+  int64_t b_exp_bytes;
+  const uint8_t* b_sc;       // packed MX scales of expert 0
+  int64_t b_sc_exp_bytes;
+  int ncb;                   // 32-row column blocks per expert (N / 32)
+  int n_tiles;               // column tiles per expert (ceil(N / 256))
+  int k_stages;              // K bytes / 128
+  const int32_t* offsets;    // [E+1]
+  int E;
+  int64_t rows;
+  int half;                  // SwiGLU: F; dSwiGLU: F (offset of the up half)
+  uint8_t* out;
+  int64_t out_row_bytes;
+  uint8_t* out_sc;
+  int64_t out_sc_row_bytes;
+  float* act_save;           // fc1: optional fp32 [rows, 2F]
+  const float* a_saved;      // dSwiGLU: saved fc1 output [rows, 2F] fp32
+  float* da_f32;             // dSwiGLU: optional fp32 copy of dA [rows, 2F]
+};
+
+template <int MAXNV, int P, int OP>
+struct XSmem {
+  static constexpr int kRows = 32 * MAXNV;
+  static constexpr int kA = kRows * kStageBytes;
+  static constexpr int kASc = kRows * XOp<OP>::kScaleBytes;
+  static constexpr int kStage = kA + kASc;
+  static constexpr int kRing = P * kStage;
+  static constexpr int kEpi = (kRows < kPassRows ? kRows : kPassRows) * kCs * 4;
+  static constexpr int kBody = kRing > kEpi ? kRing : kEpi;
+  static constexpr int kSched = (kMaxGroups + 2) * 4 + kRows * 4;
+  static constexpr int kTotal = kBody + kSched;
+};
+
+__device__ __forceinline__ float sigmoidf_(float g) { return 1.f / (1.f + expf(-g)); }
+
+// f(integral_constant<0>) ... f(integral_constant<N-1>), unrolled at compile time
+template <int I, int N, typename Fn>
+__device__ __forceinline__ void static_for_impl(Fn&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) { static_for_impl<0, N>(f); }
+
+// MAXNV: row blocks of 32 per tile (tile rows = 32 * MAXNV)
+// P:     stages in flight (LDS ring for the activations, register ring for
+//        the weights)
+template <int MAXNV, int P, int OP, int EPI, int OUTF>
+__global__ __launch_bounds__(256) void expert_gemm_kernel(XArgs p) {
+  using S = XSmem<MAXNV, P, OP>;
+  using O = XOp<OP>;
+  constexpr int kRows = S::kRows;
+  constexpr int kSB = O::kScaleBytes;
+  constexpr int kSub = O::kSub;
+  constexpr int kAIns = kRows / 8 / 4;              // 1 KB A loads per wave per stage (max)
+  constexpr int kDpr = kSB > 0 ? kSB / 4 : 1;       // scale dwords per row per stage
+  constexpr int kScRows = 64 / kDpr;                // rows per 4-byte-per-lane scale load
+  constexpr int kAScIns = kSB > 0 ? kRows / kScRows : 0;
+  constexpr int kAScPerWave = kAScIns / 4;
+  static_assert(kAIns >= 1, "tile needs at least 32 rows");
+  static_assert(kSB == 0 || kAScIns % 4 == 0, "scale loads must split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S::kTotal];
+  int32_t* s_mt = reinterpret_cast<int32_t*>(smem + S::kBody);   // [E+1] row-tile prefix
+  int32_t* s_src = s_mt + (kMaxGroups + 1);                       // [kRows] source rows
+  int32_t* s_tot = s_src + kRows;
+  int32_t* part = reinterpret_cast<int32_t*>(smem);  // scan scratch (before any load)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int E = p.E;
+
+  // ---- tile list: row tiles per expert, inclusive prefix in s_mt[1..E] ----
+  {
+    const int per = (E + 255) / 256;
+    const int lo = tid * per, hi = min(E, lo + per);
+    int s = 0;
+    for (int e = lo; e < hi; ++e) {
+      int n_e = min(p.offsets[e + 1], (int)p.rows) - p.offsets[e];
+      n_e = n_e < 0 ? 0 : n_e;
+      const int mt = (n_e + kRows - 1) / kRows;
+      s_mt[e + 1] = mt;
+      s += mt;
+    }
+    part[tid] = s;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const int v = tid >= d ? part[tid - d] : 0;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
+    }
+    int run = tid > 0 ? part[tid - 1] : 0;
+    for (int e = lo; e < hi; ++e) {
+      run += s_mt[e + 1];
+      s_mt[e + 1] = run;
+    }
+    if (tid == 0) {
+      s_mt[0] = 0;
+      s_tot[0] = part[255];
+    }
+    __syncthreads();
+  }
+  const int64_t total_tiles = static_cast<int64_t>(s_tot[0]) * p.n_tiles;
+  const XcdSlot xs = xcd_slot();
+  const int64_t t_first = total_tiles * xs.xcd / kNumXcd + xs.slot;
+  const int64_t t_end = total_tiles * (xs.xcd + 1) / kNumXcd;
+
+  for (int64_t t = t_first; t < t_end; t += xs.nslots) {
+    // ---- decode: expert, then column tile (slow) and row tile (fast) ----
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (static_cast<int64_t>(s_mt[mid]) * p.n_tiles <= t) lo = mid;
+      else hi = mid;
+    }
+    const int e = lo;
+    const int mtiles = s_mt[e + 1] - s_mt[e];
+    const int64_t local = t - static_cast<int64_t>(s_mt[e]) * p.n_tiles;
+    const int nt = static_cast<int>(local / mtiles);
+    const int mt = static_cast<int>(local % mtiles);
+    const int seg_lo = p.offsets[e];
+    const int n_e = min(p.offsets[e + 1], (int)p.rows) - seg_lo;
+    int m_per = (n_e + mtiles - 1) / mtiles;
+    m_per = (m_per + 31) & ~31;
+    const int row0 = seg_lo + mt * m_per;
+    const int nrows = min(m_per, n_e - mt * m_per);
+    const int nrb = (nrows + 31) >> 5;
+    const int cb0 = nt * 8 + 2 * wave;           // this wave's first column block
+    const bool active = cb0 < p.ncb;             // uniform per wave
+
+    // ---- per-lane sources (rows past the tile's end clamp to its last row) ----
+    // source row (token row with gather) of A load i; byte offsets stay
+    // below 2^31 for every layer shape (rows * row bytes)
+    uint32_t a_off[kAIns];
+#pragma unroll
+    for (int i = 0; i < kAIns; ++i) {
+      const int r = 8 * (wave + 4 * i) + (lane >> 3);
+      int src = row0 + min(r, nrows - 1);
+      if (p.gather) {
+        src = p.gather[src];
+        if (src < 0) src = 0;  // padding row: loads any valid row, its output is zeroed
+      }
+      a_off[i] = static_cast<uint32_t>(src) * static_cast<uint32_t>(p.a_row_bytes) +
+                 (((lane & 7) ^ swz_key<128>(r)) << 4);
+    }
+    if (p.gather && EPI == XEPI_SWIGLU)
+      for (int r = tid; r < kRows; r += 256) s_src[r] = r < nrows ? p.gather[row0 + r] : 0;
+    const uint8_t* asc_src[kAScPerWave > 0 ? kAScPerWave : 1];
+    if constexpr (kSB > 0) {
+#pragma unroll
+      for (int q = 0; q < kAScPerWave; ++q) {
+        const int j = wave + 4 * q;  // scale load j covers rows [j * kScRows, +kScRows)
+        const int r = min(j * kScRows + lane / kDpr, nrows - 1);
+        int src = row0 + r;
+        if (p.gather) {
+          src = p.gather[src];
+          if (src < 0) src = 0;
+        }
+        asc_src[q] = p.a_sc + static_cast<int64_t>(src) * p.a_sc_row_bytes + (lane % kDpr) * 4;
+      }
+    }
+    const int cbw = active ? cb0 : 0;
+    const uint8_t* b_src = p.b + static_cast<int64_t>(e) * p.b_exp_bytes +
+                           static_cast<int64_t>(cbw) * p.k_stages * kChunk + lane * 16;
+    const int64_t b_blk = static_cast<int64_t>(p.k_stages) * kChunk;   // next column block
+    const uint8_t* bsc_src = nullptr;
+    int64_t bsc_blk = 0;
+    if constexpr (kSB > 0) {
+      bsc_src = p.b_sc + static_cast<int64_t>(e) * p.b_sc_exp_bytes +
+                static_cast<int64_t>(cbw) * p.k_stages * O::kPackedScaleBytes + lane * kSub;
+      bsc_blk = static_cast<int64_t>(p.k_stages) * O::kPackedScaleBytes;
+    }
+
+    const int KT = p.k_stages;
+
+    // the weight ring: 4 pieces x 2 column blocks per stage (+ 2 scale words)
+    u32x4_t bq[P][2][4];
+    uint32_t bs[P][2];
+
+    // One stage of loads: exactly NV activation loads, kAScPerWave scale
+    // loads and 8 (+2) weight loads per wave, whatever the row count and
+    // whether the wave has columns (rows past the tile's end re-read its
+    // last row, an idle wave re-reads column block 0), so the vector-memory
+    // count of a stage is a compile-time constant for both the explicit
+    // waits and the compiler's own.
+    auto issue = [&](int kt, auto slot_c, auto nv_c) {
+      constexpr int SL = decltype(slot_c)::value;
+      constexpr int NV = decltype(nv_c)::value;
+      uint8_t* st = smem + SL * S::kStage;
+      const int64_t ka = static_cast<int64_t>(kt) * kStageBytes;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) lds_load16(p.a + a_off[i] + ka, st + (wave + 4 * i) * 1024);
+      if constexpr (kSB > 0) {
+#pragma unroll
+        for (int q = 0; q < kAScPerWave; ++q)
+          lds_load4(asc_src[q] + static_cast<int64_t>(kt) * kSB, st + S::kA + (wave + 4 * q) * 256);
+      }
+      const uint8_t* bp = b_src + static_cast<int64_t>(kt) * kChunk;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          bq[SL][c][q] = *reinterpret_cast<const u32x4_t*>(bp + c * b_blk + q * 1024);
+      if constexpr (kSB > 0) {
+        const uint8_t* sp = bsc_src + static_cast<int64_t>(kt) * O::kPackedScaleBytes;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          if constexpr (OP == XOP_FP8)
+            bs[SL][c] = *reinterpret_cast<const uint16_t*>(sp + c * bsc_blk);
+          else
+            bs[SL][c] = *reinterpret_cast<const uint32_t*>(sp + c * bsc_blk);
+        }
+      }
+    };
+
+    f32x16_t acc[MAXNV][2];
+#pragma unroll
+    for (int i = 0; i < MAXNV; ++i) {
+      acc[i][0] = f32x16_t{};
+      acc[i][1] = f32x16_t{};
+    }
+
+    // MFMAs of one stage for the first NV row blocks
+    auto compute = [&](auto slot_c, auto nv_c) {
+      constexpr int SL = decltype(slot_c)::value;
+      constexpr int NV = decltype(nv_c)::value;
+      const uint8_t* sa = smem + SL * S::kStage;
+      if constexpr (OP == XOP_BF16) {
+#pragma unroll
+        for (int s = 0; s < kSub; ++s) {
+          const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, bq[SL][0][s]);
+          const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, bq[SL][1][s]);
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sa + swz<128>(32 * i + (lane & 31), 2 * s + g));
+            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[i][0], 0, 0, 0);
+            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[i][1], 0, 0, 0);
+          }
+        }
+      } else {
+        const uint32_t* sasc = reinterpret_cast<const uint32_t*>(sa + S::kA);
+#pragma unroll
+        for (int s = 0; s < kSub; ++s) {
+          i32x8_t b0, b1;
+          if constexpr (OP == XOP_FP8) {
+            const u32x4_t l0 = bq[SL][0][2 * s], h0 = bq[SL][0][2 * s + 1];
+            const u32x4_t l1 = bq[SL][1][2 * s], h1 = bq[SL][1][2 * s + 1];
+            b0 = i32x8_t{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3]};
+            b1 = i32x8_t{(int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+          } else {
+            const u32x4_t l0 = bq[SL][0][s], l1 = bq[SL][1][s];
+            b0 = i32x8_t{(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], 0, 0, 0, 0};
+            b1 = i32x8_t{(int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3], 0, 0, 0, 0};
+          }
+          const int bs0 = static_cast<int>((bs[SL][0] >> (8 * s)) & 0xFFu);
+          const int bs1 = static_cast<int>((bs[SL][1] >> (8 * s)) & 0xFFu);
+          const int blk = 2 * s + g;  // MX block of the stage this lane group scales
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            const int row = 32 * i + (lane & 31);
+            i32x8_t a;
+            if constexpr (OP == XOP_FP8) {
+              const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz<128>(row, 4 * s + g));
+              const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sa + swz<128>(row, 4 * s + 2 + g));
+              a = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            } else {
+              const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz<128>(row, 2 * s + g));
+              a = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+            }
+            const uint32_t aw = sasc[row * kDpr + (blk >> 2)];
+            const int as = static_cast<int>((aw >> (8 * (blk & 3))) & 0xFFu);
+            constexpr int fmt = OP == XOP_FP8 ? 0 : 4;
+            acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b0, acc[i][0], fmt, fmt, 0, as, 0, bs0);
+            acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b1, acc[i][1], fmt, fmt, 0, as, 0, bs1);
+          }
+        }
+      }
+    };
+
+    // ---- main loop: stage kt waits for its loads, frees slot (kt-1)%P by
+    // the barrier, issues stage kt+P-1 into it, then computes. Every
+    // iteration issues exactly one stage (past the end it re-issues the last
+    // stage, whose data nobody reads), so the ring has a single path through
+    // the loop and the wait count is a constant; the loop runs a multiple of
+    // P iterations and only computes the real stages ----
+    auto run = [&](auto nv_c) {
+      constexpr int NV = decltype(nv_c)::value;
+      constexpr int kPer = NV + kAScPerWave + 8 + (kSB > 0 ? 2 : 0);  // loads per stage
+      static_assert((P - 2) * kPer <= 62, "vmcnt range");
+      static_for<P - 1>([&](auto s_c) {
+        issue(min(static_cast<int>(decltype(s_c)::value), KT - 1), s_c, nv_c);
+      });
+      for (int k0 = 0; k0 < KT; k0 += P) {
+        static_for<P>([&](auto j_c) {
+          constexpr int J = decltype(j_c)::value;
+          const int kt = k0 + J;
+          wait_vmcnt<(P - 2) * kPer>();
+          lds_barrier();
+          issue(min(kt + P - 1, KT - 1), std::integral_constant<int, (J + P - 1) % P>{}, nv_c);
+          if (active && kt < KT) compute(j_c, nv_c);
+        });
+      }
+    };
+    switch (min(nrb, MAXNV)) {
+#define MOE_NV(N) case N: if constexpr (N <= MAXNV) run(std::integral_constant<int, N>{}); break;
+      MOE_NV(1) MOE_NV(2) MOE_NV(3) MOE_NV(4) MOE_NV(5) MOE_NV(6) MOE_NV(7) MOE_NV(8)
+#undef MOE_NV
+      default: break;
+    }
+    __syncthreads();  // every wave is done with the LDS ring
+
+    // ---- epilogue in passes of up to 128 rows through an fp32 LDS tile ----
+    // C layout of a 32x32 MFMA: lane l, element r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
+    float* cs = reinterpret_cast<float*>(smem);
+    constexpr int kPassRB = kPassRows / 32 < MAXNV ? kPassRows / 32 : MAXNV;
+    for (int pass = 0; pass * kPassRB < nrb; ++pass) {
+      if (active) {
+#pragma unroll
+        for (int i = 0; i < MAXNV; ++i) {
+          if (i / kPassRB == pass && i < nrb) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              // SwiGLU: gate values in columns [0, 128), up values in [128, 256)
+              const int col = EPI == XEPI_SWIGLU ? 128 * c + 32 * wave + (lane & 31)
+                                                 : 64 * wave + 32 * c + (lane & 31);
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int row = (i - pass * kPassRB) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                cs[row * kCs + col] = acc[i][c][r];
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      const int prow0 = pass * kPassRB * 32;
+      const int prows = min(kPassRB * 32, nrows - prow0);
+      if constexpr (EPI == XEPI_SWIGLU) {
+        const int F = p.half;
+        const int hc0 = nt * 128;                        // first h column of the tile
+        const int width = min(128, F - hc0);
+        if constexpr (OUTF == MOE_BF16) {
+          for (int i = tid; i < prows * (width / 8); i += 256) {
+            const int row = i / (width / 8), c0 = (i % (width / 8)) * 8;
+            const bool zero = p.gather && s_src[prow0 + row] < 0;
+            const float* gp = cs + row * kCs + c0;
+            const float* up = gp + 128;
+            float h[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) h[q] = zero ? 0.f : silu_mul(gp[q], up[q]);
+            const int64_t grow = row0 + prow0 + row;
+            *reinterpret_cast<u32x4_t*>(p.out + grow * p.out_row_bytes + (hc0 + c0) * 2) =
+                u32x4_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                        pack_bf16x2(h[6], h[7])};
+            if (p.act_save) {
+              float* ar = p.act_save + grow * (2ll * F) + hc0 + c0;
+              store8_f32(ar, gp);
+              store8_f32(ar + F, up);
+            }
+          }
+        } else {
+          constexpr bool fp4 = OUTF == MOE_MXFP4_E2M1;
+          const int nblk = width / 32;
+          for (int i = tid; i < prows * nblk; i += 256) {
+            const int row = i / nblk, blk = i % nblk;
+            const bool zero = p.gather && s_src[prow0 + row] < 0;
+            const float* gp = cs + row * kCs + blk * 32;
+            float v[32];
+#pragma unroll
+            for (int q = 0; q < 32; ++q) v[q] = zero ? 0.f : silu_mul(gp[q], gp[128 + q]);
+            uint32_t words[8];
+            const uint32_t sb = mx_encode_block<fp4>(v, words);
+            const int64_t grow = row0 + prow0 + row;
+            const int gblk = hc0 / 32 + blk;
+            if (fp4) {
+              *reinterpret_cast<u32x4_t*>(p.out + grow * p.out_row_bytes + gblk * 16) =
+                  u32x4_t{words[0], words[1], words[2], words[3]};
+            } else {
+              u32x4_t* o = reinterpret_cast<u32x4_t*>(p.out + grow * p.out_row_bytes + gblk * 32);
+              o[0] = u32x4_t{words[0], words[1], words[2], words[3]};
+              o[1] = u32x4_t{words[4], words[5], words[6], words[7]};
+            }
+            p.out_sc[grow * p.out_sc_row_bytes + gblk] = static_cast<uint8_t>(sb);
+            if (p.act_save) {
+              float* ar = p.act_save + grow * (2ll * F) + hc0 + blk * 32;
+#pragma unroll
+              for (int q = 0; q < 32; q += 8) {
+                store8_f32(ar + q, gp + q);
+                store8_f32(ar + F + q, gp + 128 + q);
+              }
+            }
+          }
+        }
+      } else if constexpr (EPI == XEPI_PLAIN) {
+        const int c_first = nt * kTileCols;
+        const int width = min(kTileCols, p.ncb * 32 - c_first);
+        for (int i = tid; i < prows * (width / 8); i += 256) {
+          const int row = i / (width / 8), c0 = (i % (width / 8)) * 8;
+          const float* v = cs + row * kCs + c0;
+          *reinterpret_cast<u32x4_t*>(p.out + static_cast<int64_t>(row0 + prow0 + row) * p.out_row_bytes +
+                                      static_cast<int64_t>(c_first + c0) * 2) =
+              u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7])};
+        }
+      } else {
+        // dSwiGLU: the tile holds dH for F columns [256 nt, +width); with the
+        // saved fc1 output (g | u): dgate = dH * u * sig(g) * (1 + g * (1 - sig(g))),
+        // dup = dH * silu(g)
+        const int F = p.half;
+        const int64_t a2 = 2ll * F;
+        const int c_first = nt * kTileCols;
+        const int width = min(kTileCols, F - c_first);
+        if constexpr (OUTF == MOE_BF16) {
+          for (int i = tid; i < prows * (width / 8); i += 256) {
+            const int row = i / (width / 8), c0 = (i % (width / 8)) * 8;
+            const int col = c_first + c0;
+            const int64_t grow = row0 + prow0 + row;
+            float gv[8], uv[8], dg[8], du[8];
+            load8_f32(p.a_saved + grow * a2 + col, gv);
+            load8_f32(p.a_saved + grow * a2 + F + col, uv);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const float dh = cs[row * kCs + c0 + q];
+              const float sg = sigmoidf_(gv[q]);
+              dg[q] = dh * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
+              du[q] = dh * (gv[q] * sg);
+            }
+            uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + grow * a2;
+            *reinterpret_cast<u32x4_t*>(o + col) =
+                u32x4_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]), pack_bf16x2(dg[4], dg[5]),
+                        pack_bf16x2(dg[6], dg[7])};
+            *reinterpret_cast<u32x4_t*>(o + F + col) =
+                u32x4_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]), pack_bf16x2(du[4], du[5]),
+                        pack_bf16x2(du[6], du[7])};
+            if (p.da_f32) {
+              store8_f32(p.da_f32 + grow * a2 + col, dg);
+              store8_f32(p.da_f32 + grow * a2 + F + col, du);
+            }
+          }
+        } else {
+          constexpr bool fp4 = OUTF == MOE_MXFP4_E2M1;
+          constexpr int kBlkBytes = fp4 ? 16 : 32;
+          const int nblk = width / 32;
+          for (int i = tid; i < prows * nblk; i += 256) {
+            const int row = i / nblk, blk = i % nblk;
+            const int col = c_first + blk * 32;
+            const int64_t grow = row0 + prow0 + row;
+            float dg[32], du[32];
+#pragma unroll
+            for (int w8 = 0; w8 < 4; ++w8) {
+              float gv[8], uv[8];
+              load8_f32(p.a_saved + grow * a2 + col + w8 * 8, gv);
+              load8_f32(p.a_saved + grow * a2 + F + col + w8 * 8, uv);
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                const float dh = cs[row * kCs + blk * 32 + w8 * 8 + q];
+                const float sg = sigmoidf_(gv[q]);
+                dg[w8 * 8 + q] = dh * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
+                du[w8 * 8 + q] = dh * (gv[q] * sg);
+              }
+            }
+            uint32_t words[8];
+            uint8_t* orow = p.out + grow * p.out_row_bytes;
+            uint8_t* srow = p.out_sc + grow * p.out_sc_row_bytes;
+#pragma unroll
+            for (int part2 = 0; part2 < 2; ++part2) {
+              const float* v = part2 ? du : dg;
+              const int c = part2 ? F + col : col;
+              const uint32_t sb = mx_encode_block<fp4>(v, words);
+              u32x4_t* o = reinterpret_cast<u32x4_t*>(orow + (c / 32) * kBlkBytes);
+              o[0] = u32x4_t{words[0], words[1], words[2], words[3]};
+              if (!fp4) o[1] = u32x4_t{words[4], words[5], words[6], words[7]};
+              srow[c / 32] = static_cast<uint8_t>(sb);
+              if (p.da_f32) {
+                float* ob = p.da_f32 + grow * a2 + c;
+#pragma unroll
+                for (int w8 = 0; w8 < 4; ++w8) store8_f32(ob + w8 * 8, v + w8 * 8);
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();  // the LDS tile is rewritten by the next pass / tile
+    }
+  }
+}
+
+// ---- weight packing ---------------------------------------------------------
+// packed[e][cb][s][q][lane][16 B] = row R(cb, lane % 32) of expert e, bytes
+// [128 s + 32 q + 16 (lane / 32), +16), where R is 32 cb + lane % 32, or with
+// gate/up pairing (half = F > 0) gate row 32 (cb / 2) + lane % 32 for even cb
+// and up row F + 32 (cb / 2) + lane % 32 for odd cb.
+// packed scales [e][cb][s][lane][j] = scale of that row's MX block
+// (stage-local) 2 j + lane / 32, j < kSub.
+__device__ __forceinline__ int packed_row(int cb, int lane, int half) {
+  if (half > 0) return ((cb & 1) ? half : 0) + 32 * (cb >> 1) + (lane & 31);
+  return 32 * cb + (lane & 31);
+}
+
+__global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restrict__ w, int64_t E,
+                                                         int N, int64_t kbytes, int half,
+                                                         uint8_t* __restrict__ out) {
+  const int ncb = N / 32;
+  const int64_t S = kbytes / kStageBytes;
+  const int64_t total = E * ncb * S * 4 * 64;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += 256ll * gridDim.x) {
+    const int lane = static_cast<int>(i & 63);
+    const int q = static_cast<int>((i >> 6) & 3);
+    const int64_t rest = i >> 8;
+    const int64_t s = rest % S;
+    const int64_t cbe = rest / S;
+    const int cb = static_cast<int>(cbe % ncb);
+    const int64_t e = cbe / ncb;
+    const int64_t row = e * N + packed_row(cb, lane, half);
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(w + row * kbytes + s * kStageBytes + 32 * q + 16 * (lane >> 5));
+    *reinterpret_cast<u32x4_t*>(out + i * 16) = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restrict__ sc, int64_t E,
+                                                          int N, int64_t kblocks, int sub, int half,
+                                                          uint8_t* __restrict__ out) {
+  const int ncb = N / 32;
+  const int64_t blocks_per_stage = 2 * sub;  // MX blocks of 32 per stage
+  const int64_t S = kblocks / blocks_per_stage;
+  const int64_t total = E * ncb * S * 64 * sub;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += 256ll * gridDim.x) {
+    const int j = static_cast<int>(i % sub);
+    const int64_t li = i / sub;
+    const int lane = static_cast<int>(li & 63);
+    const int64_t rest = li >> 6;
+    const int64_t s = rest % S;
+    const int64_t cbe = rest / S;
+    const int cb = static_cast<int>(cbe % ncb);
+    const int64_t e = cbe / ncb;
+    const int64_t row = e * N + packed_row(cb, lane, half);
+    out[i] = sc[row * kblocks + s * blocks_per_stage + 2 * j + (lane >> 5)];
+  }
+}
+
+}  // namespace
+
+int xop_of(int fmt) {
+  return fmt == MOE_BF16 ? XOP_BF16 : (fmt == MOE_MXFP8_E4M3 ? XOP_FP8 : XOP_FP4);
+}
+
+// Launch of one grouped expert GEMM with packed weights. kind: 0 fc1 +
+// SwiGLU (N = 2F, out = h), 1 plain (out = y bf16), 2 dSwiGLU (N = F, out =
+// dA). All arguments are validated by the callers.
+int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const int32_t* gather,
+                const void* wp, const uint8_t* wp_scales, const int32_t* offsets, int E, int N,
+                int K, int64_t rows, int half, void* out, uint8_t* out_scales, float* act_save,
+                const float* a_saved, float* da_f32, hipStream_t stream) {
+  const int bits = fmt == MOE_BF16 ? 16 : (fmt == MOE_MXFP8_E4M3 ? 8 : 4);
+  // activation row offsets are 32-bit inside the kernel; a gathered source
+  // has at most `rows` rows as well
+  MOE_REQUIRE(rows * (static_cast<int64_t>(K) * bits / 8) < (int64_t{1} << 32), MOE_ERR_UNSUPPORTED,
+              "grouped expert GEMM: activation matrix of 4 GiB or more");
+  XArgs x{};
+  x.a = static_cast<const uint8_t*>(a);
+  x.a_row_bytes = static_cast<int64_t>(K) * bits / 8;
+  x.a_sc = a_scales;
+  x.a_sc_row_bytes = K / 32;
+  x.gather = gather;
+  x.b = static_cast<const uint8_t*>(wp);
+  x.b_exp_bytes = static_cast<int64_t>(N) * K * bits / 8;
+  x.b_sc = wp_scales;
+  x.b_sc_exp_bytes = static_cast<int64_t>(N) * (K / 32);
+  x.ncb = N / 32;
+  x.n_tiles = kind == 0 ? (N / 2 + 127) / 128 : (N + kTileCols - 1) / kTileCols;
+  x.k_stages = static_cast<int>(x.a_row_bytes / kStageBytes);
+  x.offsets = offsets;
+  x.E = E;
+  x.rows = rows;
+  x.half = half;
+  x.out = static_cast<uint8_t*>(out);
+  x.out_sc = out_scales;
+  x.act_save = act_save;
+  x.a_saved = a_saved;
+  x.da_f32 = da_f32;
+  const int outw = kind == 0 ? half : (kind == 1 ? N : 2 * half);  // output row elements
+  const bool mx_out = kind != 1 && fmt != MOE_BF16;
+  x.out_row_bytes = mx_out ? static_cast<int64_t>(outw) * bits / 8 : static_cast<int64_t>(outw) * 2;
+  x.out_sc_row_bytes = outw / 32;
+  const dim3 grid(kNumCu), block(256);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, x); };
+  constexpr int MN = 8, PP = 3;
+  switch (kind * 3 + xop_of(fmt)) {
+    case 0: go(expert_gemm_kernel<MN, PP, XOP_BF16, XEPI_SWIGLU, MOE_BF16>); break;
+    case 1: go(expert_gemm_kernel<MN, PP, XOP_FP8, XEPI_SWIGLU, MOE_MXFP8_E4M3>); break;
+    case 2: go(expert_gemm_kernel<MN, PP, XOP_FP4, XEPI_SWIGLU, MOE_MXFP4_E2M1>); break;
+    case 3: go(expert_gemm_kernel<MN, PP, XOP_BF16, XEPI_PLAIN, MOE_BF16>); break;
+    case 4: go(expert_gemm_kernel<MN, PP, XOP_FP8, XEPI_PLAIN, MOE_BF16>); break;
+    case 5: go(expert_gemm_kernel<MN, PP, XOP_FP4, XEPI_PLAIN, MOE_BF16>); break;
+    case 6: go(expert_gemm_kernel<MN, PP, XOP_BF16, XEPI_DSWIGLU, MOE_BF16>); break;
+    case 7: go(expert_gemm_kernel<MN, PP, XOP_FP8, XEPI_DSWIGLU, MOE_MXFP8_E4M3>); break;
+    default: go(expert_gemm_kernel<MN, PP, XOP_FP4, XEPI_DSWIGLU, MOE_MXFP4_E2M1>); break;
+  }
+  return check_launch("grouped expert GEMM");
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_pack_weights(const void* w, const uint8_t* w_scales, int fmt, int E, int N,
+                                int K, int half, void* out, uint8_t* out_scales,
+                                hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(E >= 1 && N > 0 && K > 0, MOE_ERR_INVALID_ARG, "moe_pack_weights: need E, N, K > 0");
+  MOE_REQUIRE(fmt == MOE_BF16 || fmt == MOE_MXFP8_E4M3 || fmt == MOE_MXFP4_E2M1, MOE_ERR_UNSUPPORTED,
+              "moe_pack_weights: fmt must be MOE_BF16 or an MX format");
+  const int bits = fmt == MOE_BF16 ? 16 : (fmt == MOE_MXFP8_E4M3 ? 8 : 4);
+  const int64_t kbytes = static_cast<int64_t>(K) * bits / 8;
+  MOE_REQUIRE(N % 64 == 0 && kbytes % kStageBytes == 0, MOE_ERR_INVALID_ARG,
+              "moe_pack_weights: need N % 64 == 0 and K a multiple of one 128-byte stage "
+              "(64 bf16, 128 E4M3 or 256 E2M1 values)");
+  MOE_REQUIRE(half == 0 || (half > 0 && N == 2 * half && half % 32 == 0), MOE_ERR_INVALID_ARG,
+              "moe_pack_weights: gate/up pairing needs N == 2 * half and half % 32 == 0");
+  MOE_REQUIRE(w && out && (fmt == MOE_BF16 || (w_scales && out_scales)), MOE_ERR_INVALID_ARG,
+              "moe_pack_weights: null pointer");
+  MOE_REQUIRE(aligned16(w) && aligned16(out), MOE_ERR_ALIGNMENT,
+              "moe_pack_weights: w and out must be 16-byte aligned");
+  const int64_t pieces = static_cast<int64_t>(E) * N * kbytes / 16;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(65536, (pieces + 255) / 256));
+  hipLaunchKernelGGL(pack_codes_kernel, dim3(grid), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(w), static_cast<int64_t>(E), N, kbytes, half,
+                     static_cast<uint8_t*>(out));
+  if (fmt != MOE_BF16) {
+    const int sub = fmt == MOE_MXFP8_E4M3 ? XOp<XOP_FP8>::kSub : XOp<XOP_FP4>::kSub;
+    const int64_t nsc = static_cast<int64_t>(E) * N * (K / 32);
+    const unsigned g2 = static_cast<unsigned>(std::min<int64_t>(65536, (nsc + 255) / 256));
+    hipLaunchKernelGGL(pack_scales_kernel, dim3(g2), dim3(256), 0, stream, w_scales,
+                       static_cast<int64_t>(E), N, static_cast<int64_t>(K / 32), sub, half,
+                       out_scales);
+  }
+  return check_launch("moe_pack_weights");
+}

@@ -40,11 +40,16 @@
 //   * fc2 tiles store y (bf16) through LDS as full 16-byte row chunks.
 #include "common.h"
 #include "mx_codec.h"
+#include "gemm_util.h"
 
 #include <algorithm>
 #include <type_traits>
 
 namespace moe {
+int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const int32_t* gather,
+                const void* wp, const uint8_t* wp_scales, const int32_t* offsets, int E, int N,
+                int K, int64_t rows, int half, void* out, uint8_t* out_scales, float* act_save,
+                const float* a_saved, float* da_f32, hipStream_t stream);
 namespace {
 
 constexpr int kMaxGroups = 1024;
@@ -113,57 +118,6 @@ struct Smem {
   static constexpr int kSched = (kMaxGroups + 2) * 4 + MMAX * 4;
   static constexpr int kTotal = STAGES * kStage + kSched;
 };
-
-__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                   (void __attribute__((address_space(3)))*)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_load4(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                   (void __attribute__((address_space(3)))*)lds, 4, 0, 0);
-}
-
-// Wait until at most n vector-memory operations of this wave are in flight.
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-#define MOE_W(N) case N: wait_vmcnt<N>(); break;
-    MOE_W(0) MOE_W(1) MOE_W(2) MOE_W(3) MOE_W(4) MOE_W(5) MOE_W(6) MOE_W(7)
-    MOE_W(8) MOE_W(9) MOE_W(10) MOE_W(11) MOE_W(12) MOE_W(13) MOE_W(14) MOE_W(15)
-    MOE_W(16) MOE_W(17) MOE_W(18) MOE_W(19) MOE_W(20) MOE_W(21) MOE_W(22) MOE_W(23)
-    MOE_W(24) MOE_W(25) MOE_W(26) MOE_W(27) MOE_W(28) MOE_W(29) MOE_W(30) MOE_W(31)
-    MOE_W(32) MOE_W(33) MOE_W(34) MOE_W(35) MOE_W(36) MOE_W(37) MOE_W(38) MOE_W(39)
-    MOE_W(40) MOE_W(41) MOE_W(42) MOE_W(43) MOE_W(44) MOE_W(45) MOE_W(46) MOE_W(47)
-    MOE_W(48) MOE_W(49) MOE_W(50) MOE_W(51) MOE_W(52) MOE_W(53) MOE_W(54) MOE_W(55)
-    MOE_W(56) MOE_W(57) MOE_W(58) MOE_W(59) MOE_W(60) MOE_W(61) MOE_W(62)
-#undef MOE_W
-    default: wait_vmcnt<0>(); break;
-  }
-}
-
-// Workgroup barrier for the stage pipeline: waits only for this wave's LDS
-// operations (not for the global->LDS loads still in flight, which the
-// explicit vmcnt accounting covers) before s_barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// byte offset of 16-byte chunk c of row r inside a [rows][128 B] stage tile
-// A stage tile stores row r's RB/16 chunks of 16 bytes XOR-permuted by a key
-// of r: (r/2)%8 for 128-byte rows, (r/4)%4 for 64-byte rows. Either way any
-// 16 consecutive rows put one logical chunk into 16 distinct 16-byte bank
-// groups of a 256-byte LDS line, so the MFMA operand reads (16 lanes = 16
-// consecutive rows per LDS cycle) are free of bank conflicts.
-template <int RB>
-__device__ __forceinline__ int swz_key(int r) {
-  return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
-}
-template <int RB>
-__device__ __forceinline__ int swz(int r, int c) { return r * RB + ((c ^ swz_key<RB>(r)) << 4); }
-
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  const float sig = 1.f / (1.f + expf(-g));
-  return g * sig * u;
-}
 
 // Weight row that tile row `br` streams. fc1 (SwiGLU): tile rows come in
 // groups of 32 = 16 gate rows then the matching 16 up rows, group q covering
@@ -803,7 +757,6 @@ static int fc1_impl(const void* a, const uint8_t* a_scales, int a_fmt, const int
                     const void* w1, const uint8_t* w1_scales, const int32_t* offsets, int E, int H,
                     int F, int64_t rows, float* act_save, void* h, uint8_t* h_scales,
                     hipStream_t stream) {
-  const int bits = elem_bits(a_fmt);
   if (a_fmt == MOE_F32) {
     const int64_t g1 = std::min<int64_t>(65536, (rows * F + 255) / 256);
     hipLaunchKernelGGL(fc1_swiglu_f32_kernel, dim3(g1), dim3(256), 0, stream,
@@ -812,48 +765,13 @@ static int fc1_impl(const void* a, const uint8_t* a_scales, int a_fmt, const int
                        static_cast<float*>(act_save));
     return check_launch("moe_grouped_fc1_swiglu");
   }
-  Args f1{};
-  f1.a = static_cast<const uint8_t*>(a);
-  f1.a_row_bytes = static_cast<int64_t>(H) * bits / 8;
-  f1.a_sc = a_scales;
-  f1.a_sc_row_bytes = H / 32;
-  f1.gather = src_row;
-  f1.b = static_cast<const uint8_t*>(w1);
-  f1.b_row_bytes = static_cast<int64_t>(H) * bits / 8;
-  f1.b_exp_bytes = 2ll * F * f1.b_row_bytes;
-  f1.b_sc = w1_scales;
-  f1.b_sc_row_bytes = H / 32;
-  f1.b_sc_exp_bytes = 2ll * F * (H / 32);
-  f1.up_row = F;
-  f1.offsets = offsets;
-  f1.E = E;
-  f1.rows = rows;
-  f1.n_blocks = F / 64;
-  f1.out = static_cast<uint8_t*>(h);
-  f1.out_row_bytes = static_cast<int64_t>(F) * bits / 8;
-  f1.out_sc = h_scales;
-  f1.out_sc_row_bytes = F / 32;
-  f1.act_save = static_cast<float*>(act_save);
-  f1.act_cols = 2 * F;
-  // 128-row tiles of 256 weight rows (two 32-column MFMA blocks per wave, 8
-  // waves) for routed experts; 256-row tiles of 128 weight rows for a single
-  // dense group (a shared expert: more rows per weight tile, fewer weight
-  // re-reads) or when F is not a multiple of 128
-  const bool wide = F % 128 == 0 && E > 1;
-  if (a_fmt == MOE_BF16)
-    return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_BF16, EPI_SWIGLU, MOE_BF16>(f1, stream)
-                : launch_gemm<256, 3, 1, 2, 1, 128, OP_BF16, EPI_SWIGLU, MOE_BF16>(f1, stream);
-  if (a_fmt == MOE_MXFP8_E4M3)
-    return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP8, EPI_SWIGLU, MOE_MXFP8_E4M3>(f1, stream)
-                : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP8, EPI_SWIGLU, MOE_MXFP8_E4M3>(f1, stream);
-  return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP4, EPI_SWIGLU, MOE_MXFP4_E2M1>(f1, stream)
-              : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP4, EPI_SWIGLU, MOE_MXFP4_E2M1>(f1, stream);
+  return expert_gemm(0, a, a_scales, a_fmt, src_row, w1, w1_scales, offsets, E, 2 * F, H, rows,
+                     F, h, h_scales, act_save, nullptr, nullptr, stream);
 }
 
 static int fc2_impl(const void* h, const uint8_t* h_scales, int h_fmt, const void* w2,
                     const uint8_t* w2_scales, const int32_t* offsets, int E, int H, int F,
                     int64_t rows, void* y, hipStream_t stream) {
-  const int bits = elem_bits(h_fmt);
   if (h_fmt == MOE_F32) {
     const int64_t g2 = std::min<int64_t>(65536, (rows * H + 255) / 256);
     hipLaunchKernelGGL(fc2_f32_kernel, dim3(g2), dim3(256), 0, stream,
@@ -861,34 +779,8 @@ static int fc2_impl(const void* h, const uint8_t* h_scales, int h_fmt, const voi
                        F, rows, static_cast<float*>(y));
     return check_launch("moe_grouped_fc2");
   }
-  Args f2{};
-  f2.a = static_cast<const uint8_t*>(h);
-  f2.a_row_bytes = static_cast<int64_t>(F) * bits / 8;
-  f2.a_sc = h_scales;
-  f2.a_sc_row_bytes = F / 32;
-  f2.gather = nullptr;
-  f2.b = static_cast<const uint8_t*>(w2);
-  f2.b_row_bytes = static_cast<int64_t>(F) * bits / 8;
-  f2.b_exp_bytes = static_cast<int64_t>(H) * f2.b_row_bytes;
-  f2.b_sc = w2_scales;
-  f2.b_sc_row_bytes = F / 32;
-  f2.b_sc_exp_bytes = static_cast<int64_t>(H) * (F / 32);
-  f2.up_row = 0;
-  f2.offsets = offsets;
-  f2.E = E;
-  f2.rows = rows;
-  f2.n_blocks = H / 128;
-  f2.out = static_cast<uint8_t*>(y);
-  f2.out_row_bytes = static_cast<int64_t>(H) * 2;
-  const bool wide = H % 256 == 0 && E > 1;
-  if (h_fmt == MOE_BF16)
-    return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_BF16, EPI_PLAIN, MOE_BF16>(f2, stream)
-                : launch_gemm<256, 3, 1, 2, 1, 128, OP_BF16, EPI_PLAIN, MOE_BF16>(f2, stream);
-  if (h_fmt == MOE_MXFP8_E4M3)
-    return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP8, EPI_PLAIN, MOE_BF16>(f2, stream)
-                : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP8, EPI_PLAIN, MOE_BF16>(f2, stream);
-  return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP4, EPI_PLAIN, MOE_BF16>(f2, stream)
-              : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP4, EPI_PLAIN, MOE_BF16>(f2, stream);
+  return expert_gemm(1, h, h_scales, h_fmt, nullptr, w2, w2_scales, offsets, E, H, F, rows, 0, y,
+                     nullptr, nullptr, nullptr, nullptr, stream);
 }
 
 }  // namespace
@@ -1020,38 +912,8 @@ extern "C" int moe_grouped_fc2_dgrad_dswiglu(const void* dy, const uint8_t* dy_s
                   (!da_f32 || aligned16(da_f32)),
               MOE_ERR_ALIGNMENT, "moe_grouped_fc2_dgrad_dswiglu: tensors must be 16-byte aligned");
   if (rows == 0) return MOE_OK;
-  const int bits = elem_bits(fmt);
-  Args g{};
-  g.a = static_cast<const uint8_t*>(dy);
-  g.a_row_bytes = static_cast<int64_t>(H) * bits / 8;
-  g.a_sc = dy_scales;
-  g.a_sc_row_bytes = H / 32;
-  g.b = static_cast<const uint8_t*>(w2t);
-  g.b_row_bytes = g.a_row_bytes;
-  g.b_exp_bytes = static_cast<int64_t>(F) * g.b_row_bytes;
-  g.b_sc = w2t_scales;
-  g.b_sc_row_bytes = H / 32;
-  g.b_sc_exp_bytes = static_cast<int64_t>(F) * (H / 32);
-  g.up_row = F;
-  g.offsets = offsets;
-  g.E = E;
-  g.rows = rows;
-  g.n_blocks = F / 128;
-  g.out = static_cast<uint8_t*>(da);
-  g.out_row_bytes = 2ll * F * bits / 8;
-  g.out_sc = da_scales;
-  g.out_sc_row_bytes = 2 * F / 32;
-  g.a_saved = static_cast<const float*>(act_save);
-  g.da_f32 = da_f32;
-  const bool wide = F % 256 == 0;
-  if (fmt == MOE_BF16)
-    return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_BF16, EPI_DSWIGLU, MOE_BF16>(g, stream)
-                : launch_gemm<256, 3, 1, 2, 1, 128, OP_BF16, EPI_DSWIGLU, MOE_BF16>(g, stream);
-  if (fmt == MOE_MXFP8_E4M3)
-    return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP8, EPI_DSWIGLU, MOE_MXFP8_E4M3>(g, stream)
-                : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP8, EPI_DSWIGLU, MOE_MXFP8_E4M3>(g, stream);
-  return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP4, EPI_DSWIGLU, MOE_MXFP4_E2M1>(g, stream)
-              : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP4, EPI_DSWIGLU, MOE_MXFP4_E2M1>(g, stream);
+  return expert_gemm(2, dy, dy_scales, fmt, nullptr, w2t, w2t_scales, offsets, E, F, H, rows, F,
+                     da, da_scales, nullptr, act_save, da_f32, stream);
 }
 
 extern "C" int moe_grouped_fc1_dgrad(const void* da, const uint8_t* da_scales, int fmt,

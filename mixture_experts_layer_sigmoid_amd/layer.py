@@ -69,13 +69,28 @@ def quantize_mx_t(t: torch.Tensor, fmt: str, stream=None):
     return codes, scales
 
 
+def pack_weights(codes: torch.Tensor, scales, fmt: str, half: int = 0, stream=None):
+    """moe_pack_weights of [E, N, K] stored weights (bf16 values or MX codes
+    with [E, N, K/32] scales) into the grouped GEMMs' streaming order.
+    Returns (packed uint8 [E, bytes per expert], packed scales or None)."""
+    E, N = codes.shape[0], codes.shape[1]
+    K = codes.shape[2] * (2 if fmt == "mxfp4" else 1)
+    nbytes = codes[0].numel() * codes.element_size()
+    out = torch.empty((E, nbytes), dtype=torch.uint8, device=codes.device)
+    out_sc = torch.empty_like(scales) if scales is not None else None
+    L.moe_pack_weights(codes, scales, FMT[fmt], E, N, K, half, out, out_sc, stream)
+    return out, out_sc
+
+
 @dataclass
 class ExpertWeights:
-    """Stored expert weights: w1 [E, 2F, H], w2 [E, H, F] in the layer
-    format (MX: codes, with scales w1_sc [E, 2F, H/32], w2_sc [E, H, F/32]).
-    With `transposed`, also the copies the backward's data-gradient GEMMs
-    contract over: w1t [E, H, 2F] (blocks along 2F), w2t [E, F, H] (blocks
-    along H), quantized from the same masters."""
+    """Expert weights as the grouped GEMMs consume them. fp32: plain w1
+    [E, 2F, H] and w2 [E, H, F]. bf16 / MX: stored values (MX: E4M3 / E2M1
+    codes with one E8M0 scale per 32 values along K) packed by
+    moe_pack_weights, w1 with its gate/up halves paired. With
+    `transposed`, also the copies the backward's data-gradient GEMMs
+    contract over: w1t [E, H, 2F] (blocks along 2F) and w2t [E, F, H]
+    (blocks along H), quantized from the same masters and packed."""
     w1: torch.Tensor
     w2: torch.Tensor
     w1_sc: torch.Tensor | None = None
@@ -88,17 +103,34 @@ class ExpertWeights:
     @staticmethod
     def from_dense(w1: torch.Tensor, w2: torch.Tensor, fmt: str, stream=None,
                    transposed: bool = False) -> "ExpertWeights":
-        if not is_mx(fmt):
+        if fmt == "fp32":
             if transposed:
                 raise ValueError("transposed weight copies are built for MX formats only")
             return ExpertWeights(w1, w2)
+        F = w1.shape[1] // 2
+        if fmt == "bf16":
+            if transposed:
+                raise ValueError("transposed weight copies are built for MX formats only")
+            p1, _ = pack_weights(w1, None, fmt, F, stream)
+            p2, _ = pack_weights(w2, None, fmt, 0, stream)
+            return ExpertWeights(p1, p2)
         c1, s1 = quantize_mx(w1, fmt, stream)
         c2, s2 = quantize_mx(w2, fmt, stream)
-        ew = ExpertWeights(c1, c2, s1, s2)
+        p1, q1 = pack_weights(c1, s1, fmt, F, stream)
+        p2, q2 = pack_weights(c2, s2, fmt, 0, stream)
+        del c1, s1, c2, s2
+        ew = ExpertWeights(p1, p2, q1, q2)
         if transposed:
-            ew.w1t, ew.w1t_sc = quantize_mx_t(w1, fmt, stream)
-            ew.w2t, ew.w2t_sc = quantize_mx_t(w2, fmt, stream)
+            c, sc = quantize_mx_t(w1, fmt, stream)
+            ew.w1t, ew.w1t_sc = pack_weights(c, sc, fmt, 0, stream)
+            del c, sc
+            c, sc = quantize_mx_t(w2, fmt, stream)
+            ew.w2t, ew.w2t_sc = pack_weights(c, sc, fmt, 0, stream)
         return ew
+
+    @property
+    def E(self) -> int:
+        return self.w1.shape[0]
 
 
 class MoEForward:
