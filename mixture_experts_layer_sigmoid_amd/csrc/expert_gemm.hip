@@ -61,7 +61,6 @@ constexpr int kMaxGroups = 1024;
 constexpr int kStageBytes = 128;        // bytes of K per row per stage
 constexpr int kChunk = 4096;            // packed bytes per (column block, stage)
 constexpr int kTileCols = 256;          // weight rows per tile (8 column blocks)
-constexpr int kPassRows = 128;          // epilogue rows per LDS pass
 constexpr int kCs = kTileCols + 4;      // padded fp32 row stride of the epilogue tile
 
 enum { XOP_BF16 = 0, XOP_FP8 = 1, XOP_FP4 = 2 };
@@ -101,8 +100,15 @@ struct XArgs {
   float* da_f32;             // dSwiGLU: optional fp32 copy of dA [rows, 2F]
 };
 
-template <int MAXNV, int P, int OP>
+// epilogue rows per LDS pass: 128, or 64 with two workgroups per CU
+template <int OCC>
+struct XPass {
+  static constexpr int kRows = OCC == 1 ? 128 : 64;
+};
+
+template <int MAXNV, int P, int OP, int OCC>
 struct XSmem {
+  static constexpr int kPassRows = XPass<OCC>::kRows;
   static constexpr int kRows = 32 * MAXNV;
   static constexpr int kA = kRows * kStageBytes;
   static constexpr int kASc = kRows * XOp<OP>::kScaleBytes;
@@ -130,9 +136,12 @@ __device__ __forceinline__ void static_for(Fn&& f) { static_for_impl<0, N>(f); }
 // MAXNV: row blocks of 32 per tile (tile rows = 32 * MAXNV)
 // P:     stages in flight (LDS ring for the activations, register ring for
 //        the weights)
-template <int MAXNV, int P, int OP, int EPI, int OUTF>
-__global__ __launch_bounds__(256) void expert_gemm_kernel(XArgs p) {
-  using S = XSmem<MAXNV, P, OP>;
+// OCC:   workgroups resident per CU (persistent grid = 256 * OCC)
+template <int MAXNV, int P, int OCC, int OP, int EPI, int OUTF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void expert_gemm_kernel(XArgs p) {
+  using S = XSmem<MAXNV, P, OP, OCC>;
+  constexpr int kPassRows = S::kPassRows;
   using O = XOp<OP>;
   constexpr int kRows = S::kRows;
   constexpr int kSB = O::kScaleBytes;
@@ -140,10 +149,12 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(XArgs p) {
   constexpr int kAIns = kRows / 8 / 4;              // 1 KB A loads per wave per stage (max)
   constexpr int kDpr = kSB > 0 ? kSB / 4 : 1;       // scale dwords per row per stage
   constexpr int kScRows = 64 / kDpr;                // rows per 4-byte-per-lane scale load
-  constexpr int kAScIns = kSB > 0 ? kRows / kScRows : 0;
-  constexpr int kAScPerWave = kAScIns / 4;
+  constexpr int kAScIns = kSB > 0 ? (kRows + kScRows - 1) / kScRows : 0;
+  // every wave issues the same number of scale loads; when there are fewer
+  // loads than waves the extra waves repeat the last one (same bytes to the
+  // same LDS words)
+  constexpr int kAScPerWave = kSB > 0 ? (kAScIns + 3) / 4 : 0;
   static_assert(kAIns >= 1, "tile needs at least 32 rows");
-  static_assert(kSB == 0 || kAScIns % 4 == 0, "scale loads must split evenly over the waves");
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::kTotal];
   int32_t* s_mt = reinterpret_cast<int32_t*>(smem + S::kBody);   // [E+1] row-tile prefix
   int32_t* s_src = s_mt + (kMaxGroups + 1);                       // [kRows] source rows
@@ -235,7 +246,7 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(XArgs p) {
     if constexpr (kSB > 0) {
 #pragma unroll
       for (int q = 0; q < kAScPerWave; ++q) {
-        const int j = wave + 4 * q;  // scale load j covers rows [j * kScRows, +kScRows)
+        const int j = min(wave + 4 * q, kAScIns - 1);  // covers rows [j * kScRows, +kScRows)
         const int r = min(j * kScRows + lane / kDpr, nrows - 1);
         int src = row0 + r;
         if (p.gather) {
@@ -263,40 +274,41 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(XArgs p) {
     u32x4_t bq[P][2][4];
     uint32_t bs[P][2];
 
-    // One stage of loads: exactly NV activation loads, kAScPerWave scale
-    // loads and 8 (+2) weight loads per wave, whatever the row count and
-    // whether the wave has columns (rows past the tile's end re-read its
-    // last row, an idle wave re-reads column block 0), so the vector-memory
-    // count of a stage is a compile-time constant for both the explicit
-    // waits and the compiler's own.
-    auto issue = [&](int kt, auto slot_c, auto nv_c) {
+    // One stage of loads is kPer(NV) operations per wave: 8 weight loads
+    // (+2 MX scale words), NV activation row loads and kAScPerWave MX
+    // scale loads of the rows, whatever the row count and whether the wave
+    // has columns (rows past the tile's end re-read its last row, an idle
+    // wave re-reads column block 0), so the vector-memory count of a stage
+    // is a compile-time constant for both the explicit waits and the
+    // compiler's own. issue_op(kt, slot, op) issues operation op of stage kt.
+    auto issue_op = [&](int kt, auto slot_c, auto nv_c, auto op_c) {
       constexpr int SL = decltype(slot_c)::value;
       constexpr int NV = decltype(nv_c)::value;
-      uint8_t* st = smem + SL * S::kStage;
-      const int64_t ka = static_cast<int64_t>(kt) * kStageBytes;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) lds_load16(p.a + a_off[i] + ka, st + (wave + 4 * i) * 1024);
-      if constexpr (kSB > 0) {
-#pragma unroll
-        for (int q = 0; q < kAScPerWave; ++q)
-          lds_load4(asc_src[q] + static_cast<int64_t>(kt) * kSB, st + S::kA + (wave + 4 * q) * 256);
+      constexpr int OPN = decltype(op_c)::value;
+      constexpr int kB = 8 + (kSB > 0 ? 2 : 0);
+      if constexpr (OPN < 8) {
+        constexpr int c = OPN / 4, q = OPN % 4;
+        const uint8_t* bp = b_src + static_cast<int64_t>(kt) * kChunk;
+        bq[SL][c][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(bp + c * b_blk + q * 1024));
+      } else if constexpr (OPN < kB) {
+        constexpr int c = OPN - 8;
+        const uint8_t* sp = bsc_src + static_cast<int64_t>(kt) * O::kPackedScaleBytes + c * bsc_blk;
+        if constexpr (OP == XOP_FP8) bs[SL][c] = *reinterpret_cast<const uint16_t*>(sp);
+        else bs[SL][c] = *reinterpret_cast<const uint32_t*>(sp);
+      } else if constexpr (OPN < kB + NV) {
+        constexpr int i = OPN - kB;
+        uint8_t* st = smem + SL * S::kStage;
+        lds_load16(p.a + a_off[i] + static_cast<int64_t>(kt) * kStageBytes, st + (wave + 4 * i) * 1024);
+      } else {
+        constexpr int q = OPN - kB - NV;
+        uint8_t* st = smem + SL * S::kStage;
+        lds_load4(asc_src[q] + static_cast<int64_t>(kt) * kSB, st + S::kA + min(wave + 4 * q, kAScIns - 1) * 256);
       }
-      const uint8_t* bp = b_src + static_cast<int64_t>(kt) * kChunk;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          bq[SL][c][q] = *reinterpret_cast<const u32x4_t*>(bp + c * b_blk + q * 1024);
-      if constexpr (kSB > 0) {
-        const uint8_t* sp = bsc_src + static_cast<int64_t>(kt) * O::kPackedScaleBytes;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          if constexpr (OP == XOP_FP8)
-            bs[SL][c] = *reinterpret_cast<const uint16_t*>(sp + c * bsc_blk);
-          else
-            bs[SL][c] = *reinterpret_cast<const uint32_t*>(sp + c * bsc_blk);
-        }
-      }
+    };
+    auto issue = [&](int kt, auto slot_c, auto nv_c) {
+      constexpr int NV = decltype(nv_c)::value;
+      constexpr int kPer = 8 + (kSB > 0 ? 2 : 0) + NV + kAScPerWave;
+      static_for<kPer>([&](auto op_c) { issue_op(kt, slot_c, nv_c, op_c); });
     };
 
     f32x16_t acc[MAXNV][2];
@@ -306,27 +318,62 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(XArgs p) {
       acc[i][1] = f32x16_t{};
     }
 
-    // MFMAs of one stage for the first NV row blocks
-    auto compute = [&](auto slot_c, auto nv_c) {
+    // MFMAs of one stage for the first NV row blocks. The (k-step, row
+    // block) sequence is walked with the activation operands (and their MX
+    // scale words) read from LDS three steps ahead into a small register
+    // ring, so LDS latency hides behind the matrix instructions of the
+    // previous steps.
+    // The weight loads of the stage P-1 ahead (kt_next, into register slot
+    // NSL) are spread over the steps, so the memory pipeline works while the
+    // matrix cores do. (The direct-to-LDS activation loads of that stage are
+    // issued right after the barrier instead: spread among the LDS operand
+    // reads they gave run-to-run differences on gfx950.)
+    auto compute = [&](auto slot_c, auto nv_c, int kt_next, auto nslot_c) {
       constexpr int SL = decltype(slot_c)::value;
       constexpr int NV = decltype(nv_c)::value;
+      constexpr int NSTEP = kSub * NV;
+      constexpr int kB = 8 + (kSB > 0 ? 2 : 0);  // weight loads per stage
+      constexpr int D = 3;  // operand ring depth
       const uint8_t* sa = smem + SL * S::kStage;
-      if constexpr (OP == XOP_BF16) {
-#pragma unroll
-        for (int s = 0; s < kSub; ++s) {
+      const uint32_t* sasc = reinterpret_cast<const uint32_t*>(sa + S::kA);
+      using AFrag = std::conditional_t<OP == XOP_BF16, bf16x8_t, i32x8_t>;
+      AFrag afr[D];
+      uint32_t asw[D];
+      auto fetch = [&](auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        constexpr int s = ST / NV, i = ST % NV, buf = ST % D;
+        const int row = 32 * i + (lane & 31);
+        if constexpr (OP == XOP_BF16) {
+          afr[buf] = *reinterpret_cast<const bf16x8_t*>(sa + swz<128>(row, 2 * s + g));
+        } else {
+          if constexpr (OP == XOP_FP8) {
+            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz<128>(row, 4 * s + g));
+            const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sa + swz<128>(row, 4 * s + 2 + g));
+            afr[buf] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          } else {
+            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz<128>(row, 2 * s + g));
+            afr[buf] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+          }
+          asw[buf] = sasc[row * kDpr + ((2 * s + g) >> 2)];
+        }
+      };
+      static_for<(NSTEP < D - 1 ? NSTEP : D - 1)>([&](auto st_c) { fetch(st_c); });
+      static_for<NSTEP>([&](auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        constexpr int s = ST / NV, i = ST % NV, buf = ST % D;
+        if constexpr (ST + D - 1 < NSTEP) fetch(std::integral_constant<int, ST + D - 1>{});
+        static_for<(ST + 1) * kB / NSTEP - ST * kB / NSTEP>([&](auto o_c) {
+          issue_op(kt_next, nslot_c, nv_c, std::integral_constant<int, ST * kB / NSTEP + decltype(o_c)::value>{});
+        });
+        // keep the reads of step ST+D-1 and the loads ahead of the MFMAs of
+        // step ST (the scheduler would otherwise sink them next to their use)
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (OP == XOP_BF16) {
           const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, bq[SL][0][s]);
           const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, bq[SL][1][s]);
-#pragma unroll
-          for (int i = 0; i < NV; ++i) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sa + swz<128>(32 * i + (lane & 31), 2 * s + g));
-            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[i][0], 0, 0, 0);
-            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[i][1], 0, 0, 0);
-          }
-        }
-      } else {
-        const uint32_t* sasc = reinterpret_cast<const uint32_t*>(sa + S::kA);
-#pragma unroll
-        for (int s = 0; s < kSub; ++s) {
+          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], b0, acc[i][0], 0, 0, 0);
+          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], b1, acc[i][1], 0, 0, 0);
+        } else {
           i32x8_t b0, b1;
           if constexpr (OP == XOP_FP8) {
             const u32x4_t l0 = bq[SL][0][2 * s], h0 = bq[SL][0][2 * s + 1];
@@ -340,35 +387,23 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(XArgs p) {
           }
           const int bs0 = static_cast<int>((bs[SL][0] >> (8 * s)) & 0xFFu);
           const int bs1 = static_cast<int>((bs[SL][1] >> (8 * s)) & 0xFFu);
-          const int blk = 2 * s + g;  // MX block of the stage this lane group scales
-#pragma unroll
-          for (int i = 0; i < NV; ++i) {
-            const int row = 32 * i + (lane & 31);
-            i32x8_t a;
-            if constexpr (OP == XOP_FP8) {
-              const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz<128>(row, 4 * s + g));
-              const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sa + swz<128>(row, 4 * s + 2 + g));
-              a = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            } else {
-              const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz<128>(row, 2 * s + g));
-              a = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
-            }
-            const uint32_t aw = sasc[row * kDpr + (blk >> 2)];
-            const int as = static_cast<int>((aw >> (8 * (blk & 3))) & 0xFFu);
-            constexpr int fmt = OP == XOP_FP8 ? 0 : 4;
-            acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b0, acc[i][0], fmt, fmt, 0, as, 0, bs0);
-            acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b1, acc[i][1], fmt, fmt, 0, as, 0, bs1);
-          }
+          const int as = static_cast<int>((asw[buf] >> (8 * ((2 * s + g) & 3))) & 0xFFu);
+          constexpr int fmt = OP == XOP_FP8 ? 0 : 4;
+          acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[buf], b0, acc[i][0], fmt, fmt, 0, as, 0, bs0);
+          acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[buf], b1, acc[i][1], fmt, fmt, 0, as, 0, bs1);
         }
-      }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
 
     // ---- main loop: stage kt waits for its loads, frees slot (kt-1)%P by
-    // the barrier, issues stage kt+P-1 into it, then computes. Every
-    // iteration issues exactly one stage (past the end it re-issues the last
-    // stage, whose data nobody reads), so the ring has a single path through
-    // the loop and the wait count is a constant; the loop runs a multiple of
-    // P iterations and only computes the real stages ----
+    // the barrier, then computes while issuing stage kt+P-1 into that slot.
+    // Every wave computes (a wave without columns works on duplicate data
+    // it never stores) and every iteration issues exactly one stage (past
+    // the end it re-issues the last stage, whose data nobody reads), so the
+    // steady-state loop has a single path and the wait count is a constant.
+    // Whole groups of P stages run unconditionally; the last KT % P stages
+    // follow in a short tail. ----
     auto run = [&](auto nv_c) {
       constexpr int NV = decltype(nv_c)::value;
       constexpr int kPer = NV + kAScPerWave + 8 + (kSB > 0 ? 2 : 0);  // loads per stage
@@ -376,16 +411,23 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(XArgs p) {
       static_for<P - 1>([&](auto s_c) {
         issue(min(static_cast<int>(decltype(s_c)::value), KT - 1), s_c, nv_c);
       });
-      for (int k0 = 0; k0 < KT; k0 += P) {
-        static_for<P>([&](auto j_c) {
-          constexpr int J = decltype(j_c)::value;
-          const int kt = k0 + J;
-          wait_vmcnt<(P - 2) * kPer>();
-          lds_barrier();
-          issue(min(kt + P - 1, KT - 1), std::integral_constant<int, (J + P - 1) % P>{}, nv_c);
-          if (active && kt < KT) compute(j_c, nv_c);
+      auto step = [&](int kt, auto j_c) {
+        constexpr int J = decltype(j_c)::value;
+        constexpr int kB = 8 + (kSB > 0 ? 2 : 0);
+        using NSL = std::integral_constant<int, (J + P - 1) % P>;
+        const int kt_next = min(kt + P - 1, KT - 1);
+        wait_vmcnt<(P - 2) * kPer>();
+        lds_barrier();
+        static_for<NV + kAScPerWave>([&](auto o_c) {
+          issue_op(kt_next, NSL{}, nv_c, std::integral_constant<int, kB + decltype(o_c)::value>{});
         });
-      }
+        compute(j_c, nv_c, kt_next, NSL{});
+      };
+      int k0 = 0;
+      for (; k0 + P <= KT; k0 += P) static_for<P>([&](auto j_c) { step(k0 + decltype(j_c)::value, j_c); });
+      static_for<P - 1>([&](auto j_c) {
+        if (k0 + decltype(j_c)::value < KT) step(k0 + decltype(j_c)::value, j_c);
+      });
     };
     switch (min(nrb, MAXNV)) {
 #define MOE_NV(N) case N: if constexpr (N <= MAXNV) run(std::integral_constant<int, N>{}); break;
@@ -668,19 +710,19 @@ int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const
   const bool mx_out = kind != 1 && fmt != MOE_BF16;
   x.out_row_bytes = mx_out ? static_cast<int64_t>(outw) * bits / 8 : static_cast<int64_t>(outw) * 2;
   x.out_sc_row_bytes = outw / 32;
-  const dim3 grid(kNumCu), block(256);
+  constexpr int MN = 8, PP = 3, OC = 1;
+  const dim3 grid(kNumCu * OC), block(256);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, x); };
-  constexpr int MN = 8, PP = 3;
   switch (kind * 3 + xop_of(fmt)) {
-    case 0: go(expert_gemm_kernel<MN, PP, XOP_BF16, XEPI_SWIGLU, MOE_BF16>); break;
-    case 1: go(expert_gemm_kernel<MN, PP, XOP_FP8, XEPI_SWIGLU, MOE_MXFP8_E4M3>); break;
-    case 2: go(expert_gemm_kernel<MN, PP, XOP_FP4, XEPI_SWIGLU, MOE_MXFP4_E2M1>); break;
-    case 3: go(expert_gemm_kernel<MN, PP, XOP_BF16, XEPI_PLAIN, MOE_BF16>); break;
-    case 4: go(expert_gemm_kernel<MN, PP, XOP_FP8, XEPI_PLAIN, MOE_BF16>); break;
-    case 5: go(expert_gemm_kernel<MN, PP, XOP_FP4, XEPI_PLAIN, MOE_BF16>); break;
-    case 6: go(expert_gemm_kernel<MN, PP, XOP_BF16, XEPI_DSWIGLU, MOE_BF16>); break;
-    case 7: go(expert_gemm_kernel<MN, PP, XOP_FP8, XEPI_DSWIGLU, MOE_MXFP8_E4M3>); break;
-    default: go(expert_gemm_kernel<MN, PP, XOP_FP4, XEPI_DSWIGLU, MOE_MXFP4_E2M1>); break;
+    case 0: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_SWIGLU, MOE_BF16>); break;
+    case 1: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_SWIGLU, MOE_MXFP8_E4M3>); break;
+    case 2: go(expert_gemm_kernel<MN, PP, OC, XOP_FP4, XEPI_SWIGLU, MOE_MXFP4_E2M1>); break;
+    case 3: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_PLAIN, MOE_BF16>); break;
+    case 4: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_PLAIN, MOE_BF16>); break;
+    case 5: go(expert_gemm_kernel<MN, PP, OC, XOP_FP4, XEPI_PLAIN, MOE_BF16>); break;
+    case 6: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_DSWIGLU, MOE_BF16>); break;
+    case 7: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_DSWIGLU, MOE_MXFP8_E4M3>); break;
+    default: go(expert_gemm_kernel<MN, PP, OC, XOP_FP4, XEPI_DSWIGLU, MOE_MXFP4_E2M1>); break;
   }
   return check_launch("grouped expert GEMM");
 }

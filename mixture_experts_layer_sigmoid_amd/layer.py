@@ -107,6 +107,8 @@ class ExpertWeights:
             if transposed:
                 raise ValueError("transposed weight copies are built for MX formats only")
             return ExpertWeights(w1, w2)
+        if w1.dim() == 2:                     # a single (shared) expert
+            w1, w2 = w1.unsqueeze(0), w2.unsqueeze(0)
         F = w1.shape[1] // 2
         if fmt == "bf16":
             if transposed:

@@ -280,8 +280,14 @@ def test_backward_full_size_sampled(gpu_lib):
     w1 = wts["w1"][e].float().cpu().numpy()
     w2 = wts["w2"][e].float().cpu().numpy()
     dy = (ow[t, j][:, None].astype(np.float32) * dout[t]).astype(np.float32)
-    dx_e, dw1_e, dw2_e = obw.expert_backward(x[t], dy, w1, w2, cfg.fmt)
     rows = host(fw.row_map)[t, j]
+    # the forward's saved fc1 output of these rows first (isolates fc1)
+    from oracle import mlp as omlp
+    a_ref = omlp.operand(x[t], cfg.fmt) @ omlp.operand(w1, cfg.fmt).T
+    e_a = rel_l2(host(fw.act_save[torch.from_numpy(rows).cuda()]), a_ref)
+    log(f"  expert {e}: saved fc1 output rel L2 {e_a:.2e}")
+    assert e_a < 1e-4
+    dx_e, dw1_e, dw2_e = obw.expert_backward(x[t], dy, w1, w2, cfg.fmt)
     e_dx = rel_l2(host(bw.dx_perm[torch.from_numpy(rows).cuda()]), dx_e)
     e_w1 = rel_l2(host(dw1_d[e]), dw1_e)
     e_w2 = rel_l2(host(dw2_d[e]), dw2_e)

@@ -158,3 +158,36 @@ def test_shared_expert_shape(gpu_lib, name):
     _, _, ref = omlp.expert_mlp(omlp.operand(h["x"], cfg.fmt), omlp.operand(h["w1s"], cfg.fmt),
                                 omlp.operand(h["w2s"], cfg.fmt), cfg.fmt)
     assert rel_l2(y, ref) < TOL[cfg.fmt]
+
+
+@pytest.mark.parametrize("fmt,H,F,E,T,k", [
+    ("mxfp8", 2048, 256, 8, 600, 2),     # long K: 16 MX stages, at most one tile per workgroup
+    ("bf16", 2048, 256, 8, 600, 2),      # long K: 32 bf16 stages
+    ("mxfp8", 512, 512, 64, 4000, 8),    # many tiles per persistent workgroup
+    ("bf16", 512, 512, 64, 4000, 8),
+    ("mxfp4", 1024, 512, 64, 4000, 8)])
+def test_long_k_and_many_tiles(gpu_lib, fmt, H, F, E, T, k):
+    """K loops of several full pipeline groups, and more tiles than
+    workgroups (every workgroup runs tile after tile); repeated calls must
+    agree bit for bit."""
+    base = configs.get("mini_bf16")
+    cfg = configs.MoEConfig(**{**base.__dict__, "name": f"lk_{fmt}_{H}_{E}", "family": f"lk_{fmt}_{H}_{E}",
+                               "H": H, "F": F, "E": E, "T": T, "k": k, "n_group": 1, "topk_group": 1,
+                               "fmt": fmt, "F_shared": F})
+    log(f"grouped MLP {fmt} H={H} F={F} E={E} T={T} k={k}")
+    h = gen.host_inputs(cfg)
+    idx = _routing(T, E, k, 17, heavy=0)
+    _, offsets, _, src = pm.permute_maps(idx, E, 1)
+    ew = _weights_dev(cfg, h)
+    x_d = dev(h["x"], cfg.act_dtype)
+    y, save = _run(cfg, x_d, ew, offsets, src, len(src), T, act_save=True)
+    y_ref, a_ref = _oracle_rows(cfg, h, offsets, src, E)
+    # the pipeline is deterministic: repeated calls agree bit for bit
+    for _ in range(3):
+        y2, save2 = _run(cfg, x_d, ew, offsets, src, len(src), T, act_save=True)
+        assert np.array_equal(y, y2) and np.array_equal(save, save2), "run-to-run difference"
+    e_a = rel_l2(save, a_ref)
+    e_y = rel_l2(y, y_ref)
+    log(f"  saved fc1 output {e_a:.2e}, y {e_y:.2e}")
+    assert e_a < 1e-4
+    assert e_y < TOL[fmt]

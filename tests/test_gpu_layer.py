@@ -63,7 +63,7 @@ def test_single_expert_k1_is_dense_swiglu(gpu_lib):
     w2 = gen.round_to_storage(g.standard_normal((1, H, F)) / 11, "bf16")
     fw = moe.MoEForward(T=T, H=H, F=F, E=1, n_group=1, topk_group=1, k=1, routed_scale=1.0, fmt="bf16")
     out = fw(dev(x, "bf16"), dev(np.ones((1, H), np.float32), "bf16"), dev(np.zeros(1, np.float32)),
-             moe.ExpertWeights(dev(w1, "bf16"), dev(w2, "bf16")))
+             moe.ExpertWeights.from_dense(dev(w1, "bf16"), dev(w2, "bf16"), "bf16"))
     torch.cuda.synchronize()
     xt = torch.tensor(x, dtype=torch.float64)
     a = xt @ torch.tensor(w1[0], dtype=torch.float64).T
