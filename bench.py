@@ -2,6 +2,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--cpu-tokens N]
+    python bench.py --copy-calibration MIB
+
+The second form only runs a plain device-to-device copy of MIB MiB a few
+times: under rocprofv3 --pmc it gives the FETCH_SIZE / WRITE_SIZE readings
+of a known byte count, the scale for the layer kernels' readings.
 
 A step is one whole pass of the layer over one batch of synthetic inputs
 that are resident in HBM before timing starts: router GEMM + grouped top-k,
@@ -24,12 +29,17 @@ the dominant kernel of the roofline entry: its algorithmic bytes and flops
 per launch (weights of the experts that received rows read once, activation
 rows read or written once, in their storage formats) decide the bound
 (arithmetic intensity against the ridge of the format's MFMA peak over the
-8 TB/s HBM peak) and the achieved rate. The CPU baseline times the oracle
-(plain numpy) on the first --cpu-tokens tokens of the same batch.
+8 TB/s HBM peak) and the achieved rate. `traffic` is the HBM bytes per
+launch of that kernel measured with rocprofv3 counters (profiles/
+pmc_<stage>_<workload>.txt, scaled by the copy calibration), reported only
+while the kernel source is the one that was measured (its SHA-256 is
+recorded in that file), else null. The CPU baseline times the oracle (plain
+numpy) on the first --cpu-tokens tokens of the same batch.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -99,6 +109,57 @@ def roofline_entry(name, nbytes, flops, ms, fmt):
             "bytes_per_launch": nbytes, "flops_per_launch": flops, "avg_launch_ms": round(ms, 4)}
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+# source file of each stage's dominant kernel (for the traffic record)
+STAGE_SOURCE = {
+    "fc1_swiglu": "expert_gemm.hip", "fc2": "expert_gemm.hip", "shared": "expert_gemm.hip",
+    "fc2_dgrad_dswiglu": "expert_gemm.hip", "fc1_dgrad": "expert_gemm.hip",
+    "wgrad_dw1": "grouped_mlp.hip", "wgrad_dw2": "grouped_mlp.hip", "route": "route.hip",
+    "combine": "combine.hip", "combine_bwd": "backward.hip",
+}
+
+
+def source_sha(stage: str):
+    name = STAGE_SOURCE.get(stage)
+    if name is None:
+        return None
+    path = os.path.join(HERE, "mixture_experts_layer_sigmoid_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(stage: str, workload: str):
+    """HBM bytes per launch from profiles/pmc_<stage>_<workload>.txt, or None
+    when there is no record or the kernel source changed since."""
+    path = os.path.join(HERE, "profiles", f"pmc_{stage}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != source_sha(stage):
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+
+
 def _host_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -149,7 +210,11 @@ def main():
     ap.add_argument("--workload", default="dsv3_bf16_t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None)
+    ap.add_argument("--copy-calibration", type=int, default=None, metavar="MIB")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the layer runs on a single MI355X with no "
               f"collectives (asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
@@ -264,6 +329,7 @@ def main():
     peak = PEAK_TFLOPS[cfg.fmt]
     dom = max(names, key=lambda n: stage_ms[n])
     roof = roofline_entry(dom, work[dom][0], work[dom][1], stage_ms[dom], cfg.fmt)
+    roof["traffic"] = measured_traffic(dom, cfg.name)
     stages = {n: {"ms": round(stage_ms[n], 4),
                   **({"gbs": round(work[n][0] / (stage_ms[n] * 1e-3) / 1e9, 1)} if n in work else {}),
                   **({"tflops": round(work[n][1] / (stage_ms[n] * 1e-3) / 1e12, 1)}
