@@ -53,9 +53,11 @@ __device__ __forceinline__ int swz_key(int r) {
 template <int RB>
 __device__ __forceinline__ int swz(int r, int c) { return r * RB + ((c ^ swz_key<RB>(r)) << 4); }
 
+// silu(g) * u with the hardware exp2 and reciprocal (a few ulp of fp32; the
+// result is rounded to bf16 or MX right after)
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  const float sig = 1.f / (1.f + expf(-g));
-  return g * sig * u;
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * g);
+  return g * __builtin_amdgcn_rcpf(1.f + e) * u;
 }
 
 }  // namespace moe

@@ -36,41 +36,38 @@ __device__ __forceinline__ int mx_scale_exponent(float amax, uint32_t* scale_byt
   return e;
 }
 
-// E4M3 (bias 7, 3 mantissa bits, max 448, no inf) code of y.
+// E4M3 (bias 7, 3 mantissa bits, max 448, no inf) code of y, |y| < 2^9.
+// Branch-free: at or above the smallest normal 2^-6 the fp32 bits are
+// rounded to 3 mantissa bits with ties to even (a carry correctly bumps the
+// exponent), and the code is the rounded exponent/mantissa field rebased to
+// bias 7; below it the grid step is 2^-9 and the code is rint(|y| * 512),
+// which reaches 8 (= 2^-6, the first normal code) when it rounds up. Codes
+// above the largest finite value 448 (0x7E) saturate.
 __device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
-  uint32_t code;
-  if (a >= 448.f) {
-    code = 0x7Eu;
-  } else if (a < 0.015625f) {  // below the smallest normal 2^-6: grid step 2^-9
-    code = static_cast<uint32_t>(rintf(a * 512.f));
-  } else {
-    const int ex = floor_log2(a);                 // -6 .. 8
-    const float m = ldexpf(a, 3 - ex);            // [8, 16)
-    const uint32_t q = static_cast<uint32_t>(rintf(m));   // 8 .. 16
-    code = static_cast<uint32_t>((ex + 7) << 3) + (q - 8u);
-    if (code > 0x7Eu) code = 0x7Eu;
-  }
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+  const int normal = static_cast<int>(r >> 20) - ((127 - 7) << 3);
+  const uint32_t sub = static_cast<uint32_t>(rintf(__uint_as_float(a) * 512.f));
+  uint32_t code = a < 0x3C800000u ? sub : static_cast<uint32_t>(normal);  // 2^-6
+  code = code > 0x7Eu ? 0x7Eu : code;
   return sign | code;
 }
 
-// E2M1 (bias 1, 1 mantissa bit, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6) code.
+// E2M1 (bias 1, 1 mantissa bit, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6) code
+// of y, |y| < 8. Same scheme: at or above 1 the bits are rounded to one
+// mantissa bit (ties to even); below 1 the step is 0.5 and the code is
+// rint(|y| * 2) (2 = the code of 1.0); above 6 (code 7) saturates.
 __device__ __forceinline__ uint32_t e2m1_code(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 28) & 0x8u;
-  const float a = fabsf(y);
-  uint32_t code;
-  if (a >= 6.f) {
-    code = 7u;
-  } else if (a < 1.f) {  // subnormal step 0.5; rounding up to 1 gives code 2
-    code = static_cast<uint32_t>(rintf(a * 2.f));
-  } else {
-    const int ex = floor_log2(a);                 // 0 .. 2
-    const float m = ldexpf(a, 1 - ex);            // [2, 4)
-    const uint32_t q = static_cast<uint32_t>(rintf(m));   // 2 .. 4
-    code = static_cast<uint32_t>((ex + 1) << 1) + (q - 2u);
-    if (code > 7u) code = 7u;
-  }
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 28) & 0x8u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  const uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);
+  const int normal = static_cast<int>(r >> 22) - ((127 - 1) << 1);
+  const uint32_t sub = static_cast<uint32_t>(rintf(__uint_as_float(a) * 2.f));
+  uint32_t code = a < 0x3F800000u ? sub : static_cast<uint32_t>(normal);  // 1.0
+  code = code > 7u ? 7u : code;
   return sign | code;
 }
 
