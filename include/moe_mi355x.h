@@ -342,10 +342,10 @@ int64_t moe_segments_kstride(int64_t rows, int E);
  * moe_quantize_mx_segments — MX quantization of expert-major rows along the
  * rows of each expert segment (the weight-gradient operands): segment e is
  * rows [offsets[e], offsets[e+1]) (lengths multiples of 32, as moe_permute
- * with align 32 writes them); column c of segment e becomes K-major codes
- * codes[c, kofs[e] .. kofs[e] + len_e) in blocks of 32 rows, the segment
- * padded with zeros to a multiple of 128, kofs[e] the sum of the padded
- * lengths before e (written to kofs [E+1]). Values are formed in fp32:
+ * with align 32 writes them); channel c of segment e becomes the K values
+ * kofs[e] .. kofs[e] + len_e in blocks of 32 rows, the segment padded with
+ * zeros to a multiple of 128, kofs[e] the sum of the padded lengths before
+ * e (written to kofs [E+1]). Values are formed in fp32:
  * mode 0: in [rows, C], row r used as is (zero where src_row[r] < 0)
  * mode 1: in [T, C] token rows gathered through src_row (zero for -1)
  * mode 2: in [rows, 2C] = the saved fc1 output (gate | up); the value
@@ -353,9 +353,13 @@ int64_t moe_segments_kstride(int64_t rows, int E);
  * in_fmt  MOE_BF16 or MOE_F32.
  * row_scale optional [rows] fp32: row r's values are multiplied by
  *         row_scale[r] (mode 1 with moe_combine_bwd's row_w gives dY).
- * codes [C, kstride] (E4M3) or [C, kstride/2] (E2M1), scales [C, kstride/32];
- * kstride >= moe_segments_kstride(rows, E), a multiple of 128. Columns past
- * kofs[E] are not written.
+ * out_fmt MOE_MXFP8_E4M3. Stage-major layout: K is cut into stages of 128;
+ * codes [kstride/128][C][128]: stage g, channel c holds the E4M3 codes of K
+ * values [128g, 128g + 128) (one 128-channel block of a stage is 16 KB
+ * contiguous); scales [kstride/128][C][4], byte j the E8M0 scale of K block
+ * [128g + 32j, +32). kstride >= moe_segments_kstride(rows, E), a multiple
+ * of 128; stages past kofs[E] / 128 are not written. C % 8 == 0; in and
+ * codes 16-byte aligned, scales 4-byte aligned.
  */
 int moe_quantize_mx_segments(const void* in, int in_fmt, int mode,
                              const int32_t* src_row, const int32_t* offsets,
@@ -399,11 +403,13 @@ int moe_grouped_fc1_dgrad(const void* da, const uint8_t* da_scales, int fmt,
 /*
  * moe_grouped_wgrad — per expert e, dw[e] = A_e^T-contracted product over
  * the K segment [kofs[e], kofs[e+1]):  dw[e][m, n] = sum_k at[m, k] bt[n, k]
- * at [M, kstride], bt [N, kstride] MXFP8 K-major codes with scales
- * [M or N, kstride/32] (moe_quantize_mx_segments' outputs); dw [E, M, N]
- * bf16 out; an expert with an empty segment gets exact zeros.
- * Limits: fmt MOE_MXFP8_E4M3; M % 128 == 0 and N % 256 == 0, or M % 256 == 0
- * and N % 128 == 0; kstride % 128 == 0.
+ * at (M channels) and bt (N channels): MXFP8 codes and scales in the
+ * stage-major layout of moe_quantize_mx_segments (codes [kstride/128][M or
+ * N][128], scales [kstride/128][M or N][4]); kofs as that call writes it
+ * (kofs[E] <= kstride); dw [E, M, N] bf16 out; an expert with an empty
+ * segment gets exact zeros.
+ * Limits: fmt MOE_MXFP8_E4M3; M % 128 == 0, N % 128 == 0; kstride % 128 == 0;
+ * kofs[e] multiples of 128 (as moe_quantize_mx_segments writes them).
  */
 int moe_grouped_wgrad(const void* at, const uint8_t* at_scales, const void* bt,
                       const uint8_t* bt_scales, int fmt, const int32_t* kofs,

@@ -113,20 +113,16 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const void* __restrict
 
 enum { SEG_ROWS = 0, SEG_GATHER = 1, SEG_SWIGLU = 2 };
 
-// Segment-transposed MX quantization. Input rows r (expert-major, segments
-// [offsets[e], offsets[e+1]) with lengths multiple of 32) of C columns:
+// K-major MX quantization of row segments: codes[c, kofs[e] + i] for the
+// segment's rows i (blocks of 32 rows), each segment padded with zeros to a
+// multiple of `pad` columns; scales [c, kstride/32]. Input rows r
+// (segments [offsets[e], offsets[e+1])) of C columns:
 //   SEG_ROWS:   in[r, c], zero where src_row[r] < 0
 //   SEG_GATHER: in[src_row[r], c] (token rows), zero where src_row < 0
-//   SEG_SWIGLU: silu(in[r, c]) * in[r, C + c] (in is [rows, 2C]),
-//               zero where src_row[r] < 0
-// in is bf16 (IN = MOE_BF16) or fp32; with row_scale the value of row r is
-// multiplied by row_scale[r] in fp32 before encoding.
-// Output K-major: codes[c, kofs[e] + i] for the segment's rows i, each
-// segment padded with zeros to a multiple of `pad` columns; scales
-// [c, kstride/32], one per 32 columns. kofs[e] = sum over e' < e of the
-// padded lengths (written to kofs_out when given, kofs_out[E] = total).
-// offsets == nullptr means one segment [0, rows); src_row == nullptr means
-// every row is live (SEG_ROWS / SEG_SWIGLU only).
+//   SEG_SWIGLU: silu(in[r, c]) * in[r, C + c] (in is [rows, 2C])
+// with an optional fp32 row_scale[r]. offsets == nullptr means one segment
+// [0, rows); src_row == nullptr means every row is live. Used by
+// moe_quantize_mx along axis 1 (one segment, pad 32).
 template <int IN>
 __device__ __forceinline__ float ld_in(const void* in, int64_t i) {
   if (IN == MOE_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(in)[i]);
@@ -134,7 +130,7 @@ __device__ __forceinline__ float ld_in(const void* in, int64_t i) {
 }
 
 template <int MODE, bool FP4, int IN>
-__global__ __launch_bounds__(256) void quantize_segments_kernel(
+__global__ __launch_bounds__(256) void quantize_kmajor_kernel(
     const void* __restrict__ in, const int32_t* __restrict__ src_row,
     const int32_t* __restrict__ offsets, const float* __restrict__ row_scale, int E, int64_t rows,
     int C, int64_t kstride, int pad, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -222,6 +218,132 @@ __global__ __launch_bounds__(256) void quantize_segments_kernel(
   }
 }
 
+
+// Stage-major MX quantization of the weight-gradient operands. The K axis
+// (the rows of the expert segments, each padded to a multiple of 128) is cut
+// into stages of 128; stage g holds K columns [128g, 128g + 128) of every
+// channel c as 128 contiguous E4M3 bytes:
+//   codes  [kstride/128][C][128],  scales [kstride/128][C][4]
+// so one 128-channel block of one stage is a contiguous 16 KB tile (what a
+// weight-gradient tile loads per stage). A workgroup item is (stage, 64
+// channels): it reads the stage's 128 rows x 64 channels (row-contiguous),
+// forms the fp32 values in an LDS tile, encodes 4 blocks of 32 rows per
+// channel and writes 64 x 128 contiguous code bytes and 64 x 4 scale bytes.
+constexpr int kSegCols = 64;
+template <int MODE, int IN>
+__global__ __launch_bounds__(256) void quantize_stages_kernel(
+    const void* __restrict__ in, const int32_t* __restrict__ src_row,
+    const int32_t* __restrict__ offsets, const float* __restrict__ row_scale, int E, int C,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int32_t* __restrict__ kofs_out) {
+  __shared__ int32_t s_kofs[kMaxE + 1];
+  __shared__ int32_t part[256];
+  __shared__ float tile[128][kSegCols + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t ocodes[kSegCols * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t oscale[kSegCols * 4];
+  const int tid = threadIdx.x;
+  {
+    const int per = (E + 255) / 256;
+    const int lo = min(E, tid * per), hi = min(E, lo + per);
+    int s = 0;
+    for (int e = lo; e < hi; ++e) {
+      const int seg = offsets[e + 1] - offsets[e];
+      s_kofs[e + 1] = (seg + 127) / 128 * 128;
+      s += s_kofs[e + 1];
+    }
+    part[tid] = s;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const int v = tid >= d ? part[tid - d] : 0;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
+    }
+    int run = tid > 0 ? part[tid - 1] : 0;
+    for (int e = lo; e < hi; ++e) {
+      run += s_kofs[e + 1];
+      s_kofs[e + 1] = run;
+    }
+    if (tid == 0) s_kofs[0] = 0;
+    __syncthreads();
+  }
+  if (blockIdx.x == 0 && kofs_out)
+    for (int e = tid; e <= E; e += 256) kofs_out[e] = s_kofs[e];
+  const int nstage = s_kofs[E] / 128;
+  const int ncb = (C + kSegCols - 1) / kSegCols;
+  const int64_t n_items = static_cast<int64_t>(nstage) * ncb;
+  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int g = static_cast<int>(item / ncb);
+    const int c0 = static_cast<int>(item - static_cast<int64_t>(g) * ncb) * kSegCols;
+    int lo = 0, hi = E;  // the segment holding K columns [128g, 128g + 128)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_kofs[mid] <= g * 128) lo = mid;
+      else hi = mid;
+    }
+    const int local0 = g * 128 - s_kofs[lo];
+    const int seg_lo = offsets[lo];
+    const int seg = offsets[lo + 1] - seg_lo;
+    // ---- 128 rows x 64 channels -> fp32 tile; unit = (row, 8 channels) ----
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i;
+      const int r = u >> 3, c = c0 + (u & 7) * 8;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (local0 + r < seg && c < C) {
+        const int64_t row = seg_lo + local0 + r;
+        const int src = src_row[row];
+        if (src >= 0) {
+          if (MODE == SEG_SWIGLU) {
+            float gv[8], uv[8];
+            load_row8<IN>(in, row * 2 * C + c, gv);
+            load_row8<IN>(in, row * 2 * C + C + c, uv);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = gv[q] * (1.f / (1.f + expf(-gv[q]))) * uv[q];
+          } else {
+            const int64_t srow = MODE == SEG_GATHER ? src : row;
+            load_row8<IN>(in, srow * C + c, v);
+          }
+          if (row_scale) {
+            const float rs = row_scale[row];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] *= rs;
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) tile[r][(u & 7) * 8 + q] = v[q];
+    }
+    __syncthreads();
+    // ---- encode: thread -> (channel t % 64, block of 32 rows t / 64) ----
+    {
+      const int c = tid & 63, b = tid >> 6;
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = tile[32 * b + i][c];
+      uint32_t words[8];
+      const uint32_t sb = mx_encode_block<false>(v, words);
+      u32x4_t* o = reinterpret_cast<u32x4_t*>(ocodes + c * 128 + 32 * b);
+      o[0] = u32x4_t{words[0], words[1], words[2], words[3]};
+      o[1] = u32x4_t{words[4], words[5], words[6], words[7]};
+      oscale[c * 4 + b] = static_cast<uint8_t>(sb);
+    }
+    __syncthreads();
+    // ---- 64 channel rows of 128 code bytes, contiguous in the output ----
+    const int64_t obase = static_cast<int64_t>(g) * C + c0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 256 * i;  // 16-byte chunk: channel q / 8, part q % 8
+      if (c0 + (q >> 3) < C)
+        *reinterpret_cast<u32x4_t*>(codes + (obase + (q >> 3)) * 128 + (q & 7) * 16) =
+            *reinterpret_cast<const u32x4_t*>(ocodes + q * 16);
+    }
+    if (tid < kSegCols && c0 + tid < C)
+      *reinterpret_cast<uint32_t*>(scales + (obase + tid) * 4) =
+          *reinterpret_cast<const uint32_t*>(oscale + tid * 4);
+    __syncthreads();
+  }
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -275,39 +397,36 @@ extern "C" int moe_quantize_mx_segments(const void* in, int in_fmt, int mode,
                                         int64_t kstride, int out_fmt, uint8_t* codes,
                                         uint8_t* scales, int32_t* kofs, hipStream_t stream) {
   clear_error();
-  MOE_REQUIRE(E >= 1 && E <= kMaxE && C > 0 && rows >= 0, MOE_ERR_INVALID_ARG,
-              "moe_quantize_mx_segments: need 1 <= E <= 1024, C > 0, rows >= 0");
+  MOE_REQUIRE(E >= 1 && E <= kMaxE && C > 0 && C % 8 == 0 && rows >= 0, MOE_ERR_INVALID_ARG,
+              "moe_quantize_mx_segments: need 1 <= E <= 1024, C a positive multiple of 8, rows >= 0");
   MOE_REQUIRE(mode >= SEG_ROWS && mode <= SEG_SWIGLU, MOE_ERR_INVALID_ARG,
               "moe_quantize_mx_segments: mode must be 0 (rows), 1 (gather) or 2 (swiglu)");
   MOE_REQUIRE(in_fmt == MOE_BF16 || in_fmt == MOE_F32, MOE_ERR_UNSUPPORTED,
               "moe_quantize_mx_segments: in_fmt must be MOE_BF16 or MOE_F32");
-  MOE_REQUIRE(out_fmt == MOE_MXFP8_E4M3 || out_fmt == MOE_MXFP4_E2M1, MOE_ERR_UNSUPPORTED,
-              "moe_quantize_mx_segments: out_fmt must be an MX format");
+  MOE_REQUIRE(out_fmt == MOE_MXFP8_E4M3, MOE_ERR_UNSUPPORTED,
+              "moe_quantize_mx_segments: out_fmt must be MOE_MXFP8_E4M3");
   MOE_REQUIRE(kstride >= moe_segments_kstride(rows, E) && kstride % 128 == 0, MOE_ERR_INVALID_ARG,
               "moe_quantize_mx_segments: kstride below moe_segments_kstride(rows, E) or not a "
               "multiple of 128");
   MOE_REQUIRE(in && src_row && offsets && codes && scales && kofs, MOE_ERR_INVALID_ARG,
               "moe_quantize_mx_segments: null pointer");
-  MOE_REQUIRE(aligned16(codes), MOE_ERR_ALIGNMENT, "moe_quantize_mx_segments: codes not 16-byte aligned");
-  const int64_t work = (kstride / 32) * ((C + 255) / 256);
-  const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>(work, 16384)));
+  MOE_REQUIRE(aligned16(codes) && aligned16(in) && (reinterpret_cast<uintptr_t>(scales) & 3u) == 0,
+              MOE_ERR_ALIGNMENT,
+              "moe_quantize_mx_segments: in and codes must be 16-byte, scales 4-byte aligned");
+  const int64_t work = (kstride / 128) * ((C + kSegCols - 1) / kSegCols);
+  const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>(work, 1536)));
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, in, src_row, offsets, row_scale, E,
-                       rows, C, kstride, 128, codes, scales, kofs);
+                       C, codes, scales, kofs);
   };
-  auto by_mode = [&](auto fp4_c, auto in_c) {
-    constexpr bool FP4 = decltype(fp4_c)::value;
+  auto by_mode = [&](auto in_c) {
     constexpr int IN = decltype(in_c)::value;
-    if (mode == SEG_ROWS) go(quantize_segments_kernel<SEG_ROWS, FP4, IN>);
-    else if (mode == SEG_GATHER) go(quantize_segments_kernel<SEG_GATHER, FP4, IN>);
-    else go(quantize_segments_kernel<SEG_SWIGLU, FP4, IN>);
+    if (mode == SEG_ROWS) go(quantize_stages_kernel<SEG_ROWS, IN>);
+    else if (mode == SEG_GATHER) go(quantize_stages_kernel<SEG_GATHER, IN>);
+    else go(quantize_stages_kernel<SEG_SWIGLU, IN>);
   };
-  auto by_in = [&](auto fp4_c) {
-    if (in_fmt == MOE_BF16) by_mode(fp4_c, std::integral_constant<int, MOE_BF16>{});
-    else by_mode(fp4_c, std::integral_constant<int, MOE_F32>{});
-  };
-  if (out_fmt == MOE_MXFP4_E2M1) by_in(std::true_type{});
-  else by_in(std::false_type{});
+  if (in_fmt == MOE_BF16) by_mode(std::integral_constant<int, MOE_BF16>{});
+  else by_mode(std::integral_constant<int, MOE_F32>{});
   return check_launch("moe_quantize_mx_segments");
 }
 
@@ -319,11 +438,11 @@ int quantize_mx_columns(const void* in, int64_t rows, int K, int out_fmt, uint8_
   const int64_t work = (rows / 32) * ((K + 255) / 256);
   const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>(work, 16384)));
   if (out_fmt == MOE_MXFP4_E2M1)
-    hipLaunchKernelGGL((quantize_segments_kernel<SEG_ROWS, true, MOE_BF16>), dim3(grid), dim3(256), 0,
+    hipLaunchKernelGGL((quantize_kmajor_kernel<SEG_ROWS, true, MOE_BF16>), dim3(grid), dim3(256), 0,
                        stream, in, nullptr, nullptr, nullptr, 1, rows, K, rows, 32, codes, scales,
                        nullptr);
   else
-    hipLaunchKernelGGL((quantize_segments_kernel<SEG_ROWS, false, MOE_BF16>), dim3(grid), dim3(256), 0,
+    hipLaunchKernelGGL((quantize_kmajor_kernel<SEG_ROWS, false, MOE_BF16>), dim3(grid), dim3(256), 0,
                        stream, in, nullptr, nullptr, nullptr, 1, rows, K, rows, 32, codes, scales,
                        nullptr);
   return check_launch("moe_quantize_mx");

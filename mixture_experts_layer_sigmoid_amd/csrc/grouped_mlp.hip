@@ -56,12 +56,6 @@ constexpr int kMaxGroups = 1024;
 
 enum { OP_BF16 = 0, OP_FP8 = 1, OP_FP4 = 2 };
 enum { EPI_SWIGLU = 0, EPI_PLAIN = 1, EPI_DSWIGLU = 2 };
-// MODE_M: groups are row segments [offsets[e], offsets[e+1]) of A and of the
-//         output, K fixed (the forward GEMMs and the data gradients);
-// MODE_K: groups are K segments [kofs[e], kofs[e+1]) of A and B (both stored
-//         K-major), M and N fixed, one output matrix per group (the weight
-//         gradients).
-enum { MODE_M = 0, MODE_K = 1 };
 
 // Per-format constants for RB bytes of K per row per stage: MFMA k-steps per
 // stage (32x32x16 bf16 consumes 32 bytes of K per row, 32x32x64 E4M3 64
@@ -97,11 +91,6 @@ struct Args {
   int64_t out_sc_row_bytes;
   float* act_save;         // optional [rows, 2F] fp32 (fc1 only)
   int act_cols;            // 2F
-  // MODE_K
-  const int32_t* kofs;     // [E+1] K offsets (elements) of the groups
-  int m_blocks;            // row tiles of the fixed M
-  int64_t out_exp_bytes;   // bytes of one group's output matrix
-  int bits;                // bits per element of A and B
   // EPI_DSWIGLU
   const float* a_saved;    // saved fc1 output A [rows, 2F] fp32 (gate | up)
   float* da_f32;           // optional fp32 copy of dA [rows, 2F]
@@ -138,8 +127,7 @@ __device__ __forceinline__ int weight_row(int nblk, int br, int up_row) {
 // WM:     wavefront groups along the rows (4 * WM wavefronts; wave w owns
 //         column group w % 4 and row blocks w / 4, w / 4 + WM, ...)
 // OCC:    workgroups resident per CU (persistent grid = 256 * OCC)
-template <int MMAX, int STAGES, int NCB, int WM, int OCC, int RB, int OP, int EPI, int OUTF,
-          int MODE = MODE_M>
+template <int MMAX, int STAGES, int NCB, int WM, int OCC, int RB, int OP, int EPI, int OUTF>
 __global__ __launch_bounds__(256 * WM) __attribute__((amdgpu_waves_per_eu(OCC * WM, OCC * WM)))
 void grouped_gemm_kernel(Args p) {
   using S = Smem<MMAX, STAGES, NCB, OP, RB>;
@@ -171,7 +159,7 @@ void grouped_gemm_kernel(Args p) {
   const int E = p.E;
 
   // ---- tile list: m-tiles per expert, inclusive prefix in s_mt[1..E] ----
-  if constexpr (MODE == MODE_M) {
+  {
     const int per = (E + NT - 1) / NT;
     const int lo = tid * per, hi = min(E, lo + per);
     int s = 0;
@@ -201,27 +189,15 @@ void grouped_gemm_kernel(Args p) {
     }
     __syncthreads();
   }
-  // MODE_M: the tile list is cut into 8 contiguous chunks, one per XCD;
-  // MODE_K: plain grid stride, so the tiles of one group spread over every
-  // XCD (groups' K lengths are skewed; this balances the work)
-  int64_t t_first, t_end, t_step;
-  if constexpr (MODE == MODE_M) {
-    const int64_t total_tiles = static_cast<int64_t>(s_tot[0]) * p.n_blocks;
-    const XcdSlot xs = xcd_slot();
-    t_first = total_tiles * xs.xcd / kNumXcd + xs.slot;
-    t_end = total_tiles * (xs.xcd + 1) / kNumXcd;
-    t_step = xs.nslots;
-  } else {
-    t_first = blockIdx.x;
-    t_end = static_cast<int64_t>(E) * p.m_blocks * p.n_blocks;
-    t_step = gridDim.x;
-  }
+  // the tile list is cut into 8 contiguous chunks, one per XCD
+  const int64_t total_tiles = static_cast<int64_t>(s_tot[0]) * p.n_blocks;
+  const XcdSlot xs = xcd_slot();
+  const int64_t t_first = total_tiles * xs.xcd / kNumXcd + xs.slot;
+  const int64_t t_end = total_tiles * (xs.xcd + 1) / kNumXcd;
 
-  for (int64_t t = t_first; t < t_end; t += t_step) {
+  for (int64_t t = t_first; t < t_end; t += xs.nslots) {
     int e, nblk, mblk, row0, nrows, KT;
-    int64_t kbyte0 = 0;        // MODE_K: byte offset of the group's K segment
-    int64_t kscale0 = 0;       // MODE_K: its offset in the scale rows (one per 32)
-    if constexpr (MODE == MODE_M) {
+    {
       // ---- decode: expert e (s_mt[e]*nb <= t < s_mt[e+1]*nb), then column
       // block (slow) and row block (fast) inside the expert ----
       int lo = 0, hi = E;
@@ -242,18 +218,6 @@ void grouped_gemm_kernel(Args p) {
       row0 = seg_lo + mblk * MMAX;
       nrows = min(MMAX, n_e - mblk * MMAX);
       KT = p.k_stages;
-    } else {
-      const int64_t per = static_cast<int64_t>(p.m_blocks) * p.n_blocks;
-      e = static_cast<int>(t / per);
-      const int rem = static_cast<int>(t % per);
-      mblk = rem / p.n_blocks;
-      nblk = rem % p.n_blocks;
-      row0 = mblk * MMAX;
-      nrows = MMAX;
-      const int k0 = p.kofs[e], k1 = p.kofs[e + 1];
-      kbyte0 = static_cast<int64_t>(k0) * p.bits / 8;
-      kscale0 = k0 / 32;
-      KT = static_cast<int>((static_cast<int64_t>(k1 - k0) * p.bits / 8) / RB);
     }
     if (nrows <= 0) continue;  // uniform across the workgroup
     const int nrb = (nrows + 31) >> 5;
@@ -268,14 +232,14 @@ void grouped_gemm_kernel(Args p) {
         src = p.gather[src];
         if (src < 0) src = 0;  // padding row: loads any valid row, h is zeroed
       }
-      a_src[i] = p.a + static_cast<int64_t>(src) * p.a_row_bytes + kbyte0 +
+      a_src[i] = p.a + static_cast<int64_t>(src) * p.a_row_bytes +
                  (((lane % kCpr) ^ swz_key<RB>(r)) << 4);
     }
     if (p.gather && EPI == EPI_SWIGLU) {
       for (int r = tid; r < MMAX; r += NT) s_src[r] = r < nrows ? p.gather[row0 + r] : 0;
     }
     const uint8_t* b_src[kBIns];
-    const uint8_t* bexp = MODE == MODE_M ? p.b + static_cast<int64_t>(e) * p.b_exp_bytes : p.b + kbyte0;
+    const uint8_t* bexp = p.b + static_cast<int64_t>(e) * p.b_exp_bytes;
 #pragma unroll
     for (int i = 0; i < kBIns; ++i) {
       const int br = kRpi * (wave + NW * i) + lane / kCpr;
@@ -300,10 +264,9 @@ void grouped_gemm_kernel(Args p) {
           src = p.gather[src];
           if (src < 0) src = 0;
         }
-        asc_src[q] = p.a_sc + static_cast<int64_t>(src) * p.a_sc_row_bytes + kscale0 + (lane % kDpr) * 4;
+        asc_src[q] = p.a_sc + static_cast<int64_t>(src) * p.a_sc_row_bytes + (lane % kDpr) * 4;
       }
-      const uint8_t* bsexp = MODE == MODE_M ? p.b_sc + static_cast<int64_t>(e) * p.b_sc_exp_bytes
-                                            : p.b_sc + kscale0;
+      const uint8_t* bsexp = p.b_sc + static_cast<int64_t>(e) * p.b_sc_exp_bytes;
 #pragma unroll
       for (int q = 0; q < (kBScIns + NW - 1) / NW; ++q) {
         const int r = min((wave + NW * q) * kScRows + lane / kDpr, kBR - 1);
@@ -549,7 +512,7 @@ void grouped_gemm_kernel(Args p) {
         }
       }
     } else if constexpr (EPI == EPI_PLAIN) {
-      uint8_t* obase = MODE == MODE_K ? p.out + static_cast<int64_t>(e) * p.out_exp_bytes : p.out;
+      uint8_t* obase = p.out;
       for (int i = tid; i < nrows * (kBR / 8); i += NT) {
         const int row = i / (kBR / 8), c0 = (i % (kBR / 8)) * 8;
         const float* v = cs + row * kCs + c0;
@@ -699,14 +662,12 @@ __global__ __launch_bounds__(256) void fc2_f32_kernel(const float* __restrict__ 
   }
 }
 
-template <int MMAX, int STAGES, int NCB, int WM, int OCC, int RB, int OP, int EPI, int OUTF,
-          int MODE = MODE_M>
+template <int MMAX, int STAGES, int NCB, int WM, int OCC, int RB, int OP, int EPI, int OUTF>
 int launch_gemm(Args a, hipStream_t stream) {
   a.n_blocks /= NCB;
-  if (MODE == MODE_M) a.k_stages = static_cast<int>(a.a_row_bytes / RB);
-  else a.m_blocks /= MMAX / 32;  // caller passes M / 32
+  a.k_stages = static_cast<int>(a.a_row_bytes / RB);
   const int grid = kNumCu * OCC;  // persistent: OCC workgroups per CU
-  hipLaunchKernelGGL((grouped_gemm_kernel<MMAX, STAGES, NCB, WM, OCC, RB, OP, EPI, OUTF, MODE>), dim3(grid),
+  hipLaunchKernelGGL((grouped_gemm_kernel<MMAX, STAGES, NCB, WM, OCC, RB, OP, EPI, OUTF>), dim3(grid),
                      dim3(256 * WM), 0, stream, a);
   return check_launch("grouped GEMM");
 }
@@ -886,7 +847,7 @@ extern "C" int moe_grouped_mlp_fwd(const void* a, const uint8_t* a_scales, int a
 // ---------------------------------------------------------------------------
 // Backward grouped GEMMs (page "[PyTorch] DeepSeekV3Layer: full MoE
 // transformer layer (MLA + DeepSeek MoE)", Performance section, "Where the
-// time goes": dGLU bwd and wgrad of the fused grouped MLP).
+// time goes": dGLU bwd of the fused grouped MLP; its wgrad is in wgrad.hip).
 
 extern "C" int moe_grouped_fc2_dgrad_dswiglu(const void* dy, const uint8_t* dy_scales, int fmt,
                                              const void* w2t, const uint8_t* w2t_scales,
@@ -938,44 +899,4 @@ extern "C" int moe_grouped_fc1_dgrad(const void* da, const uint8_t* da_scales, i
               "moe_grouped_fc1_dgrad: tensors must be 16-byte aligned");
   if (rows == 0) return MOE_OK;
   return fc2_impl(da, da_scales, fmt, w1t, w1t_scales, offsets, E, H, 2 * F, rows, dx_perm, stream);
-}
-
-extern "C" int moe_grouped_wgrad(const void* at, const uint8_t* at_scales, const void* bt,
-                                 const uint8_t* bt_scales, int fmt, const int32_t* kofs, int E,
-                                 int M, int N, int64_t kstride, void* dw, hipStream_t stream) {
-  clear_error();
-  MOE_REQUIRE(E >= 1 && E <= kMaxGroups && M > 0 && N > 0 && kstride > 0 && kstride % 128 == 0,
-              MOE_ERR_INVALID_ARG,
-              "moe_grouped_wgrad: need 1 <= E <= 1024, M, N > 0, kstride a positive multiple of 128");
-  MOE_REQUIRE(fmt == MOE_MXFP8_E4M3, MOE_ERR_UNSUPPORTED, "moe_grouped_wgrad: fmt must be MXFP8");
-  const bool wide = M % 128 == 0 && N % 256 == 0;
-  MOE_REQUIRE(wide || (M % 256 == 0 && N % 128 == 0), MOE_ERR_INVALID_ARG,
-              "moe_grouped_wgrad: need M % 128 == 0 and N % 256 == 0, or M % 256 == 0 and N % 128 == 0");
-  MOE_REQUIRE(at && bt && at_scales && bt_scales && kofs && dw, MOE_ERR_INVALID_ARG,
-              "moe_grouped_wgrad: null pointer");
-  MOE_REQUIRE(aligned16(at) && aligned16(bt) && aligned16(dw) && scale_aligned(at_scales) &&
-                  scale_aligned(bt_scales),
-              MOE_ERR_ALIGNMENT, "moe_grouped_wgrad: tensors must be 16-byte aligned");
-  const int bits = elem_bits(fmt);
-  Args g{};
-  g.a = static_cast<const uint8_t*>(at);
-  g.a_row_bytes = kstride * bits / 8;
-  g.a_sc = at_scales;
-  g.a_sc_row_bytes = kstride / 32;
-  g.b = static_cast<const uint8_t*>(bt);
-  g.b_row_bytes = g.a_row_bytes;
-  g.b_sc = bt_scales;
-  g.b_sc_row_bytes = kstride / 32;
-  g.kofs = kofs;
-  g.bits = bits;
-  g.E = E;
-  g.rows = M;
-  g.m_blocks = M / 32;
-  g.n_blocks = N / 128;
-  g.out = static_cast<uint8_t*>(dw);
-  g.out_row_bytes = 2ll * N;
-  g.out_exp_bytes = 2ll * M * N;
-  // segments are padded to 128 elements = one 128-byte stage of E4M3
-  return wide ? launch_gemm<128, 3, 2, 2, 1, 128, OP_FP8, EPI_PLAIN, MOE_BF16, MODE_K>(g, stream)
-              : launch_gemm<256, 3, 1, 2, 1, 128, OP_FP8, EPI_PLAIN, MOE_BF16, MODE_K>(g, stream);
 }

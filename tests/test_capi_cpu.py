@@ -158,10 +158,12 @@ def test_backward_validation(lib):
     assert un(H=60) == INVALID
     assert un(of=3) == UNSUPPORTED
     qs = lambda **k: lib.moe_quantize_mx_segments(
-        A, k.get("fi", 1), k.get("mode", 0), k.get("src", A), A, None, 4, k.get("rows", 128), 64,
-        k.get("ks", 1024), k.get("fo", 2), A, A, A, None)
+        A, k.get("fi", 1), k.get("mode", 0), k.get("src", A), A, None, 4, k.get("rows", 128),
+        k.get("C", 64), k.get("ks", 1024), k.get("fo", 2), A, A, A, None)
     assert qs(mode=3) == INVALID
     assert qs(fo=1) == UNSUPPORTED
+    assert qs(fo=3) == UNSUPPORTED                # stage-major segments are E4M3 only
+    assert qs(C=60) == INVALID
     assert qs(fi=2) == UNSUPPORTED
     assert qs(ks=256) == INVALID                  # below moe_segments_kstride(128, 4)
     assert qs(src=None) == INVALID

@@ -159,7 +159,7 @@ def test_quantize_segments(gpu_lib, mode, in_fmt, scaled):
     ec, es, ekofs = _segments_expected(vals, src, offsets, E, "mxfp8")
     assert np.array_equal(host(kofs), ekofs)
     n = ekofs[-1]
-    gc, gs = host(codes)[:, :n], host(scales)[:, : n // 32]
+    gc, gs = _stage_major(host(codes), host(scales), C, ks, n)
     if mode < 2:
         assert np.array_equal(gc, ec) and np.array_equal(gs, es)
     else:
@@ -171,12 +171,24 @@ def test_quantize_segments(gpu_lib, mode, in_fmt, scaled):
         assert rel_l2(a, b) < 1e-3
 
 
-@pytest.mark.parametrize("M,N", [(256, 384), (384, 256)])
-def test_wgrad_ragged_segments(gpu_lib, M, N):
-    T, E, k = 400, 16, 4
+def _stage_major(codes, scales, C, ks, n):
+    """The segment quantizer's stage-major output ([ks/128][C][128] codes,
+    [ks/128][C][4] scales) as K-major [C, n] codes and [C, n/32] scales."""
+    c = codes.reshape(-1)[: ks * C].reshape(ks // 128, C, 128)[: n // 128]
+    s = scales.reshape(-1)[: ks * C // 32].reshape(ks // 128, C, 4)[: n // 128]
+    return (c.transpose(1, 0, 2).reshape(C, n), s.transpose(1, 0, 2).reshape(C, n // 32))
+
+
+@pytest.mark.parametrize("M,N,T", [(256, 384, 400), (384, 256, 400), (256, 384, 2400)])
+def test_wgrad_ragged_segments(gpu_lib, M, N, T):
+    # T = 2400 gives expert 0 more than 1024 rows: a segment longer than 8
+    # stages, whose tiles are split across the XCDs instead of staying whole
+    E, k = 16, 4
     log(f"grouped wgrad M={M} N={N} T={T} E={E}")
     idx, counts, offsets, row_map, src = _maps(T, E, k, 32, 9)
     assert counts[0] > 256 and (counts[-3:] == 0).all()
+    if T > 1000:
+        assert counts[0] > 1024
     bound = len(src)
     g = np.random.default_rng(10)
     A = _bf16(g.standard_normal((bound, M)))
