@@ -271,9 +271,19 @@ __global__ __launch_bounds__(256) void quantize_stages_kernel(
   const int nstage = s_kofs[E] / 128;
   const int ncb = (C + kSegCols - 1) / kSegCols;
   const int64_t n_items = static_cast<int64_t>(nstage) * ncb;
-  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+  // ---- input of one item: 128 rows x 64 channels; unit = (row, 8 channels),
+  // 4 units per thread; raw 16-byte words held in registers so the next
+  // item's loads are in flight while this one is encoded ----
+  constexpr int kW = (IN == MOE_BF16 ? 1 : 2) * (MODE == SEG_SWIGLU ? 2 : 1);
+  u32x4_t raw[4][kW];
+  float rsc[4];
+  bool ok[4];
+  int cur_g = 0, cur_c0 = 0;
+  auto load_item = [&](int64_t item) {
     const int g = static_cast<int>(item / ncb);
     const int c0 = static_cast<int>(item - static_cast<int64_t>(g) * ncb) * kSegCols;
+    cur_g = g;
+    cur_c0 = c0;
     int lo = 0, hi = E;  // the segment holding K columns [128g, 128g + 128)
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -283,37 +293,87 @@ __global__ __launch_bounds__(256) void quantize_stages_kernel(
     const int local0 = g * 128 - s_kofs[lo];
     const int seg_lo = offsets[lo];
     const int seg = offsets[lo + 1] - seg_lo;
-    // ---- 128 rows x 64 channels -> fp32 tile; unit = (row, 8 channels) ----
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = tid + 256 * i;
       const int r = u >> 3, c = c0 + (u & 7) * 8;
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      ok[i] = false;
+      rsc[i] = 1.f;
       if (local0 + r < seg && c < C) {
         const int64_t row = seg_lo + local0 + r;
         const int src = src_row[row];
         if (src >= 0) {
-          if (MODE == SEG_SWIGLU) {
-            float gv[8], uv[8];
-            load_row8<IN>(in, row * 2 * C + c, gv);
-            load_row8<IN>(in, row * 2 * C + C + c, uv);
+          ok[i] = true;
+          const int64_t srow = MODE == SEG_GATHER ? src : row;
+          const int64_t stride = MODE == SEG_SWIGLU ? 2ll * C : C;
+          const int64_t off = srow * stride + c;  // elements
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = gv[q] * (1.f / (1.f + expf(-gv[q]))) * uv[q];
-          } else {
-            const int64_t srow = MODE == SEG_GATHER ? src : row;
-            load_row8<IN>(in, srow * C + c, v);
+          for (int w = 0; w < kW; ++w) {
+            // bf16: one word of 8 values (+ the up half for SwiGLU);
+            // fp32: two words of 4 values each (x2 for SwiGLU)
+            const int half = IN == MOE_BF16 ? w : w / 2;         // 0 gate / plain, 1 up
+            const int part = IN == MOE_BF16 ? 0 : w % 2;
+            const int64_t e0 = off + (MODE == SEG_SWIGLU ? half * C : 0) + 4 * part;
+            raw[i][w] = IN == MOE_BF16
+                ? *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(in) + e0)
+                : *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(in) + e0);
           }
-          if (row_scale) {
-            const float rs = row_scale[row];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] *= rs;
-          }
+          if (row_scale) rsc[i] = row_scale[row];
         }
       }
+    }
+  };
+  auto values = [&](int i, float* v) {  // unit i's 8 fp32 values
+    float a[8], b[8];
+    auto unpack = [&](int first, float* o) {
+      if constexpr (IN == MOE_BF16) {
+        const u32x4_t q = raw[i][first];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) tile[r][(u & 7) * 8 + q] = v[q];
+        for (int t = 0; t < 4; ++t) {
+          o[2 * t] = __uint_as_float(q[t] << 16);
+          o[2 * t + 1] = __uint_as_float(q[t] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          o[t] = __uint_as_float(raw[i][first][t]);
+          o[4 + t] = __uint_as_float(raw[i][first + 1][t]);
+        }
+      }
+    };
+    if (!ok[i]) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = 0.f;
+      return;
+    }
+    unpack(0, a);
+    if constexpr (MODE == SEG_SWIGLU) {
+      unpack(IN == MOE_BF16 ? 1 : 2, b);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = a[q] * (1.f / (1.f + expf(-a[q]))) * b[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = a[q];
+    }
+    if (row_scale) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] *= rsc[i];
+    }
+  };
+  int64_t item = blockIdx.x;
+  if (item < n_items) load_item(item);
+  for (; item < n_items; item += gridDim.x) {
+    const int g = cur_g, c0 = cur_c0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i;
+      float v[8];
+      values(i, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) tile[u >> 3][(u & 7) * 8 + q] = v[q];
     }
     __syncthreads();
+    if (item + gridDim.x < n_items) load_item(item + gridDim.x);
     // ---- encode: thread -> (channel t % 64, block of 32 rows t / 64) ----
     {
       const int c = tid & 63, b = tid >> 6;
