@@ -44,14 +44,13 @@ constexpr int kMaxE = 1024;
 constexpr int kOcc = 2;        // workgroups per CU
 constexpr int kNT = 256;       // threads per workgroup
 
-// One LDS buffer: A codes [128][128] | B codes [128][128] | A scales
-// [128][4] | B scales [128][4].
-constexpr int kCodes = kTile * kRB;            // 16 KB per operand
-constexpr int kScOfs = 2 * kCodes;
-constexpr int kBuf = 2 * kCodes + 2 * kTile * 4;
+// LDS operand slots: two for A blocks, two for B blocks; a slot holds one
+// 128-row block of one stage, codes [128][128] then scales [128][4].
+constexpr int kCodes = kTile * kRB;            // 16 KB
+constexpr int kSlot = kCodes + kTile * 4;
 // schedule tables after the two buffers: segment starts [E+1] int32, then
 // the split experts and this XCD's whole experts as int16 lists
-constexpr int kSchedOfs = 2 * kBuf;
+constexpr int kSchedOfs = 4 * kSlot;
 constexpr int kSmem = kSchedOfs + (kMaxE + 1) * 4 + 2 * kMaxE * 2;
 // An expert whose segment has more than kWideKT stages is split across all
 // XCDs by dW row blocks; shorter ones go whole to one XCD. Scheduling cost
@@ -232,25 +231,25 @@ void wgrad_kernel(WArgs p) {
     ld_row[i] = r;
     ld_chunk[i] = ((lane & 7) ^ swz_key<kRB>(r)) << 4;
   }
-  // scales: wave w loads 64 rows x 4 bytes: A rows for w < 2, B rows else
+  // scales: waves 0-1 load the A block's, waves 2-3 the B block's, 64 rows
+  // x 4 bytes each
   const int sc_row = 64 * (wave & 1) + lane;
-  const bool sc_is_a = wave < 2;
 
-  // stage ks of tile t into an LDS buffer; a 128-row block of one stage is
-  // 16 KB contiguous (rows of 128 bytes). 9 loads per wave.
-  auto issue = [&](const Tile& t, int ks, uint8_t* buf) {
-    const int64_t gg = t.g + ks;
-    const uint8_t* a = p.at + (gg * p.M + t.m0) * kRB;
-    const uint8_t* b = p.bt + (gg * p.N + t.n0) * kRB;
+  // one operand block (128 channel rows of stage g) into a slot: 16 KB
+  // contiguous in the stage-major layout; 4 loads per wave (+1 scale load)
+  auto issue_block = [&](const uint8_t* codes, const uint8_t* scl, int64_t row0, bool scl_wave,
+                         uint8_t* slot) {
+    const uint8_t* c = codes + row0 * kRB;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      lds_load16(a + ld_row[i] * kRB + ld_chunk[i], buf + (wave + 4 * i) * 1024);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      lds_load16(b + ld_row[i] * kRB + ld_chunk[i], buf + kCodes + (wave + 4 * i) * 1024);
-    const uint8_t* sc = sc_is_a ? p.at_sc + (gg * p.M + t.m0 + sc_row) * 4
-                                : p.bt_sc + (gg * p.N + t.n0 + sc_row) * 4;
-    lds_load4(sc, buf + kScOfs + wave * 256);
+      lds_load16(c + ld_row[i] * kRB + ld_chunk[i], slot + (wave + 4 * i) * 1024);
+    if (scl_wave) lds_load4(scl + (row0 + sc_row) * 4, slot + kCodes + (wave & 1) * 256);
+  };
+  auto issue_a = [&](const Tile& t, int ks, uint8_t* slot) {
+    issue_block(p.at, p.at_sc, static_cast<int64_t>(t.g + ks) * p.M + t.m0, wave < 2, slot);
+  };
+  auto issue_b = [&](const Tile& t, int ks, uint8_t* slot) {
+    issue_block(p.bt, p.bt_sc, static_cast<int64_t>(t.g + ks) * p.N + t.n0, wave >= 2, slot);
   };
 
   f32x16_t acc[2][2];  // [dW row block mi][dW column block ni]
@@ -261,11 +260,9 @@ void wgrad_kernel(WArgs p) {
 
   // One stage: 2 k-steps of 64. MFMA A operand = bt rows (dW columns, the
   // accumulator's register index), B operand = at rows (dW rows, lanes).
-  auto compute = [&](const uint8_t* buf) {
-    const uint8_t* sa = buf;
-    const uint8_t* sb = buf + kCodes;
-    const uint32_t* ssa = reinterpret_cast<const uint32_t*>(buf + kScOfs);
-    const uint32_t* ssb = ssa + kTile;
+  auto compute = [&](const uint8_t* sa, const uint8_t* sb) {
+    const uint32_t* ssa = reinterpret_cast<const uint32_t*>(sa + kCodes);
+    const uint32_t* ssb = reinterpret_cast<const uint32_t*>(sb + kCodes);
     uint32_t sca[2], scb[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -303,19 +300,20 @@ void wgrad_kernel(WArgs p) {
     }
   };
 
-  // Tile output, per wave (its 64 x 64 quarter), through its own 8 KB of the
-  // LDS buffer the tile's last stage was read from. In a 32x32 block, lane l
-  // holds dW row l % 32 and, in registers 4q..4q+3, dW columns 8q + 4g +
-  // 0..3 (g = l / 32); one permlane32 swap per dword pair gives lane l < 32
-  // columns [16p, 16p + 8) and lane l + 32 columns [16p + 8, 16p + 16) of the
-  // same row, written as 16 bytes into a [64 rows][128 B] tile (16-byte
-  // chunks XOR-permuted by row % 8). Read back as whole rows, each store
-  // covers 8 rows x 128 contiguous bytes of dW.
-  auto epilogue = [&](const Tile& t, uint8_t* buf) {
-    uint8_t* stg = buf + wave * 8192;
+  // Tile output, per wave (its 64 x 64 quarter), through its own 4 KB of the
+  // B slot the tile's last stage was read from, in two rounds of 32 rows.
+  // In a 32x32 block, lane l holds dW row l % 32 and, in registers
+  // 4q..4q+3, dW columns 8q + 4g + 0..3 (g = l / 32); one permlane32 swap per
+  // dword pair gives lane l < 32 columns [16p, 16p + 8) and lane l + 32
+  // columns [16p + 8, 16p + 16) of the same row, written as 16 bytes into a
+  // [32 rows][128 B] tile (16-byte chunks XOR-permuted by row % 8). Read back
+  // as whole rows, each store covers 8 rows x 128 contiguous bytes of dW.
+  auto epilogue = [&](const Tile& t, uint8_t* slot) {
+    uint8_t* stg = slot + wave * 4096;
+    uint8_t* out = p.dw + (static_cast<int64_t>(t.e) * p.M + t.m0 + 64 * wm) * p.N * 2 +
+                   (t.n0 + 64 * wn) * 2;
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
-      const int row = 32 * mi + l32;
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
         const f32x16_t& a = acc[mi][ni];
@@ -329,43 +327,58 @@ void wgrad_kernel(WArgs p) {
           const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
           const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
           const int chunk = 4 * ni + 2 * pp + g;  // 16-byte chunk of the 128-byte row
-          ds_write16(stg + row * 128 + ((chunk ^ (row & 7)) << 4), s0[0], s1[0], s0[1], s1[1]);
+          ds_write16(stg + l32 * 128 + ((chunk ^ (l32 & 7)) << 4), s0[0], s1[0], s0[1], s1[1]);
         }
       }
-    }
-    uint8_t* out = p.dw + (static_cast<int64_t>(t.e) * p.M + t.m0 + 64 * wm) * p.N * 2 +
-                   (t.n0 + 64 * wn) * 2;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int row = 8 * it + (lane >> 3), chunk = lane & 7;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + row * 128 + ((chunk ^ (row & 7)) << 4));
-      __builtin_nontemporal_store(
-          v, reinterpret_cast<u32x4_t*>(out + static_cast<int64_t>(row) * p.N * 2 + chunk * 16));
+      for (int it = 0; it < 4; ++it) {
+        const int row = 8 * it + (lane >> 3), chunk = lane & 7;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + row * 128 + ((chunk ^ (row & 7)) << 4));
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<u32x4_t*>(out + static_cast<int64_t>(32 * mi + row) * p.N * 2 + chunk * 16));
+      }
     }
   };
 
-  // ---- the item pipeline: (tile, stage) items through two LDS buffers ----
+  // ---- the item pipeline: (tile, stage) items, B blocks through two slots,
+  // A blocks through two more, an A block that the next item shares (the
+  // next tile of a group runs on the same dW rows) staying where it is ----
   // Per wave, in issue order: loads of item i+1, then the stores of the tile
   // item i ends; waiting for item i+1's loads leaves those stores in flight.
   Tile tc = current();
   bool tn_ok = step();
   Tile tn = tc;
   if (tn_ok) tn = current();
-  int ks = 0, b = 0;
-  if (tc.kt > 0) issue(tc, 0, smem);
+  int ks = 0, sa = 0, sb = 0;           // slots of the item being computed
+  int a_e = -1, a_m0 = -1, a_g = -1;    // the A block loaded last (slot sa_last)
+  int sa_last = 0;
+  // loads of item (t, k) into B slot sb_next and, unless the last A block
+  // loaded is the same one, the other A slot; returns its A slot
+  auto issue = [&](const Tile& t, int k, int sb_next) {
+    if (t.e != a_e || t.m0 != a_m0 || t.g + k != a_g) {
+      sa_last ^= 1;
+      issue_a(t, k, smem + sa_last * kSlot);
+      a_e = t.e;
+      a_m0 = t.m0;
+      a_g = t.g + k;
+    }
+    issue_b(t, k, smem + (2 + sb_next) * kSlot);
+    return sa_last;
+  };
+  if (tc.kt > 0) sa = issue(tc, 0, 0);
   bool stored = false;  // previous item ended a tile (8 stores in flight)
   for (;;) {
     if (stored) wait_vmcnt<8>();
     else wait_vmcnt<0>();
-    lds_barrier();  // stage loads visible; the other buffer is free again
+    lds_barrier();  // the item's loads are visible; slots of item i-1 are free
     const bool same = ks + 1 < tc.kt;  // false for an empty segment
-    uint8_t* other = smem + (b ^ 1) * kBuf;
-    if (same) issue(tc, ks + 1, other);
-    else if (tn_ok && tn.kt > 0) issue(tn, 0, other);
-    if (tc.kt > 0) compute(smem + b * kBuf);
+    int sa_next = sa;
+    if (same) sa_next = issue(tc, ks + 1, sb ^ 1);
+    else if (tn_ok && tn.kt > 0) sa_next = issue(tn, 0, sb ^ 1);
+    if (tc.kt > 0) compute(smem + sa * kSlot, smem + (2 + sb) * kSlot);
     if (!same) {
-      lds_barrier();  // every wave is done reading this buffer's operands
-      epilogue(tc, smem + b * kBuf);
+      lds_barrier();  // every wave is done reading this item's B slot
+      epilogue(tc, smem + (2 + sb) * kSlot);
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -379,7 +392,8 @@ void wgrad_kernel(WArgs p) {
       ++ks;
     }
     stored = !same;
-    b ^= 1;
+    sa = sa_next;
+    sb ^= 1;
   }
 }
 

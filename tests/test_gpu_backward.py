@@ -179,10 +179,14 @@ def _stage_major(codes, scales, C, ks, n):
     return (c.transpose(1, 0, 2).reshape(C, n), s.transpose(1, 0, 2).reshape(C, n // 32))
 
 
-@pytest.mark.parametrize("M,N,T", [(256, 384, 400), (384, 256, 400), (256, 384, 2400)])
+@pytest.mark.parametrize("M,N,T", [(256, 384, 400), (384, 256, 400), (256, 384, 2400),
+                                   (1024, 2048, 400)])
 def test_wgrad_ragged_segments(gpu_lib, M, N, T):
     # T = 2400 gives expert 0 more than 1024 rows: a segment longer than 8
-    # stages, whose tiles are split across the XCDs instead of staying whole
+    # stages, whose tiles are split across the XCDs instead of staying whole.
+    # M = 1024, N = 2048: 128 tiles per expert, more than the 64 workgroups
+    # of an XCD, so a workgroup runs consecutive tiles on the same dW rows
+    # (the A block stays in LDS between them)
     E, k = 16, 4
     log(f"grouped wgrad M={M} N={N} T={T} E={E}")
     idx, counts, offsets, row_map, src = _maps(T, E, k, 32, 9)
