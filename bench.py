@@ -58,8 +58,10 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def stage_work(cfg, counts: np.ndarray, backward: bool):
-    """Algorithmic (bytes, flops) per launch of each timed stage."""
+def stage_work(cfg, counts: np.ndarray, backward: bool, kpad: int = 0):
+    """Algorithmic (bytes, flops) per launch of each timed stage. kpad: the
+    padded length of the weight-gradient contraction (the segment rows, each
+    segment padded to 128), which the stage-major operands hold."""
     T, H, F, E, k = cfg.T, cfg.H, cfg.F, cfg.E, cfg.k
     R = T * k                                   # token-expert rows
     touched = int((counts > 0).sum())
@@ -87,10 +89,12 @@ def stage_work(cfg, counts: np.ndarray, backward: bool):
         work["fc1_dgrad"] = (touched * H * 2 * F * wb + R * 2 * F * qb + R * H * 2,
                              2.0 * R * 2 * F * H)
         work["unpermute"] = (R * H * 2 + T * H * 2, 0.0)
-        work["wgrad_dw2"] = (R * H * ab + R * 2 * F * 4 + R * (H + F) * qb * 2
-                             + E * H * F * 2, 2.0 * R * H * F)
-        work["wgrad_dw1"] = (R * 2 * F * 4 + R * H * ab + R * (2 * F + H) * qb * 2
-                             + E * 2 * F * H * 2, 2.0 * R * 2 * F * H)
+        op2 = kpad * (H + F) * 33 // 32           # E4M3 codes + E8M0 scales
+        op1 = kpad * (2 * F + H) * 33 // 32
+        work["operands_dw2"] = (R * H * ab + R * 2 * F * 4 + op2, 0.0)
+        work["wgrad_dw2"] = (op2 + E * H * F * 2, 2.0 * R * H * F)
+        work["operands_dw1"] = (R * 2 * F * 4 + R * H * ab + op1, 0.0)
+        work["wgrad_dw1"] = (op1 + E * 2 * F * H * 2, 2.0 * R * 2 * F * H)
     return work
 
 
@@ -114,7 +118,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 STAGE_SOURCE = {
     "fc1_swiglu": "expert_gemm.hip", "fc2": "expert_gemm.hip", "shared": "expert_gemm.hip",
     "fc2_dgrad_dswiglu": "expert_gemm.hip", "fc1_dgrad": "expert_gemm.hip",
-    "wgrad_dw1": "grouped_mlp.hip", "wgrad_dw2": "grouped_mlp.hip", "route": "route.hip",
+    "wgrad_dw1": "wgrad.hip", "wgrad_dw2": "wgrad.hip", "route": "route.hip",
+    "operands_dw1": "backward.hip", "operands_dw2": "backward.hip",
     "combine": "combine.hip", "combine_bwd": "backward.hip",
 }
 
@@ -255,8 +260,8 @@ def main():
 
     names = ["route", "quantize_x", "permute", "fc1_swiglu", "fc2", "shared", "combine"]
     if backward:
-        names += ["combine_bwd", "fc2_dgrad_dswiglu", "fc1_dgrad", "unpermute", "wgrad_dw2",
-                  "wgrad_dw1"]
+        names += ["combine_bwd", "fc2_dgrad_dswiglu", "fc1_dgrad", "unpermute", "operands_dw2",
+                  "wgrad_dw2", "operands_dw1", "wgrad_dw1"]
     if not moe.layer.is_mx(cfg.fmt):
         names.remove("quantize_x")
     if not cfg.n_shared:
@@ -291,10 +296,14 @@ def main():
         elif name == "unpermute":
             moe.moe_unpermute(bw.dx_perm, moe.MOE_BF16, fw.row_map, fw.T, fw.k, fw.H, bw.dx,
                               moe.MOE_BF16)
+        elif name == "operands_dw2":
+            bw.operands_dw2(dout_d)
         elif name == "wgrad_dw2":
-            bw.weight_grad_dw2(dout_d)
+            bw.gemm_dw2()
+        elif name == "operands_dw1":
+            bw.operands_dw1(x_d)
         elif name == "wgrad_dw1":
-            bw.weight_grad_dw1(x_d)
+            bw.gemm_dw1()
 
     def step(evs=None):
         for i, n in enumerate(names):
@@ -321,7 +330,8 @@ def main():
                                   for s in range(args.steps)])) for i, n in enumerate(names)}
     ms_per_step = elapsed * 1e3 / args.steps
     counts = fw.counts.cpu().numpy()
-    work = stage_work(cfg, counts, backward)
+    kpad = int(bw.kofs[-1].item()) if backward else 0
+    work = stage_work(cfg, counts, backward, kpad)
 
     tokens_per_s = cfg.T * args.steps / elapsed
     flops = cfg.flops_forward() + (cfg.flops_backward() if backward else 0.0)

@@ -62,6 +62,10 @@ constexpr int kStageBytes = 128;        // bytes of K per row per stage
 constexpr int kChunk = 4096;            // packed bytes per (column block, stage)
 constexpr int kTileCols = 256;          // weight rows per tile (8 column blocks)
 constexpr int kCs = kTileCols + 4;      // padded fp32 row stride of the epilogue tile
+// Scheduling cost of a tile = kTileCost + its rows: streaming a tile's
+// weights takes about as long as the matrix work of ~220 rows at the
+// chip's byte-to-flop ratio (the same for bf16, E4M3 and E2M1 tiles).
+constexpr int kTileCost = 220;
 
 enum { XOP_BF16 = 0, XOP_FP8 = 1, XOP_FP4 = 2 };
 enum { XEPI_SWIGLU = 0, XEPI_PLAIN = 1, XEPI_DSWIGLU = 2 };
@@ -116,7 +120,7 @@ struct XSmem {
   static constexpr int kRing = P * kStage;
   static constexpr int kEpi = (kRows < kPassRows ? kRows : kPassRows) * kCs * 4;
   static constexpr int kBody = kRing > kEpi ? kRing : kEpi;
-  static constexpr int kSched = (kMaxGroups + 2) * 4 + kRows * 4;
+  static constexpr int kSched = (kMaxGroups + 2) * 4 + kRows * 4 + (kMaxGroups + 1) * 4;
   static constexpr int kTotal = kBody + kSched;
 };
 
@@ -159,6 +163,7 @@ void expert_gemm_kernel(XArgs p) {
   int32_t* s_mt = reinterpret_cast<int32_t*>(smem + S::kBody);   // [E+1] row-tile prefix
   int32_t* s_src = s_mt + (kMaxGroups + 1);                       // [kRows] source rows
   int32_t* s_tot = s_src + kRows;
+  int32_t* s_cost = s_tot + 1;                                    // [E+1] cost prefix
   int32_t* part = reinterpret_cast<int32_t*>(smem);  // scan scratch (before any load)
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -196,11 +201,55 @@ void expert_gemm_kernel(XArgs p) {
       s_tot[0] = part[255];
     }
     __syncthreads();
+    // cost of an expert's tiles per column tile: every row tile streams the
+    // same weight bytes (kTileCost, in the matrix time of that many rows)
+    // and does matrix work in proportion to its rows
+    int c = 0;
+    for (int e = lo; e < hi; ++e) {
+      int n_e = min(p.offsets[e + 1], (int)p.rows) - p.offsets[e];
+      n_e = n_e < 0 ? 0 : n_e;
+      s_cost[e + 1] = (s_mt[e + 1] - s_mt[e]) * kTileCost + n_e;
+      c += s_cost[e + 1];
+    }
+    part[tid] = c;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const int v = tid >= d ? part[tid - d] : 0;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
+    }
+    run = tid > 0 ? part[tid - 1] : 0;
+    for (int e = lo; e < hi; ++e) {
+      run += s_cost[e + 1];
+      s_cost[e + 1] = run;
+    }
+    if (tid == 0) s_cost[0] = 0;
+    __syncthreads();
   }
+  // XCD x runs the tiles between the points where the running cost reaches
+  // x/8 and (x+1)/8 of the total (inside an expert, its tiles are taken as
+  // equally costly): a skewed routing's long segments, whose row tiles do
+  // most of the matrix work, do not pile up on one XCD
   const int64_t total_tiles = static_cast<int64_t>(s_tot[0]) * p.n_tiles;
   const XcdSlot xs = xcd_slot();
-  const int64_t t_first = total_tiles * xs.xcd / kNumXcd + xs.slot;
-  const int64_t t_end = total_tiles * (xs.xcd + 1) / kNumXcd;
+  auto boundary = [&](int x) -> int64_t {
+    if (x == 0) return 0;
+    if (x == kNumXcd) return total_tiles;
+    const int64_t target = static_cast<int64_t>(s_cost[E]) * x / kNumXcd;
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_cost[mid] <= target) lo = mid;
+      else hi = mid;
+    }
+    const int64_t ce = s_cost[lo + 1] - s_cost[lo];
+    const int64_t tiles_e = static_cast<int64_t>(s_mt[lo + 1] - s_mt[lo]) * p.n_tiles;
+    const int64_t within = ce > 0 ? (target - s_cost[lo]) * tiles_e / ce : 0;
+    return static_cast<int64_t>(s_mt[lo]) * p.n_tiles + within;
+  };
+  const int64_t t_first = boundary(xs.xcd) + xs.slot;
+  const int64_t t_end = boundary(xs.xcd + 1);
 
   for (int64_t t = t_first; t < t_end; t += xs.nslots) {
     // ---- decode: expert, then column tile (slow) and row tile (fast) ----

@@ -298,23 +298,39 @@ class MoEBackward:
                                    fw.bound, C, self.kstride, FMT["mxfp8"], codes, scales,
                                    self.kofs, stream)
 
-    def weight_grad_dw2(self, dout, stream=None):
-        """dW2 = dY^T h per expert, contracting over the expert's rows (MX
-        blocks of 32 rows of the segment): dY rows formed as w * dout, h
-        recomputed from the saved fc1 output."""
+    def operands_dw2(self, dout, stream=None):
+        """The dW2 operands in the stage-major segment layout: dY rows formed
+        as w * dout, h recomputed from the saved fc1 output, both MX
+        quantized along the rows of each expert segment."""
         fw = self.fwd
         self._seg(dout, fw.act_fmt, 1, self.row_w, fw.H, self.dyT, self.dyT_sc, stream)
         self._seg(fw.act_save, L.MOE_F32, 2, None, fw.F, self.hT, self.hT_sc, stream)
+
+    def gemm_dw2(self, stream=None):
+        """dW2 = dY^T h per expert, contracting over the expert's rows."""
+        fw = self.fwd
         L.moe_grouped_wgrad(self.dyT, self.dyT_sc, self.hT, self.hT_sc, FMT["mxfp8"], self.kofs,
                             fw.E, fw.H, fw.F, self.kstride, self.dw2, stream)
 
-    def weight_grad_dw1(self, x, stream=None):
-        """dW1 = dA^T x per expert, contracting over the expert's rows."""
+    def operands_dw1(self, x, stream=None):
+        """The dW1 operands: dA (its fp32 copy) and the token rows x."""
         fw = self.fwd
         self._seg(self.da_f32, L.MOE_F32, 0, None, 2 * fw.F, self.daT, self.daT_sc, stream)
         self._seg(x, fw.act_fmt, 1, None, fw.H, self.xT, self.xT_sc, stream)
+
+    def gemm_dw1(self, stream=None):
+        """dW1 = dA^T x per expert, contracting over the expert's rows."""
+        fw = self.fwd
         L.moe_grouped_wgrad(self.daT, self.daT_sc, self.xT, self.xT_sc, FMT["mxfp8"], self.kofs,
                             fw.E, 2 * fw.F, fw.H, self.kstride, self.dw1, stream)
+
+    def weight_grad_dw2(self, dout, stream=None):
+        self.operands_dw2(dout, stream)
+        self.gemm_dw2(stream)
+
+    def weight_grad_dw1(self, x, stream=None):
+        self.operands_dw1(x, stream)
+        self.gemm_dw1(stream)
 
     def weight_grad(self, dout, x, stream=None):
         self.weight_grad_dw2(dout, stream)
