@@ -11,11 +11,14 @@
 // in fp64 and rounded once to fp32.
 //
 // Layout of the work, two kernels:
-//  * router GEMM: logits = x . W_r^T over tiles of 64 tokens x 64 experts,
-//    optionally split along H into S chunks so that small token counts still
-//    spread over the chip; partial sums go to a workspace [S, T, E] fp32.
-//    bf16: MFMA 16x16x32 with each wave owning 16 tokens and the tile's 64
-//    experts; fp32: plain FMA.
+//  * router GEMM: logits = x . W_r^T, split along H into S chunks so the
+//    launch has a few hundred workgroups whatever T; partial sums go to a
+//    workspace [S, T, E] fp32. bf16 with H % 64 == 0: tiles of 64 tokens x
+//    256 experts, both operands staged through two LDS buffers of 64 K
+//    values (direct global->LDS loads, XOR-swizzled rows), each wave owning
+//    64 tokens x 64 experts as 2 x 2 blocks of 32x32x16 bf16 MFMAs; other
+//    bf16 shapes: MFMA 16x16x32 straight from global memory; fp32: plain
+//    FMA.
 //  * selection: one wavefront per token sums the S partials in chunk order
 //    and spreads the E scores over the 64 lanes (expert e on lane e % 64);
 //    every argmax is a 64-lane max-reduction of a 64-bit key
@@ -23,6 +26,7 @@
 //    in the low word, which turns "ties to the lower index" into a plain
 //    max).
 #include "common.h"
+#include "gemm_util.h"
 
 #include <algorithm>
 #include <cmath>
@@ -118,6 +122,103 @@ __global__ __launch_bounds__(kThreads) void router_gemm_kernel(const void* __res
       for (int h = k0; h < k1; ++h) acc = fmaf(xp[h], wp[h], acc);
       out[static_cast<int64_t>(t) * E + e] = acc;
     }
+  }
+}
+
+// Partial logits over H chunk [k0, k1) (a multiple of 64) for a tile of 64
+// tokens x 256 experts: part[s, t, e] = sum_{h in chunk} x[t, h] * w[e, h].
+// Rows past T or E load the last valid row and are not stored.
+constexpr int kRtTok = 64, kRtExp = 256, kRtK = 64;   // tile and stage (bf16 values)
+constexpr int kRtRowB = kRtK * 2;                     // bytes per row per stage
+constexpr int kRtStage = (kRtTok + kRtExp) * kRtRowB;  // 40 KB
+__global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ wr,
+                                                               int T, int H, int E, int chunk,
+                                                               int S, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kRtStage];
+  const int ne = (E + kRtExp - 1) / kRtExp;
+  int b = blockIdx.x;
+  const int s = b % S;
+  b /= S;
+  const int t0 = (b / ne) * kRtTok, e0 = (b % ne) * kRtExp;
+  const int k0 = s * chunk, k1 = min(H, k0 + chunk);
+  const int KT = (k1 - k0) / kRtK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  // loads: instruction q covers 8 rows x 128 bytes; rows 0..63 are tokens
+  // (q = 0..7), 64..319 experts (q = 8..39); wave w issues q = w + 4i
+  const uint16_t* src[10];
+  int dst[10];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const int q = wave + 4 * i;
+    const int r = 8 * q + (lane >> 3);
+    const int chunk16 = (lane & 7) ^ swz_key<128>(r);
+    const uint16_t* row = r < kRtTok ? x + static_cast<int64_t>(min(t0 + r, T - 1)) * H
+                                     : wr + static_cast<int64_t>(min(e0 + r - kRtTok, E - 1)) * H;
+    src[i] = row + k0 + chunk16 * 8;
+    dst[i] = q * 1024;
+  }
+  auto issue = [&](int kt) {
+    uint8_t* st = smem + (kt & 1) * kRtStage;
+#pragma unroll
+    for (int i = 0; i < 10; ++i) lds_load16(src[i] + kt * kRtK, st + dst[i]);
+  };
+  f32x16_t acc[2][2];  // [token block][expert block]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+  issue(0);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT) {
+      issue(kt + 1);
+      wait_vmcnt<10>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    const uint8_t* st = smem + (kt & 1) * kRtStage;
+#pragma unroll
+    for (int ks = 0; ks < kRtK / 16; ++ks) {
+      bf16x8_t a[2], w[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = *reinterpret_cast<const bf16x8_t*>(st + swz<128>(32 * i + (lane & 31), 2 * ks + g));
+        const int er = kRtTok + 64 * wave + 32 * i + (lane & 31);
+        w[i] = *reinterpret_cast<const bf16x8_t*>(st + swz<128>(er, 2 * ks + g));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[j], a[i], acc[i][j], 0, 0, 0);
+    }
+    lds_barrier();  // the buffer is reloaded by the next iteration's issue
+  }
+  // accumulator of block (i, j): lane l holds token 32 i + l % 32 and, in
+  // element r, expert 64 wave + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4
+  float* out = part + static_cast<int64_t>(s) * T * E;
+  const int t = t0 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (t + 32 * i >= T) continue;
+    float* orow = out + static_cast<int64_t>(t + 32 * i) * E;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = e0 + 64 * wave + 32 * j + 8 * q + 4 * g;
+        if (e + 3 < E && (E & 3) == 0) {
+          *reinterpret_cast<f32x4_t*>(orow + e) =
+              f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (e + r < E) orow[e + r] = acc[i][j][4 * q + r];
+        }
+      }
   }
 }
 
@@ -218,8 +319,13 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 struct Split {
   int S, chunk;
 };
-Split router_split(int T, int H, int E) {
-  const int64_t tiles = static_cast<int64_t>((T + kTile - 1) / kTile) * ((E + kTile - 1) / kTile);
+bool router_mfma_path(int x_fmt, int H) { return x_fmt == MOE_BF16 && H % kRtK == 0; }
+
+Split router_split(int T, int H, int E, bool mfma) {
+  const int64_t tiles =
+      mfma ? static_cast<int64_t>((T + kRtTok - 1) / kRtTok) * ((E + kRtExp - 1) / kRtExp)
+           : static_cast<int64_t>((T + kTile - 1) / kTile) * ((E + kTile - 1) / kTile);
+  const int align = mfma ? kRtK : 32;
   int S = 1;
   if (tiles < kTargetWgs) {
     const int64_t want = (kTargetWgs + tiles - 1) / tiles;
@@ -227,7 +333,7 @@ Split router_split(int T, int H, int E) {
     S = static_cast<int>(std::min<int64_t>(want, most));
   }
   int chunk = (H + S - 1) / S;
-  chunk = (chunk + 31) / 32 * 32;
+  chunk = (chunk + align - 1) / align * align;
   S = (H + chunk - 1) / chunk;
   return {S, chunk};
 }
@@ -239,7 +345,9 @@ using namespace moe;
 
 extern "C" size_t moe_route_workspace(int T, int H, int E) {
   if (T <= 0 || H <= 0 || E <= 0) return 0;
-  const Split sp = router_split(T, H, E);
+  // the larger of the two paths' needs (the x format is not an argument)
+  const Split a = router_split(T, H, E, H % kRtK == 0), b = router_split(T, H, E, false);
+  const Split sp = a.S > b.S ? a : b;
   return static_cast<size_t>(sp.S) * T * E * sizeof(float);
 }
 
@@ -280,13 +388,23 @@ extern "C" int moe_route(const void* x, int x_fmt, const void* w_router, const f
                        n_group, topk_group, k, routed_scale, logits_out, topk_idx, topk_w);
     return check_launch("moe_route");
   }
-  const Split sp = router_split(T, H, E);
+  const bool mfma = router_mfma_path(x_fmt, H);
+  const Split sp = router_split(T, H, E, mfma);
   const size_t need = static_cast<size_t>(sp.S) * T * E * sizeof(float);
   MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE,
               "moe_route: workspace smaller than moe_route_workspace(T, H, E)");
+  float* part = static_cast<float*>(ws);
+  if (mfma) {
+    const int tiles = ((T + kRtTok - 1) / kRtTok) * ((E + kRtExp - 1) / kRtExp);
+    hipLaunchKernelGGL(router_mfma_kernel, dim3(static_cast<unsigned>(tiles * sp.S)), block, 0,
+                       stream, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(w_router), T, H, E, sp.chunk, sp.S, part);
+    hipLaunchKernelGGL(select_kernel, sel_grid, block, 0, stream, part, sp.S, bias, T, E, n_group,
+                       topk_group, k, routed_scale, logits_out, topk_idx, topk_w);
+    return check_launch("moe_route");
+  }
   const int tiles = ((T + kTile - 1) / kTile) * ((E + kTile - 1) / kTile);
   const dim3 grid(static_cast<unsigned>(tiles * sp.S));
-  float* part = static_cast<float*>(ws);
   if (x_fmt == MOE_BF16)
     hipLaunchKernelGGL(router_gemm_kernel<MOE_BF16>, grid, block, 0, stream, x, w_router, T, H, E,
                        sp.chunk, sp.S, part);
