@@ -292,7 +292,7 @@ int moe_grouped_fc2(const void* h, const uint8_t* h_scales, int h_fmt,
  *   out[t] = sum_{j<k} topk_w[t, j] * y[row_map[t, j]]  (+ shared[t])
  * accumulated in fp32 in slot order j = 0..k-1.
  * y [rows, H] in y_fmt (MOE_F32 or MOE_BF16); shared optional [T, H] in
- * y_fmt; out [T, H] in out_fmt (MOE_F32 or MOE_BF16). H % 8 == 0.
+ * y_fmt; out [T, H] in out_fmt (MOE_F32 or MOE_BF16). H % 8 == 0, k <= 16.
  */
 int moe_combine(const void* y, int y_fmt, const int32_t* row_map,
                 const float* topk_w, const void* shared, int T, int k, int H,

@@ -35,6 +35,8 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float* v) {
   }
 }
 
+constexpr int kMaxK = 16;  // moe_route's limit on k
+
 template <int YF, int OF>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
                                                       const int32_t* __restrict__ row_map,
@@ -43,18 +45,50 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       int H, void* __restrict__ out) {
   const int t = blockIdx.x;
   const int nvec = H / 8;
+  // the token's k rows and weights (uniform across the workgroup)
+  int64_t rows[kMaxK];
+  float wts[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    rows[j] = j < k ? static_cast<int64_t>(row_map[static_cast<int64_t>(t) * k + j]) * H : 0;
+    wts[j] = j < k ? (w ? w[static_cast<int64_t>(t) * k + j] : 1.f) : 0.f;
+  }
+  constexpr int kWords = YF == MOE_BF16 ? 1 : 2;  // 16-byte words per 8 values
   for (int c = threadIdx.x; c < nvec; c += 256) {
+    // all k loads in flight before the first product
+    u32x4_t raw[kMaxK][kWords];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k) {
+#pragma unroll
+        for (int q = 0; q < kWords; ++q)
+          raw[j][q] = YF == MOE_BF16
+              ? *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(y) + rows[j] + c * 8)
+              : reinterpret_cast<const u32x4_t*>(static_cast<const float*>(y) + rows[j] + c * 8)[q];
+      }
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const float wj = w ? w[static_cast<int64_t>(t) * k + j] : 1.f;
-      const int64_t row = row_map[static_cast<int64_t>(t) * k + j];
-      float v[8];
-      load8<YF>(y, row * H + c * 8, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
-    }
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k) {
+        float v[8];
+        if (YF == MOE_BF16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(raw[j][0][i] << 16);
+            v[2 * i + 1] = __uint_as_float(raw[j][0][i] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[i] = __uint_as_float(raw[j][0][i]);
+            v[4 + i] = __uint_as_float(raw[j][kWords - 1][i]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wts[j], v[i], acc[i]);
+      }
     if (shared) {
       float v[8];
       load8<YF>(shared, static_cast<int64_t>(t) * H + c * 8, v);
@@ -83,8 +117,8 @@ extern "C" int moe_combine(const void* y, int y_fmt, const int32_t* row_map, con
                            const void* shared, int T, int k, int H, void* out, int out_fmt,
                            hipStream_t stream) {
   clear_error();
-  MOE_REQUIRE(T >= 0 && k >= 1 && H > 0 && H % 8 == 0, MOE_ERR_INVALID_ARG,
-              "moe_combine: need T >= 0, k >= 1, H a positive multiple of 8");
+  MOE_REQUIRE(T >= 0 && k >= 1 && k <= kMaxK && H > 0 && H % 8 == 0, MOE_ERR_INVALID_ARG,
+              "moe_combine: need T >= 0, 1 <= k <= 16, H a positive multiple of 8");
   MOE_REQUIRE((y_fmt == MOE_F32 || y_fmt == MOE_BF16) && (out_fmt == MOE_F32 || out_fmt == MOE_BF16),
               MOE_ERR_UNSUPPORTED, "moe_combine: formats must be MOE_F32 or MOE_BF16");
   if (T == 0) return MOE_OK;

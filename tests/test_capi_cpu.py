@@ -125,9 +125,10 @@ def test_grouped_mlp_validation(lib):
 
 
 def test_combine_validation(lib):
-    c = lambda **k: lib.moe_combine(A, k.get("yf", 1), A, A, None, k.get("T", 4), 2, k.get("H", 64),
-                                    k.get("out", A), k.get("of", 1), None)
+    c = lambda **k: lib.moe_combine(A, k.get("yf", 1), A, A, None, k.get("T", 4), k.get("k", 2),
+                                    k.get("H", 64), k.get("out", A), k.get("of", 1), None)
     assert c(H=60) == INVALID
+    assert c(k=17) == INVALID
     assert c(yf=2) == UNSUPPORTED
     assert c(out=A + 4) == ALIGN
     assert c(T=0) == OK
