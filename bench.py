@@ -58,10 +58,11 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def stage_work(cfg, counts: np.ndarray, backward: bool, kpad: int = 0):
+def stage_work(cfg, counts: np.ndarray, backward: bool, kpad: int = 0, fused_shared: bool = False):
     """Algorithmic (bytes, flops) per launch of each timed stage. kpad: the
     padded length of the weight-gradient contraction (the segment rows, each
-    segment padded to 128), which the stage-major operands hold."""
+    segment padded to 128), which the stage-major operands hold.
+    fused_shared: the shared expert runs inside the fc1 / fc2 launches."""
     T, H, F, E, k = cfg.T, cfg.H, cfg.F, cfg.E, cfg.k
     R = T * k                                   # token-expert rows
     touched = int((counts > 0).sum())
@@ -77,7 +78,14 @@ def stage_work(cfg, counts: np.ndarray, backward: bool, kpad: int = 0):
     work["fc1_swiglu"] = (touched * 2 * F * H * wb + T * H * qb + R * F * qb + save,
                           2.0 * R * H * 2 * F)
     work["fc2"] = (touched * H * F * wb + R * F * qb + R * H * ab, 2.0 * R * F * H)
-    if cfg.n_shared:
+    if cfg.n_shared and fused_shared:
+        # x rows are read once for both; the shared h goes through HBM
+        Fs = cfg.F_shared
+        b1, f1 = work["fc1_swiglu"]
+        work["fc1_swiglu"] = (b1 + 2 * Fs * H * wb + T * Fs * qb, f1 + 2.0 * T * H * 2 * Fs)
+        b2, f2 = work["fc2"]
+        work["fc2"] = (b2 + H * Fs * wb + T * Fs * qb + T * H * ab, f2 + 2.0 * T * Fs * H)
+    elif cfg.n_shared:
         Fs = cfg.F_shared
         work["shared"] = (2 * Fs * H * wb + H * Fs * wb + T * H * qb + T * H * ab,
                           2.0 * T * H * 2 * Fs + 2.0 * T * Fs * H)
@@ -264,8 +272,8 @@ def main():
                   "wgrad_dw2", "operands_dw1", "wgrad_dw1"]
     if not moe.layer.is_mx(cfg.fmt):
         names.remove("quantize_x")
-    if not cfg.n_shared:
-        names.remove("shared")
+    if not cfg.n_shared or fw.fuse_shared:
+        names.remove("shared")      # none, or inside fc1_swiglu / fc2
     f8 = moe.FMT["mxfp8"]
 
     def run_stage(name):
@@ -276,9 +284,9 @@ def main():
         elif name == "permute":
             fw.permute()
         elif name == "fc1_swiglu":
-            fw.experts_fc1(x_d, ew)
+            fw.experts_fc1(x_d, ew, sw=sw)
         elif name == "fc2":
-            fw.experts_fc2(ew)
+            fw.experts_fc2(ew, sw=sw)
         elif name == "shared":
             fw.shared(x_d, sw)
         elif name == "combine":
@@ -331,7 +339,7 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     counts = fw.counts.cpu().numpy()
     kpad = int(bw.kofs[-1].item()) if backward else 0
-    work = stage_work(cfg, counts, backward, kpad)
+    work = stage_work(cfg, counts, backward, kpad, fused_shared=fw.fuse_shared)
 
     tokens_per_s = cfg.T * args.steps / elapsed
     flops = cfg.flops_forward() + (cfg.flops_backward() if backward else 0.0)

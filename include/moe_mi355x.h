@@ -286,6 +286,35 @@ int moe_grouped_fc2(const void* h, const uint8_t* h_scales, int h_fmt,
                     void* y, int y_fmt, hipStream_t stream);
 
 /*
+ * moe_grouped_fc1_swiglu_dense / moe_grouped_fc2_dense — the routed grouped
+ * fc1 (resp. fc2) and the layer's always-on shared expert (TE DeepSeekV3Layer
+ * page, Description: optional shared expert) in one launch. The shared
+ * expert takes all T token rows and has the routed experts' format and
+ * shape (F_shared == F); its weights w1d [2F, H] (gate rows then up rows) /
+ * w2d [H, F], packed by moe_pack_weights like one routed expert (w1d with
+ * half = F). Arguments as moe_grouped_fc1_swiglu / moe_grouped_fc2, except:
+ * fc1: h (+ h_scales) has rows + T rows; row rows + t holds the shared
+ *      expert's h of token t, computed from row t of `a` (no gather);
+ *      act_save covers the routed rows only.
+ * fc2: h and y have rows + T rows; rows [rows, rows + T) are the shared
+ *      expert's input and output.
+ * Not for fp32 layers (MOE_ERR_UNSUPPORTED). The shared expert's tiles are
+ * spread through the routed experts' tile list.
+ */
+int moe_grouped_fc1_swiglu_dense(const void* a, const uint8_t* a_scales, int a_fmt,
+                                 const int32_t* src_row, const void* w1,
+                                 const uint8_t* w1_scales, int w_fmt,
+                                 const int32_t* offsets, int E, int H, int F,
+                                 int64_t rows, float* act_save, void* h,
+                                 uint8_t* h_scales, const void* w1d,
+                                 const uint8_t* w1d_scales, int T, hipStream_t stream);
+int moe_grouped_fc2_dense(const void* h, const uint8_t* h_scales, int h_fmt,
+                          const void* w2, const uint8_t* w2_scales, int w_fmt,
+                          const int32_t* offsets, int E, int H, int F, int64_t rows,
+                          void* y, int y_fmt, const void* w2d,
+                          const uint8_t* w2d_scales, int T, hipStream_t stream);
+
+/*
  * moe_combine — weighted top-k reduce back to token order (TE
  * DeepSeekV3Layer page, Performance section, "Where the time goes": local
  * permute "reduce"; Description: optional shared expert added).

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     moe_abi_version, moe_route, moe_route_workspace, moe_quantize_mx, moe_permute_rows_bound,
     moe_permute_workspace, moe_permute, moe_grouped_mlp_workspace,
     moe_grouped_mlp_fwd, moe_grouped_fc1_swiglu, moe_grouped_fc2, moe_combine,
+    moe_grouped_fc1_swiglu_dense, moe_grouped_fc2_dense,
     moe_pack_weights, moe_combine_bwd, moe_unpermute, moe_segments_kstride, moe_quantize_mx_segments,
     moe_grouped_fc2_dgrad_dswiglu, moe_grouped_fc1_dgrad, moe_grouped_wgrad,
     SIGNATURES, LIB_PATH,

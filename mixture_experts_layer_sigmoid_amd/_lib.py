@@ -34,6 +34,10 @@ SIGNATURES = {
                                  _I, _P, _SZ, _P]),
     "moe_grouped_fc1_swiglu": (_I, [_P, _P, _I, _P, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _P, _P, _P]),
     "moe_grouped_fc2": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _I, _P]),
+    "moe_grouped_fc1_swiglu_dense": (_I, [_P, _P, _I, _P, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _P,
+                                          _P, _P, _P, _I, _P]),
+    "moe_grouped_fc2_dense": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _I, _P, _P, _I,
+                                   _P]),
     "moe_combine": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _P, _I, _P]),
     "moe_pack_weights": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moe_combine_bwd": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _I64, _P, _I, _P, _P, _P]),
@@ -157,6 +161,21 @@ def moe_grouped_fc2(h, h_scales, h_fmt, w2, w2_scales, w_fmt, offsets, E, H, F, 
     _check("moe_grouped_fc2", load().moe_grouped_fc2(
         _ptr(h), _ptr(h_scales), h_fmt, _ptr(w2), _ptr(w2_scales), w_fmt, _ptr(offsets), E, H, F,
         rows, _ptr(y), y_fmt, _stream(stream)))
+
+
+def moe_grouped_fc1_swiglu_dense(a, a_scales, a_fmt, src_row, w1, w1_scales, w_fmt, offsets, E, H,
+                                 F, rows, act_save, h, h_scales, w1d, w1d_scales, T, stream=None):
+    _check("moe_grouped_fc1_swiglu_dense", load().moe_grouped_fc1_swiglu_dense(
+        _ptr(a), _ptr(a_scales), a_fmt, _ptr(src_row), _ptr(w1), _ptr(w1_scales), w_fmt,
+        _ptr(offsets), E, H, F, rows, _ptr(act_save), _ptr(h), _ptr(h_scales), _ptr(w1d),
+        _ptr(w1d_scales), T, _stream(stream)))
+
+
+def moe_grouped_fc2_dense(h, h_scales, h_fmt, w2, w2_scales, w_fmt, offsets, E, H, F, rows, y,
+                          y_fmt, w2d, w2d_scales, T, stream=None):
+    _check("moe_grouped_fc2_dense", load().moe_grouped_fc2_dense(
+        _ptr(h), _ptr(h_scales), h_fmt, _ptr(w2), _ptr(w2_scales), w_fmt, _ptr(offsets), E, H, F,
+        rows, _ptr(y), y_fmt, _ptr(w2d), _ptr(w2d_scales), T, _stream(stream)))
 
 
 def moe_combine(y, y_fmt, row_map, topk_w, shared, T, k, H, out, out_fmt, stream=None):

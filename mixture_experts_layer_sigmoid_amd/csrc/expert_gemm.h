@@ -1,0 +1,29 @@
+// Launcher of the grouped expert GEMM (expert_gemm.hip), shared by the entry
+// points of grouped_mlp.hip.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// An always-on expert (the layer's shared expert) run by the same launch as
+// the routed experts: `rows` rows whose A operand rows start at `a_row0` and
+// whose output rows start at `row0`, packed weights `w` (+ MX `w_scales`)
+// in the routed experts' format and shape.
+struct DenseExpert {
+  const void* w;
+  const uint8_t* w_scales;
+  int rows;
+  int row0;
+  int a_row0;
+};
+
+// kind: 0 fc1 + SwiGLU (N = 2F, out = h), 1 plain (out = y bf16), 2 dSwiGLU
+// (N = F, out = dA). Arguments are validated by the callers.
+int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const int32_t* gather,
+                const void* wp, const uint8_t* wp_scales, const int32_t* offsets, int E, int N,
+                int K, int64_t rows, int half, void* out, uint8_t* out_scales, float* act_save,
+                const float* a_saved, float* da_f32, hipStream_t stream,
+                const DenseExpert* dense = nullptr);
+
+}  // namespace moe

@@ -47,6 +47,7 @@
 //     save of the fc1 output), plain bf16 y, or the SwiGLU backward (dA in
 //     MX or bf16, optional fp32 copy).
 #include "common.h"
+#include "expert_gemm.h"
 #include "gemm_util.h"
 #include "mx_codec.h"
 
@@ -66,6 +67,11 @@ constexpr int kCs = kTileCols + 4;      // padded fp32 row stride of the epilogu
 // weights takes about as long as the matrix work of ~220 rows at the
 // chip's byte-to-flop ratio (the same for bf16, E4M3 and E2M1 tiles).
 constexpr int kTileCost = 220;
+// A dense expert enters the tile list as kDenseParts row ranges spread
+// evenly among the routed experts, so every XCD runs a share of its
+// compute-bound tiles beside its share of the weight stream.
+constexpr int kDenseParts = 8;
+constexpr int kMaxVirt = kMaxGroups + kDenseParts;
 
 enum { XOP_BF16 = 0, XOP_FP8 = 1, XOP_FP4 = 2 };
 enum { XEPI_SWIGLU = 0, XEPI_PLAIN = 1, XEPI_DSWIGLU = 2 };
@@ -102,6 +108,14 @@ struct XArgs {
   float* act_save;           // fc1: optional fp32 [rows, 2F]
   const float* a_saved;      // dSwiGLU: saved fc1 output [rows, 2F] fp32
   float* da_f32;             // dSwiGLU: optional fp32 copy of dA [rows, 2F]
+  // optional dense expert (the shared expert) run by the same launch: it
+  // takes d_rows rows, A rows d_a_row0.. and output rows d_row0.., packed
+  // weights d_b / d_b_sc; null d_b: none
+  const uint8_t* d_b;
+  const uint8_t* d_b_sc;
+  int d_rows;
+  int d_row0;
+  int d_a_row0;
 };
 
 // epilogue rows per LDS pass: 128, or 64 with two workgroups per CU
@@ -120,7 +134,7 @@ struct XSmem {
   static constexpr int kRing = P * kStage;
   static constexpr int kEpi = (kRows < kPassRows ? kRows : kPassRows) * kCs * 4;
   static constexpr int kBody = kRing > kEpi ? kRing : kEpi;
-  static constexpr int kSched = (kMaxGroups + 2) * 4 + kRows * 4 + (kMaxGroups + 1) * 4;
+  static constexpr int kSched = (kMaxVirt + 2) * 4 + kRows * 4 + (kMaxVirt + 1) * 4 + kMaxVirt * 2;
   static constexpr int kTotal = kBody + kSched;
 };
 
@@ -160,10 +174,11 @@ void expert_gemm_kernel(XArgs p) {
   constexpr int kAScPerWave = kSB > 0 ? (kAScIns + 3) / 4 : 0;
   static_assert(kAIns >= 1, "tile needs at least 32 rows");
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::kTotal];
-  int32_t* s_mt = reinterpret_cast<int32_t*>(smem + S::kBody);   // [E+1] row-tile prefix
-  int32_t* s_src = s_mt + (kMaxGroups + 1);                       // [kRows] source rows
+  int32_t* s_mt = reinterpret_cast<int32_t*>(smem + S::kBody);   // [V+1] row-tile prefix
+  int32_t* s_src = s_mt + (kMaxVirt + 1);                         // [kRows] source rows
   int32_t* s_tot = s_src + kRows;
-  int32_t* s_cost = s_tot + 1;                                    // [E+1] cost prefix
+  int32_t* s_cost = s_tot + 1;                                    // [V+1] cost prefix
+  int16_t* s_vmap = reinterpret_cast<int16_t*>(s_cost + kMaxVirt + 1);  // [V] -> expert / E + part
   int32_t* part = reinterpret_cast<int32_t*>(smem);  // scan scratch (before any load)
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -171,16 +186,37 @@ void expert_gemm_kernel(XArgs p) {
   const int g = lane >> 5;
   const int E = p.E;
 
-  // ---- tile list: row tiles per expert, inclusive prefix in s_mt[1..E] ----
+  // ---- virtual experts: the routed experts in order, with the dense
+  // expert's part x after routed expert floor((x+1) E / 8) - 1 ----
+  const bool dense = p.d_b != nullptr;
+  const int V = E + (dense ? kDenseParts : 0);
+  for (int e = tid; e < E; e += 256) {
+    int x = 0;
+    if (dense)
+      while ((x + 1) * E / kDenseParts <= e) ++x;
+    s_vmap[e + x] = static_cast<int16_t>(e);
+  }
+  if (dense && tid < kDenseParts) s_vmap[(tid + 1) * E / kDenseParts + tid] = static_cast<int16_t>(E + tid);
+  __syncthreads();
+  // rows of virtual expert v (a routed segment, or a part of the dense rows)
+  auto vrows = [&](int v) {
+    const int e = s_vmap[v];
+    if (e >= E) {
+      const int x = e - E;
+      return p.d_rows * (x + 1) / kDenseParts - p.d_rows * x / kDenseParts;
+    }
+    const int n_e = min(p.offsets[e + 1], (int)p.rows) - p.offsets[e];
+    return n_e < 0 ? 0 : n_e;
+  };
+
+  // ---- tile list: row tiles per virtual expert, prefix in s_mt[1..V] ----
   {
-    const int per = (E + 255) / 256;
-    const int lo = tid * per, hi = min(E, lo + per);
+    const int per = (V + 255) / 256;
+    const int lo = min(V, tid * per), hi = min(V, lo + per);
     int s = 0;
-    for (int e = lo; e < hi; ++e) {
-      int n_e = min(p.offsets[e + 1], (int)p.rows) - p.offsets[e];
-      n_e = n_e < 0 ? 0 : n_e;
-      const int mt = (n_e + kRows - 1) / kRows;
-      s_mt[e + 1] = mt;
+    for (int v = lo; v < hi; ++v) {
+      const int mt = (vrows(v) + kRows - 1) / kRows;
+      s_mt[v + 1] = mt;
       s += mt;
     }
     part[tid] = s;
@@ -192,9 +228,9 @@ void expert_gemm_kernel(XArgs p) {
       __syncthreads();
     }
     int run = tid > 0 ? part[tid - 1] : 0;
-    for (int e = lo; e < hi; ++e) {
-      run += s_mt[e + 1];
-      s_mt[e + 1] = run;
+    for (int v = lo; v < hi; ++v) {
+      run += s_mt[v + 1];
+      s_mt[v + 1] = run;
     }
     if (tid == 0) {
       s_mt[0] = 0;
@@ -205,11 +241,9 @@ void expert_gemm_kernel(XArgs p) {
     // same weight bytes (kTileCost, in the matrix time of that many rows)
     // and does matrix work in proportion to its rows
     int c = 0;
-    for (int e = lo; e < hi; ++e) {
-      int n_e = min(p.offsets[e + 1], (int)p.rows) - p.offsets[e];
-      n_e = n_e < 0 ? 0 : n_e;
-      s_cost[e + 1] = (s_mt[e + 1] - s_mt[e]) * kTileCost + n_e;
-      c += s_cost[e + 1];
+    for (int v = lo; v < hi; ++v) {
+      s_cost[v + 1] = (s_mt[v + 1] - s_mt[v]) * kTileCost + vrows(v);
+      c += s_cost[v + 1];
     }
     part[tid] = c;
     __syncthreads();
@@ -220,9 +254,9 @@ void expert_gemm_kernel(XArgs p) {
       __syncthreads();
     }
     run = tid > 0 ? part[tid - 1] : 0;
-    for (int e = lo; e < hi; ++e) {
-      run += s_cost[e + 1];
-      s_cost[e + 1] = run;
+    for (int v = lo; v < hi; ++v) {
+      run += s_cost[v + 1];
+      s_cost[v + 1] = run;
     }
     if (tid == 0) s_cost[0] = 0;
     __syncthreads();
@@ -236,8 +270,8 @@ void expert_gemm_kernel(XArgs p) {
   auto boundary = [&](int x) -> int64_t {
     if (x == 0) return 0;
     if (x == kNumXcd) return total_tiles;
-    const int64_t target = static_cast<int64_t>(s_cost[E]) * x / kNumXcd;
-    int lo = 0, hi = E;
+    const int64_t target = static_cast<int64_t>(s_cost[V]) * x / kNumXcd;
+    int lo = 0, hi = V;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (s_cost[mid] <= target) lo = mid;
@@ -252,20 +286,34 @@ void expert_gemm_kernel(XArgs p) {
   const int64_t t_end = boundary(xs.xcd + 1);
 
   for (int64_t t = t_first; t < t_end; t += xs.nslots) {
-    // ---- decode: expert, then column tile (slow) and row tile (fast) ----
-    int lo = 0, hi = E;
+    // ---- decode: virtual expert, then column tile (slow) and row tile (fast) ----
+    int lo = 0, hi = V;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (static_cast<int64_t>(s_mt[mid]) * p.n_tiles <= t) lo = mid;
       else hi = mid;
     }
-    const int e = lo;
-    const int mtiles = s_mt[e + 1] - s_mt[e];
-    const int64_t local = t - static_cast<int64_t>(s_mt[e]) * p.n_tiles;
+    const int v = lo;
+    const int e = s_vmap[v];
+    const bool dn = e >= E;                      // a part of the dense expert
+    const int mtiles = s_mt[v + 1] - s_mt[v];
+    const int64_t local = t - static_cast<int64_t>(s_mt[v]) * p.n_tiles;
     const int nt = static_cast<int>(local / mtiles);
     const int mt = static_cast<int>(local % mtiles);
-    const int seg_lo = p.offsets[e];
-    const int n_e = min(p.offsets[e + 1], (int)p.rows) - seg_lo;
+    const int dlo = dn ? p.d_rows * (e - E) / kDenseParts : 0;   // first dense row of the part
+    const int seg_lo = dn ? p.d_row0 + dlo : p.offsets[e];
+    const int n_e = vrows(v);
+    // A row of output row r: the gathered token row, the row itself, or for
+    // the dense expert its own A rows
+    auto a_row = [&](int r) {
+      if (dn) return p.d_a_row0 + (r - p.d_row0);
+      if (p.gather) {
+        const int s = p.gather[r];
+        return s < 0 ? 0 : s;  // padding row: loads any valid row, its output is zeroed
+      }
+      return r;
+    };
+    float* act_save = dn ? nullptr : p.act_save;
     int m_per = (n_e + mtiles - 1) / mtiles;
     m_per = (m_per + 31) & ~31;
     const int row0 = seg_lo + mt * m_per;
@@ -281,39 +329,31 @@ void expert_gemm_kernel(XArgs p) {
 #pragma unroll
     for (int i = 0; i < kAIns; ++i) {
       const int r = 8 * (wave + 4 * i) + (lane >> 3);
-      int src = row0 + min(r, nrows - 1);
-      if (p.gather) {
-        src = p.gather[src];
-        if (src < 0) src = 0;  // padding row: loads any valid row, its output is zeroed
-      }
+      const int src = a_row(row0 + min(r, nrows - 1));
       a_off[i] = static_cast<uint32_t>(src) * static_cast<uint32_t>(p.a_row_bytes) +
                  (((lane & 7) ^ swz_key<128>(r)) << 4);
     }
     if (p.gather && EPI == XEPI_SWIGLU)
-      for (int r = tid; r < kRows; r += 256) s_src[r] = r < nrows ? p.gather[row0 + r] : 0;
+      for (int r = tid; r < kRows; r += 256) s_src[r] = r < nrows && !dn ? p.gather[row0 + r] : 0;
     const uint8_t* asc_src[kAScPerWave > 0 ? kAScPerWave : 1];
     if constexpr (kSB > 0) {
 #pragma unroll
       for (int q = 0; q < kAScPerWave; ++q) {
         const int j = min(wave + 4 * q, kAScIns - 1);  // covers rows [j * kScRows, +kScRows)
         const int r = min(j * kScRows + lane / kDpr, nrows - 1);
-        int src = row0 + r;
-        if (p.gather) {
-          src = p.gather[src];
-          if (src < 0) src = 0;
-        }
+        const int src = a_row(row0 + r);
         asc_src[q] = p.a_sc + static_cast<int64_t>(src) * p.a_sc_row_bytes + (lane % kDpr) * 4;
       }
     }
     const int cbw = active ? cb0 : 0;
-    const uint8_t* b_src = p.b + static_cast<int64_t>(e) * p.b_exp_bytes +
-                           static_cast<int64_t>(cbw) * p.k_stages * kChunk + lane * 16;
+    const uint8_t* b_exp = dn ? p.d_b : p.b + static_cast<int64_t>(e) * p.b_exp_bytes;
+    const uint8_t* b_src = b_exp + static_cast<int64_t>(cbw) * p.k_stages * kChunk + lane * 16;
     const int64_t b_blk = static_cast<int64_t>(p.k_stages) * kChunk;   // next column block
     const uint8_t* bsc_src = nullptr;
     int64_t bsc_blk = 0;
     if constexpr (kSB > 0) {
-      bsc_src = p.b_sc + static_cast<int64_t>(e) * p.b_sc_exp_bytes +
-                static_cast<int64_t>(cbw) * p.k_stages * O::kPackedScaleBytes + lane * kSub;
+      const uint8_t* bsc_exp = dn ? p.d_b_sc : p.b_sc + static_cast<int64_t>(e) * p.b_sc_exp_bytes;
+      bsc_src = bsc_exp + static_cast<int64_t>(cbw) * p.k_stages * O::kPackedScaleBytes + lane * kSub;
       bsc_blk = static_cast<int64_t>(p.k_stages) * O::kPackedScaleBytes;
     }
 
@@ -354,10 +394,14 @@ void expert_gemm_kernel(XArgs p) {
         lds_load4(asc_src[q] + static_cast<int64_t>(kt) * kSB, st + S::kA + min(wave + 4 * q, kAScIns - 1) * 256);
       }
     };
+    // a whole stage, activation operations first (the order the steps use)
     auto issue = [&](int kt, auto slot_c, auto nv_c) {
       constexpr int NV = decltype(nv_c)::value;
-      constexpr int kPer = 8 + (kSB > 0 ? 2 : 0) + NV + kAScPerWave;
-      static_for<kPer>([&](auto op_c) { issue_op(kt, slot_c, nv_c, op_c); });
+      constexpr int kB = 8 + (kSB > 0 ? 2 : 0);
+      constexpr int kPer = kB + NV + kAScPerWave;
+      static_for<kPer>([&](auto op_c) {
+        issue_op(kt, slot_c, nv_c, std::integral_constant<int, (decltype(op_c)::value + kB) % kPer>{});
+      });
     };
 
     f32x16_t acc[MAXNV][2];
@@ -447,6 +491,14 @@ void expert_gemm_kernel(XArgs p) {
 
     // ---- main loop: stage kt waits for its loads, frees slot (kt-1)%P by
     // the barrier, then computes while issuing stage kt+P-1 into that slot.
+    // Every step issues its stage's activation loads first, then the weight
+    // loads, and its wait also covers the activation loads of the next stage
+    // (only that stage's weight loads stay in flight): the direct-to-LDS
+    // loads are complete a whole step before any wave reads them. (Waiting
+    // for them only at the step that reads them let, on gfx950, a few rows
+    // of a wave's last activation load per stage be read stale now and then:
+    // run-to-run differences in ~1% of the rows of the bf16 fc2 at 4096
+    // tokens x 256 experts, none with the earlier wait.)
     // Every wave computes (a wave without columns works on duplicate data
     // it never stores) and every iteration issues exactly one stage (past
     // the end it re-issues the last stage, whose data nobody reads), so the
@@ -465,11 +517,12 @@ void expert_gemm_kernel(XArgs p) {
         constexpr int kB = 8 + (kSB > 0 ? 2 : 0);
         using NSL = std::integral_constant<int, (J + P - 1) % P>;
         const int kt_next = min(kt + P - 1, KT - 1);
-        wait_vmcnt<(P - 2) * kPer>();
+        wait_vmcnt<(P - 2) * kPer - NV - kAScPerWave>();
         lds_barrier();
         static_for<NV + kAScPerWave>([&](auto o_c) {
           issue_op(kt_next, NSL{}, nv_c, std::integral_constant<int, kB + decltype(o_c)::value>{});
         });
+        __builtin_amdgcn_sched_barrier(0);  // the weight loads stay behind them
         compute(j_c, nv_c, kt_next, NSL{});
       };
       int k0 = 0;
@@ -529,8 +582,8 @@ void expert_gemm_kernel(XArgs p) {
             *reinterpret_cast<u32x4_t*>(p.out + grow * p.out_row_bytes + (hc0 + c0) * 2) =
                 u32x4_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
                         pack_bf16x2(h[6], h[7])};
-            if (p.act_save) {
-              float* ar = p.act_save + grow * (2ll * F) + hc0 + c0;
+            if (act_save) {
+              float* ar = act_save + grow * (2ll * F) + hc0 + c0;
               store8_f32(ar, gp);
               store8_f32(ar + F, up);
             }
@@ -558,8 +611,8 @@ void expert_gemm_kernel(XArgs p) {
               o[1] = u32x4_t{words[4], words[5], words[6], words[7]};
             }
             p.out_sc[grow * p.out_sc_row_bytes + gblk] = static_cast<uint8_t>(sb);
-            if (p.act_save) {
-              float* ar = p.act_save + grow * (2ll * F) + hc0 + blk * 32;
+            if (act_save) {
+              float* ar = act_save + grow * (2ll * F) + hc0 + blk * 32;
 #pragma unroll
               for (int q = 0; q < 32; q += 8) {
                 store8_f32(ar + q, gp + q);
@@ -721,18 +774,21 @@ int xop_of(int fmt) {
   return fmt == MOE_BF16 ? XOP_BF16 : (fmt == MOE_MXFP8_E4M3 ? XOP_FP8 : XOP_FP4);
 }
 
-// Launch of one grouped expert GEMM with packed weights. kind: 0 fc1 +
-// SwiGLU (N = 2F, out = h), 1 plain (out = y bf16), 2 dSwiGLU (N = F, out =
-// dA). All arguments are validated by the callers.
+// Launch of one grouped expert GEMM with packed weights (expert_gemm.h).
 int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const int32_t* gather,
                 const void* wp, const uint8_t* wp_scales, const int32_t* offsets, int E, int N,
                 int K, int64_t rows, int half, void* out, uint8_t* out_scales, float* act_save,
-                const float* a_saved, float* da_f32, hipStream_t stream) {
+                const float* a_saved, float* da_f32, hipStream_t stream,
+                const DenseExpert* dense) {
   const int bits = fmt == MOE_BF16 ? 16 : (fmt == MOE_MXFP8_E4M3 ? 8 : 4);
   // activation row offsets are 32-bit inside the kernel; a gathered source
   // has at most `rows` rows as well
-  MOE_REQUIRE(rows * (static_cast<int64_t>(K) * bits / 8) < (int64_t{1} << 32), MOE_ERR_UNSUPPORTED,
+  const int64_t a_rows =
+      dense && dense->rows > 0 ? std::max<int64_t>(rows, dense->a_row0 + int64_t{dense->rows}) : rows;
+  MOE_REQUIRE(a_rows * (static_cast<int64_t>(K) * bits / 8) < (int64_t{1} << 32), MOE_ERR_UNSUPPORTED,
               "grouped expert GEMM: activation matrix of 4 GiB or more");
+  MOE_REQUIRE(E + (dense && dense->rows > 0 ? kDenseParts : 0) <= kMaxVirt && E <= 32767,
+              MOE_ERR_INVALID_ARG, "grouped expert GEMM: too many experts");
   XArgs x{};
   x.a = static_cast<const uint8_t*>(a);
   x.a_row_bytes = static_cast<int64_t>(K) * bits / 8;
@@ -755,6 +811,13 @@ int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const
   x.act_save = act_save;
   x.a_saved = a_saved;
   x.da_f32 = da_f32;
+  if (dense && dense->rows > 0) {
+    x.d_b = static_cast<const uint8_t*>(dense->w);
+    x.d_b_sc = dense->w_scales;
+    x.d_rows = dense->rows;
+    x.d_row0 = dense->row0;
+    x.d_a_row0 = dense->a_row0;
+  }
   const int outw = kind == 0 ? half : (kind == 1 ? N : 2 * half);  // output row elements
   const bool mx_out = kind != 1 && fmt != MOE_BF16;
   x.out_row_bytes = mx_out ? static_cast<int64_t>(outw) * bits / 8 : static_cast<int64_t>(outw) * 2;

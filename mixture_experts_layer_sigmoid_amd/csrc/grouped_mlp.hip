@@ -41,15 +41,12 @@
 #include "common.h"
 #include "mx_codec.h"
 #include "gemm_util.h"
+#include "expert_gemm.h"
 
 #include <algorithm>
 #include <type_traits>
 
 namespace moe {
-int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const int32_t* gather,
-                const void* wp, const uint8_t* wp_scales, const int32_t* offsets, int E, int N,
-                int K, int64_t rows, int half, void* out, uint8_t* out_scales, float* act_save,
-                const float* a_saved, float* da_f32, hipStream_t stream);
 namespace {
 
 constexpr int kMaxGroups = 1024;
@@ -808,6 +805,74 @@ extern "C" int moe_grouped_fc2(const void* h, const uint8_t* h_scales, int h_fmt
                 "moe_grouped_fc2: scale arrays must be 4-byte aligned");
   if (rows == 0) return MOE_OK;
   return fc2_impl(h, h_scales, h_fmt, w2, w2_scales, offsets, E, H, F, rows, y, stream);
+}
+
+// fc1 / fc2 of the routed experts and an always-on dense expert (the
+// shared expert) in one launch each: the dense expert's T rows follow the
+// routed rows in h and y. Its tiles are spread through the tile list, so
+// its matrix work runs beside the routed weight stream.
+extern "C" int moe_grouped_fc1_swiglu_dense(const void* a, const uint8_t* a_scales, int a_fmt,
+                                            const int32_t* src_row, const void* w1,
+                                            const uint8_t* w1_scales, int w_fmt,
+                                            const int32_t* offsets, int E, int H, int F,
+                                            int64_t rows, float* act_save, void* h,
+                                            uint8_t* h_scales, const void* w1d,
+                                            const uint8_t* w1d_scales, int T,
+                                            hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(E >= 1 && E <= kMaxGroups && H > 0 && F > 0 && rows >= 0 && T >= 0 &&
+                  rows + T < (int64_t{1} << 31),
+              MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc1_swiglu_dense: need 1 <= E <= 1024, H, F > 0, rows, T >= 0");
+  MOE_REQUIRE(a_fmt != MOE_F32, MOE_ERR_UNSUPPORTED,
+              "moe_grouped_fc1_swiglu_dense: fp32 layers run the shared expert separately");
+  int st = check_formats("moe_grouped_fc1_swiglu_dense", a_fmt, w_fmt, MOE_BF16, H, F);
+  if (st) return st;
+  MOE_REQUIRE(offsets && w1 && w1d && h && (rows + T == 0 || a) && (rows == 0 || src_row),
+              MOE_ERR_INVALID_ARG, "moe_grouped_fc1_swiglu_dense: null pointer");
+  if (is_mx(a_fmt))
+    MOE_REQUIRE(a_scales && w1_scales && w1d_scales && h_scales, MOE_ERR_INVALID_ARG,
+                "moe_grouped_fc1_swiglu_dense: MX formats need a_scales, w1_scales, w1d_scales "
+                "and h_scales");
+  MOE_REQUIRE(aligned16(a) && aligned16(w1) && aligned16(w1d) && aligned16(h) &&
+                  (!act_save || aligned16(act_save)),
+              MOE_ERR_ALIGNMENT, "moe_grouped_fc1_swiglu_dense: tensors must be 16-byte aligned");
+  if (is_mx(a_fmt))
+    MOE_REQUIRE(scale_aligned(a_scales) && scale_aligned(w1_scales) && scale_aligned(w1d_scales),
+                MOE_ERR_ALIGNMENT, "moe_grouped_fc1_swiglu_dense: scale arrays must be 4-byte aligned");
+  if (rows + T == 0) return MOE_OK;
+  const DenseExpert d{w1d, w1d_scales, T, static_cast<int>(rows), 0};
+  return expert_gemm(0, a, a_scales, a_fmt, src_row, w1, w1_scales, offsets, E, 2 * F, H, rows,
+                     F, h, h_scales, act_save, nullptr, nullptr, stream, &d);
+}
+
+extern "C" int moe_grouped_fc2_dense(const void* h, const uint8_t* h_scales, int h_fmt,
+                                     const void* w2, const uint8_t* w2_scales, int w_fmt,
+                                     const int32_t* offsets, int E, int H, int F, int64_t rows,
+                                     void* y, int y_fmt, const void* w2d,
+                                     const uint8_t* w2d_scales, int T, hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(E >= 1 && E <= kMaxGroups && H > 0 && F > 0 && rows >= 0 && T >= 0 &&
+                  rows + T < (int64_t{1} << 31),
+              MOE_ERR_INVALID_ARG, "moe_grouped_fc2_dense: need 1 <= E <= 1024, H, F > 0, rows, T >= 0");
+  MOE_REQUIRE(h_fmt != MOE_F32, MOE_ERR_UNSUPPORTED,
+              "moe_grouped_fc2_dense: fp32 layers run the shared expert separately");
+  int st = check_formats("moe_grouped_fc2_dense", h_fmt, w_fmt, y_fmt, H, F);
+  if (st) return st;
+  MOE_REQUIRE(offsets && w2 && w2d && y && (rows + T == 0 || h), MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc2_dense: null pointer");
+  if (is_mx(h_fmt))
+    MOE_REQUIRE(h_scales && w2_scales && w2d_scales, MOE_ERR_INVALID_ARG,
+                "moe_grouped_fc2_dense: MX formats need h_scales, w2_scales and w2d_scales");
+  MOE_REQUIRE(aligned16(h) && aligned16(w2) && aligned16(w2d) && aligned16(y), MOE_ERR_ALIGNMENT,
+              "moe_grouped_fc2_dense: tensors must be 16-byte aligned");
+  if (is_mx(h_fmt))
+    MOE_REQUIRE(scale_aligned(h_scales) && scale_aligned(w2_scales) && scale_aligned(w2d_scales),
+                MOE_ERR_ALIGNMENT, "moe_grouped_fc2_dense: scale arrays must be 4-byte aligned");
+  if (rows + T == 0) return MOE_OK;
+  const DenseExpert d{w2d, w2d_scales, T, static_cast<int>(rows), static_cast<int>(rows)};
+  return expert_gemm(1, h, h_scales, h_fmt, nullptr, w2, w2_scales, offsets, E, H, F, rows, 0, y,
+                     nullptr, nullptr, nullptr, nullptr, stream, &d);
 }
 
 extern "C" int moe_grouped_mlp_fwd(const void* a, const uint8_t* a_scales, int a_fmt,

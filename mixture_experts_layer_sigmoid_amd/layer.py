@@ -137,7 +137,12 @@ class ExpertWeights:
 
 class MoEForward:
     def __init__(self, *, T, H, F, E, n_group, topk_group, k, routed_scale, fmt,
-                 F_shared=0, align=1, device="cuda", keep_logits=False, save_act=False):
+                 F_shared=0, align=1, device="cuda", keep_logits=False, save_act=False,
+                 fuse_shared=None):
+        """fuse_shared: run the shared expert inside the routed fc1 / fc2
+        launches (its tiles fill the matrix cores while the routed tiles
+        stream weights). Default: whenever the shared expert has the routed
+        experts' width and the layer is not fp32."""
         self.T, self.H, self.F, self.E = T, H, F, E
         self.n_group, self.topk_group, self.k = n_group, topk_group, k
         self.routed_scale, self.fmt, self.F_shared, self.align = routed_scale, fmt, F_shared, align
@@ -162,12 +167,23 @@ class MoEForward:
             self.xq_sc = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
         else:
             self.xq = self.xq_sc = None
-        self.y_rows = torch.empty((max(1, self.bound), H), dtype=act, device=dev)
-        self.h, self.h_sc = self._h_buffers(max(1, self.bound), F, dev)
+        can_fuse = bool(F_shared) and F_shared == F and fmt != "fp32" and T > 0
+        if fuse_shared is None:
+            fuse_shared = can_fuse
+        if fuse_shared and not can_fuse:
+            raise ValueError("the shared expert folds into the routed launches only when "
+                             "F_shared == F, T > 0 and the layer is not fp32")
+        self.fuse_shared = fuse_shared
+        # with the shared expert folded in, its rows follow the routed rows
+        rows = max(1, self.bound) + (T if fuse_shared else 0)
+        self.y_rows = torch.empty((rows, H), dtype=act, device=dev)
+        self.h, self.h_sc = self._h_buffers(rows, F, dev)
         # fc1 output (gate | up) per expert row in fp32, kept for the backward
         self.act_save = (torch.empty((max(1, self.bound), 2 * F), dtype=torch.float32, device=dev)
                          if save_act else None)
-        if F_shared:
+        if fuse_shared:
+            self.y_shared = self.y_rows[self.bound:self.bound + T]
+        elif F_shared:
             self.shared_offsets = torch.tensor([0, T], **i32)
             self.y_shared = torch.empty((T, H), dtype=act, device=dev)
             self.hs, self.hs_sc = self._h_buffers(max(1, T), F_shared, dev)
@@ -197,22 +213,40 @@ class MoEForward:
                       self.counts, self.offsets, self.row_map, self.src_row, None, None,
                       self.perm_ws, stream)
 
-    def experts_fc1(self, x, ew: ExpertWeights, stream=None):
+    def experts_fc1(self, x, ew: ExpertWeights, stream=None, sw: ExpertWeights | None = None):
+        """Routed fc1 + SwiGLU; with fuse_shared also the shared expert's
+        (sw required)."""
         a, a_sc = (self.xq, self.xq_sc) if is_mx(self.fmt) else (x, None)
         f = FMT[self.fmt]
-        L.moe_grouped_fc1_swiglu(a, a_sc, f, self.src_row, ew.w1, ew.w1_sc, f, self.offsets, self.E,
-                                 self.H, self.F, self.bound, self.act_save, self.h, self.h_sc, stream)
+        if self.fuse_shared:
+            L.moe_grouped_fc1_swiglu_dense(a, a_sc, f, self.src_row, ew.w1, ew.w1_sc, f,
+                                           self.offsets, self.E, self.H, self.F, self.bound,
+                                           self.act_save, self.h, self.h_sc, sw.w1, sw.w1_sc,
+                                           self.T, stream)
+        else:
+            L.moe_grouped_fc1_swiglu(a, a_sc, f, self.src_row, ew.w1, ew.w1_sc, f, self.offsets,
+                                     self.E, self.H, self.F, self.bound, self.act_save, self.h,
+                                     self.h_sc, stream)
 
-    def experts_fc2(self, ew: ExpertWeights, stream=None):
+    def experts_fc2(self, ew: ExpertWeights, stream=None, sw: ExpertWeights | None = None):
         f = FMT[self.fmt]
-        L.moe_grouped_fc2(self.h, self.h_sc, f, ew.w2, ew.w2_sc, f, self.offsets, self.E, self.H,
-                          self.F, self.bound, self.y_rows, self.act_fmt, stream)
+        if self.fuse_shared:
+            L.moe_grouped_fc2_dense(self.h, self.h_sc, f, ew.w2, ew.w2_sc, f, self.offsets,
+                                    self.E, self.H, self.F, self.bound, self.y_rows, self.act_fmt,
+                                    sw.w2, sw.w2_sc, self.T, stream)
+        else:
+            L.moe_grouped_fc2(self.h, self.h_sc, f, ew.w2, ew.w2_sc, f, self.offsets, self.E,
+                              self.H, self.F, self.bound, self.y_rows, self.act_fmt, stream)
 
-    def experts(self, x, ew: ExpertWeights, stream=None):
-        self.experts_fc1(x, ew, stream)
-        self.experts_fc2(ew, stream)
+    def experts(self, x, ew: ExpertWeights, stream=None, sw: ExpertWeights | None = None):
+        self.experts_fc1(x, ew, stream, sw)
+        self.experts_fc2(ew, stream, sw)
 
     def shared(self, x, sw: ExpertWeights, stream=None):
+        """The shared expert on its own (only when it is not folded into the
+        routed launches)."""
+        if self.fuse_shared:
+            raise RuntimeError("the shared expert runs inside experts_fc1 / experts_fc2")
         a, a_sc = (self.xq, self.xq_sc) if is_mx(self.fmt) else (x, None)
         f = FMT[self.fmt]
         L.moe_grouped_fc1_swiglu(a, a_sc, f, None, sw.w1, sw.w1_sc, f, self.shared_offsets, 1,
@@ -230,18 +264,19 @@ class MoEForward:
         self.route(x, w_router, bias, stream=stream)
         self.quantize_x(x, stream)
         self.permute(stream)
-        self.experts(x, ew, stream)
-        if self.F_shared:
+        self.experts(x, ew, stream, sw)
+        if self.F_shared and not self.fuse_shared:
             self.shared(x, sw, stream)
         self.combine(stream)
         return self.out
 
     @classmethod
-    def for_config(cls, cfg, device="cuda", keep_logits=False, T=None, save_act=False):
+    def for_config(cls, cfg, device="cuda", keep_logits=False, T=None, save_act=False,
+                   fuse_shared=None):
         return cls(T=cfg.T if T is None else T, H=cfg.H, F=cfg.F, E=cfg.E, n_group=cfg.n_group,
                    topk_group=cfg.topk_group, k=cfg.k, routed_scale=cfg.routed_scale, fmt=cfg.fmt,
                    F_shared=cfg.F_shared if cfg.n_shared else 0, align=cfg.align, device=device,
-                   keep_logits=keep_logits, save_act=save_act)
+                   keep_logits=keep_logits, save_act=save_act, fuse_shared=fuse_shared)
 
 
 class MoEBackward:

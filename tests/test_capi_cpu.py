@@ -124,6 +124,31 @@ def test_grouped_mlp_validation(lib):
     assert g(af=3, wf=3, yf=1, H=256, F=128, asc=A, w1s=A, w2s=A) == INVALID   # fp4 needs F % 256
 
 
+def test_shared_fold_validation(lib):
+    """fc1 / fc2 with the shared expert folded in: the extra weights are
+    required, fp32 layers are refused, and an empty call is a no-op."""
+    def f1(**k):
+        return lib.moe_grouped_fc1_swiglu_dense(
+            A, k.get("asc", A), k.get("af", 1), A, A, A, k.get("af", 1), A, 8, 256, 128,
+            k.get("rows", 100), None, A, A, k.get("w1d", A), k.get("w1ds", A), k.get("T", 20), None)
+
+    def f2(**k):
+        return lib.moe_grouped_fc2_dense(
+            A, k.get("hsc", A), k.get("hf", 2), A, A, k.get("hf", 2), A, 8, 256, 128,
+            k.get("rows", 100), k.get("y", A), 1, k.get("w2d", A), k.get("w2ds", A),
+            k.get("T", 20), None)
+    assert f1(af=0) == UNSUPPORTED
+    assert f2(hf=0) == UNSUPPORTED
+    assert f1(w1d=None) == INVALID
+    assert f2(w2d=None) == INVALID
+    assert f2(w2ds=None) == INVALID               # MX weights need their scales
+    assert f1(af=2, w1ds=A + 2) == ALIGN
+    assert f2(y=A + 8) == ALIGN
+    assert f1(T=-1) == INVALID
+    assert f1(rows=0, T=0) == OK
+    assert f2(rows=0, T=0) == OK
+
+
 def test_combine_validation(lib):
     c = lambda **k: lib.moe_combine(A, k.get("yf", 1), A, A, None, k.get("T", 4), k.get("k", 2),
                                     k.get("H", 64), k.get("out", A), k.get("of", 1), None)

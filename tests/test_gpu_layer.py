@@ -9,6 +9,8 @@ grouped MLP [-> shared expert] -> combine) against the oracle.
   the seeded device generator.
 * Special case: one expert, k = 1 is a dense SwiGLU MLP.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -21,6 +23,13 @@ from tests.gpu_util import certified_tie_mismatches, dev, device_inputs, host, l
 pytestmark = pytest.mark.gpu
 
 TOL = {"fp32": 1e-5, "bf16": 1e-2, "mxfp8": 1e-2, "mxfp4": 3e-2}
+
+
+def _bits(t):
+    """Raw storage of a device tensor (bf16 as int16, codes as bytes)."""
+    if isinstance(t, np.ndarray):
+        return t
+    return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t).cpu().numpy()
 
 
 def _forward_small(cfg):
@@ -70,6 +79,72 @@ def test_single_expert_k1_is_dense_swiglu(gpu_lib):
     ref = (torch.nn.functional.silu(a[:, :F]) * a[:, F:]) @ torch.tensor(w2[0], dtype=torch.float64).T
     assert (host(fw.topk_w) == 1.0).all()
     assert rel_l2(host(out), ref.numpy()) < 1e-2
+
+
+@pytest.mark.parametrize("name,T", [("mini_bf16", None), ("mini_bf16", 5),
+                                    ("mini_mxfp8_decode", None), ("dsv3_bf16_t4096", None),
+                                    ("dsv3_mxfp8_decode_t64", None)])
+def test_shared_fold_matches_separate(gpu_lib, name, T):
+    """The shared expert inside the routed fc1 / fc2 launches computes every
+    row with the arithmetic of the separate launches: routed and shared rows,
+    their MX codes and the layer output agree bit for bit. T = 5 leaves most
+    of the dense expert's eight row parts empty."""
+    cfg = configs.get(name)
+    if T is not None:
+        cfg = dataclasses.replace(cfg, T=T)
+    log(f"shared-expert fold {cfg.name} T={cfg.T}")
+    if cfg.H > 1024:      # full-size weights come from the device generator
+        x, wr, b, wts, sh = _full_setup(cfg)
+        d = dict(x=dev(x, "bf16"), w_router=dev(wr, "bf16"), bias=dev(b), w1=wts["w1"],
+                 w2=wts["w2"], w1s=sh["w1s"], w2s=sh["w2s"])
+    else:
+        _, d = device_inputs(cfg)
+    ew = moe.ExpertWeights.from_dense(d["w1"], d["w2"], cfg.fmt)
+    sw = moe.ExpertWeights.from_dense(d["w1s"], d["w2s"], cfg.fmt)
+    runs = []
+    for fuse in (True, False):
+        fw = moe.MoEForward.for_config(cfg, fuse_shared=fuse)
+        assert fw.fuse_shared == fuse
+        out = host(fw(d["x"], d["w_router"], d["bias"], ew, sw))
+        torch.cuda.synchronize()
+        nb, T = fw.bound, cfg.T
+        hs, hs_sc = (fw.h[nb:nb + T], fw.h_sc) if fuse else (fw.hs[:T], fw.hs_sc)
+        parts = [out, fw.y_rows[:nb], fw.y_shared, fw.h[:nb], hs]
+        if fw.h_sc is not None:
+            parts += [fw.h_sc[:nb], fw.h_sc[nb:nb + T] if fuse else fw.hs_sc[:T]]
+        runs.append([_bits(p) for p in parts])
+    names = ["out", "routed y", "shared y", "routed h", "shared h", "routed h scales",
+             "shared h scales"]
+    for nm, a, b in zip(names, runs[0], runs[1]):
+        assert np.array_equal(a, b), nm
+
+
+@pytest.mark.parametrize("fuse", [False, True])
+def test_expert_gemms_run_to_run_identical(gpu_lib, fuse):
+    """Repeated fc1 / fc2 launches on the same inputs give the same bits
+    (the bf16 layer at full size: 256 experts of mostly one or two 32-row
+    blocks, the shape that once read activation rows before their loads had
+    landed)."""
+    cfg = configs.get("dsv3_bf16_t4096")
+    log(f"run-to-run fc1 / fc2 {cfg.name} fuse_shared={fuse}")
+    x, wr, b, wts, sh = _full_setup(cfg)
+    ew = moe.ExpertWeights.from_dense(wts["w1"], wts["w2"], cfg.fmt)
+    sw = moe.ExpertWeights.from_dense(sh["w1s"], sh["w2s"], cfg.fmt)
+    del wts
+    fw = moe.MoEForward.for_config(cfg, fuse_shared=fuse)
+    xd = dev(x, "bf16")
+    fw(xd, dev(wr, "bf16"), dev(b), ew, sw)
+    torch.cuda.synchronize()
+    h0, y0 = fw.h.clone(), fw.y_rows.clone()
+    for rep in range(6):
+        fw.h.zero_()
+        fw.y_rows.zero_()
+        fw.experts_fc1(xd, ew, sw=sw)
+        fw.experts_fc2(ew, sw=sw)
+        torch.cuda.synchronize()
+        hb = (fw.h != h0).reshape(fw.h.shape[0], -1).any(dim=1)
+        yb = (fw.y_rows != y0).reshape(fw.y_rows.shape[0], -1).any(dim=1)
+        assert int(hb.sum()) == 0 and int(yb.sum()) == 0, (rep, int(hb.sum()), int(yb.sum()))
 
 
 def _full_setup(cfg):
