@@ -232,14 +232,14 @@ def _gpu_backward(cfg, x_d, wr_d, b_d, w1, w2, dout_d):
     bw = moe.MoEBackward(fw)
     bw(dout_d, x_d, ew)
     torch.cuda.synchronize()
-    return fw, bw
+    return fw, bw, ew
 
 
 def test_backward_reduced_skewed(gpu_lib):
     cfg = configs.get("mini_skew_mxfp8")
     log(f"backward end to end {cfg.name}")
     h, d = device_inputs(cfg)
-    fw, bw = _gpu_backward(cfg, d["x"], d["w_router"], d["bias"], d["w1"], d["w2"], d["dout"])
+    fw, bw, _ = _gpu_backward(cfg, d["x"], d["w_router"], d["bias"], d["w1"], d["w2"], d["dout"])
     olog = rt.router_logits(h["x"], h["w_router"])
     oidx, ow, _, _ = rt.route(olog, h["bias"], cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
     assert np.array_equal(host(fw.topk_idx), oidx)
@@ -272,7 +272,8 @@ def test_backward_full_size_sampled(gpu_lib):
     dout = gen.host_dout(cfg)
     wts = gen.device_expert_weights(cfg, "cuda")
     x_d = dev(x, "bf16")
-    fw, bw = _gpu_backward(cfg, x_d, dev(wr, "bf16"), dev(b), wts["w1"], wts["w2"], dev(dout, "bf16"))
+    fw, bw, ew = _gpu_backward(cfg, x_d, dev(wr, "bf16"), dev(b), wts["w1"], wts["w2"],
+                               dev(dout, "bf16"))
     log("  forward + backward done; oracle routing of all tokens")
     olog = rt.router_logits(x, wr)
     oidx, ow, _, osel = rt.route(olog, b, cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
@@ -319,3 +320,20 @@ def test_backward_full_size_sampled(gpu_lib):
         acc = (acc + rows_h[:, jj]).astype(np.float32)
     assert np.array_equal(host(bw.dx[torch.from_numpy(toks).cuda()]), _bf16(acc))
     assert np.isfinite(host(bw.dx)).all()
+    # a second backward of the same inputs gives the same bits (row
+    # fingerprints of the weight gradients, whole dA and dX rows)
+    del wts
+    fp = lambda t: t.view(torch.int16).reshape(-1, t.shape[-1]).sum(dim=1, dtype=torch.int64)
+    used = int(fw.offsets[-1].item())          # rows past the last segment are never written
+    first = (bw.da_f32[:used].clone(), bw.dx_perm[:used].clone(), fp(bw.dw1), fp(bw.dw2))
+    bw.dw1.zero_()
+    bw.dw2.zero_()
+    bw.dx_perm.zero_()
+    bw.da_f32.zero_()
+    bw(dev(dout, "bf16"), x_d, ew)
+    torch.cuda.synchronize()
+    again = (bw.da_f32[:used], bw.dx_perm[:used], fp(bw.dw1), fp(bw.dw2))
+    bits = lambda t: t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+    for name, a, b_ in zip(["dA fp32", "dX rows", "dW1 rows", "dW2 rows"], first, again):
+        assert torch.equal(bits(a) if a.dtype != torch.int64 else a,
+                           bits(b_) if b_.dtype != torch.int64 else b_), name

@@ -84,6 +84,11 @@ def test_gemm_path_full_size(gpu_lib, name):
     assert unc == 0 and nbad <= max(2, cfg.T // 1000)
     same = (idx == oidx).all(axis=1)
     assert rel_l2(w[same], ow[same]) < 1e-5
+    # the same call again gives the same bits
+    idx2, w2, lo2 = _route_dev(gpu_lib, cfg.T, cfg.H, cfg.E, cfg.n_group, cfg.topk_group, cfg.k,
+                               cfg.routed_scale, dev(b), x=dev(x, "bf16"), w=dev(wr, "bf16"))
+    assert np.array_equal(lo.view(np.uint32), lo2.view(np.uint32))
+    assert np.array_equal(idx, idx2) and np.array_equal(w.view(np.uint32), w2.view(np.uint32))
 
 
 @pytest.mark.parametrize("name", ["dsv3_mxfp8_decode_t64", "dsv3_bf16_t4096", "dsv4_skew_mxfp8_t8192"])
