@@ -537,7 +537,12 @@ void expert_gemm_kernel(XArgs p) {
 #undef MOE_NV
       default: break;
     }
-    __syncthreads();  // every wave is done with the LDS ring
+    // every wave is done with the LDS ring, and every direct-to-LDS load
+    // (the tail re-issues the last stage) has landed before the epilogue
+    // reuses that LDS: the workgroup barrier by itself need not wait for
+    // them, so the wait is explicit
+    wait_vmcnt<0>();
+    __syncthreads();
 
     // ---- epilogue in passes of up to 128 rows through an fp32 LDS tile ----
     // C layout of a 32x32 MFMA: lane l, element r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
