@@ -43,9 +43,10 @@
 //     the column tiles of one expert, so concurrent workgroups of an XCD
 //     share activation rows and weight tiles in its L2.
 //   * Epilogues go through LDS in passes of 128 rows to row-major 16-byte
-//     stores: SwiGLU (bf16 h or MX-encoded 32-column blocks, optional fp32
-//     save of the fc1 output), plain bf16 y, or the SwiGLU backward (dA in
-//     MX or bf16, optional fp32 copy).
+//     stores: SwiGLU (bf16 h, or MX-encoded 32-column blocks of h formed in
+//     registers when the fp32 fc1 output is not saved: a wave holds both
+//     halves of the same columns), plain bf16 y, or the SwiGLU backward (dA
+//     in MX or bf16, optional fp32 copy).
 #include "common.h"
 #include "expert_gemm.h"
 #include "gemm_util.h"
@@ -549,27 +550,40 @@ void expert_gemm_kernel(XArgs p) {
     float* cs = reinterpret_cast<float*>(smem);
     constexpr int kPassRB = kPassRows / 32 < MAXNV ? kPassRows / 32 : MAXNV;
     for (int pass = 0; pass * kPassRB < nrb; ++pass) {
+      const int prow0 = pass * kPassRB * 32;
+      const int prows = min(kPassRB * 32, nrows - prow0);
       if (active) {
 #pragma unroll
         for (int i = 0; i < MAXNV; ++i) {
           if (i / kPassRB == pass && i < nrb) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              // SwiGLU: gate values in columns [0, 128), up values in [128, 256)
-              const int col = EPI == XEPI_SWIGLU ? 128 * c + 32 * wave + (lane & 31)
-                                                 : 64 * wave + 32 * c + (lane & 31);
+            if (EPI == XEPI_SWIGLU && OUTF != MOE_BF16 && !act_save) {
+              // MX-encoded h: a wave holds the gate block and the up block
+              // of the same 32 h columns in one layout, so h = silu(g) * u
+              // is formed in registers and only h goes through LDS (columns
+              // [0, 128)) to the block encoder
+              const int hcol = 32 * wave + (lane & 31);
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int row = (i - pass * kPassRB) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                cs[row * kCs + col] = acc[i][c][r];
+                cs[row * kCs + hcol] = silu_mul(acc[i][0][r], acc[i][1][r]);
+              }
+            } else {
+              // gate | up (SwiGLU with the fp32 save) or the plain tile
+#pragma unroll
+              for (int c = 0; c < 2; ++c) {
+                const int col = EPI == XEPI_SWIGLU ? 128 * c + 32 * wave + (lane & 31)
+                                                   : 64 * wave + 32 * c + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                  const int row = (i - pass * kPassRB) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                  cs[row * kCs + col] = acc[i][c][r];
+                }
               }
             }
           }
         }
       }
       __syncthreads();
-      const int prow0 = pass * kPassRB * 32;
-      const int prows = min(kPassRB * 32, nrows - prow0);
       if constexpr (EPI == XEPI_SWIGLU) {
         const int F = p.half;
         const int hc0 = nt * 128;                        // first h column of the tile
@@ -579,10 +593,9 @@ void expert_gemm_kernel(XArgs p) {
             const int row = i / (width / 8), c0 = (i % (width / 8)) * 8;
             const bool zero = p.gather && s_src[prow0 + row] < 0;
             const float* gp = cs + row * kCs + c0;
-            const float* up = gp + 128;
             float h[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) h[q] = zero ? 0.f : silu_mul(gp[q], up[q]);
+            for (int q = 0; q < 8; ++q) h[q] = zero ? 0.f : silu_mul(gp[q], gp[128 + q]);
             const int64_t grow = row0 + prow0 + row;
             *reinterpret_cast<u32x4_t*>(p.out + grow * p.out_row_bytes + (hc0 + c0) * 2) =
                 u32x4_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
@@ -590,7 +603,7 @@ void expert_gemm_kernel(XArgs p) {
             if (act_save) {
               float* ar = act_save + grow * (2ll * F) + hc0 + c0;
               store8_f32(ar, gp);
-              store8_f32(ar + F, up);
+              store8_f32(ar + F, gp + 128);
             }
           }
         } else {
@@ -601,8 +614,13 @@ void expert_gemm_kernel(XArgs p) {
             const bool zero = p.gather && s_src[prow0 + row] < 0;
             const float* gp = cs + row * kCs + blk * 32;
             float v[32];
+            if (!act_save) {
 #pragma unroll
-            for (int q = 0; q < 32; ++q) v[q] = zero ? 0.f : silu_mul(gp[q], gp[128 + q]);
+              for (int q = 0; q < 32; ++q) v[q] = zero ? 0.f : gp[q];
+            } else {
+#pragma unroll
+              for (int q = 0; q < 32; ++q) v[q] = zero ? 0.f : silu_mul(gp[q], gp[128 + q]);
+            }
             uint32_t words[8];
             const uint32_t sb = mx_encode_block<fp4>(v, words);
             const int64_t grow = row0 + prow0 + row;
