@@ -105,7 +105,7 @@ const char* moe_last_error(void);
  * topk_idx   [T, k] int32 out; topk_w [T, k] fp32 out.
  * ws         device workspace of at least moe_route_workspace(T, H, E)
  *            bytes for the router GEMM's partial sums (the GEMM is split
- *            along H when T is small; the partials are added in chunk
+ *            along H when T is small; the partials are added in a fixed
  *            order); may be NULL when logits_in is given. Otherwise
  *            MOE_ERR_WORKSPACE.
  * Limits: 1 <= E <= 512, E % n_group == 0, E / n_group >= 2 when

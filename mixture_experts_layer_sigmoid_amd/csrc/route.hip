@@ -241,8 +241,26 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     const int e = lane + 64 * i;
     val[i] = -INFINITY;
     if (e < E) {
-      float l = 0.f;
-      for (int s = 0; s < S; ++s) l += part[(static_cast<int64_t>(s) * T + t) * E + e];
+      const float* pe = part + static_cast<int64_t>(t) * E + e;
+      const int64_t ps = static_cast<int64_t>(T) * E;   // between partials
+      float l;
+      if (S == 1) {
+        l = pe[0];
+      } else {
+        // eight independent running sums, so eight partials per step are in
+        // flight instead of one dependent load at a time (a decode batch
+        // splits H over dozens of partials)
+        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        int s = 0;
+        for (; s + 8 <= S; s += 8) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) a[u] += pe[(s + u) * ps];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s + u < S) a[u] += pe[(s + u) * ps];
+        l = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+      }
       if (logits_out) logits_out[static_cast<int64_t>(t) * E + e] = l;
       const float sc = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(l))));
       const float sel = sc + bias[e];
