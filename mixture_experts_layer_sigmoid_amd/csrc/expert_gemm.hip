@@ -845,20 +845,29 @@ int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const
   const bool mx_out = kind != 1 && fmt != MOE_BF16;
   x.out_row_bytes = mx_out ? static_cast<int64_t>(outw) * bits / 8 : static_cast<int64_t>(outw) * 2;
   x.out_sc_row_bytes = outw / 32;
-  constexpr int MN = 8, PP = 3, OC = 1;
+  constexpr int OC = 1;
   const dim3 grid(kNumCu * OC), block(256);
-  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, x); };
-  switch (kind * 3 + xop_of(fmt)) {
-    case 0: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_SWIGLU, MOE_BF16>); break;
-    case 1: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_SWIGLU, MOE_MXFP8_E4M3>); break;
-    case 2: go(expert_gemm_kernel<MN, PP, OC, XOP_FP4, XEPI_SWIGLU, MOE_MXFP4_E2M1>); break;
-    case 3: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_PLAIN, MOE_BF16>); break;
-    case 4: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_PLAIN, MOE_BF16>); break;
-    case 5: go(expert_gemm_kernel<MN, PP, OC, XOP_FP4, XEPI_PLAIN, MOE_BF16>); break;
-    case 6: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_DSWIGLU, MOE_BF16>); break;
-    case 7: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_DSWIGLU, MOE_MXFP8_E4M3>); break;
-    default: go(expert_gemm_kernel<MN, PP, OC, XOP_FP4, XEPI_DSWIGLU, MOE_MXFP4_E2M1>); break;
-  }
+  auto launch = [&](auto mn_c, auto pp_c) {
+    constexpr int MN = decltype(mn_c)::value, PP = decltype(pp_c)::value;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, x); };
+    switch (kind * 3 + xop_of(fmt)) {
+      case 0: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_SWIGLU, MOE_BF16>); break;
+      case 1: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_SWIGLU, MOE_MXFP8_E4M3>); break;
+      case 2: go(expert_gemm_kernel<MN, PP, OC, XOP_FP4, XEPI_SWIGLU, MOE_MXFP4_E2M1>); break;
+      case 3: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_PLAIN, MOE_BF16>); break;
+      case 4: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_PLAIN, MOE_BF16>); break;
+      case 5: go(expert_gemm_kernel<MN, PP, OC, XOP_FP4, XEPI_PLAIN, MOE_BF16>); break;
+      case 6: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_DSWIGLU, MOE_BF16>); break;
+      case 7: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_DSWIGLU, MOE_MXFP8_E4M3>); break;
+      default: go(expert_gemm_kernel<MN, PP, OC, XOP_FP4, XEPI_DSWIGLU, MOE_MXFP4_E2M1>); break;
+    }
+  };
+  // decode batches (a few rows per expert on average): 64-row tiles and a
+  // 6-deep ring keep more weight bytes in flight per wave
+  if (kind != 2 && rows <= 8ll * E)
+    launch(std::integral_constant<int, 2>{}, std::integral_constant<int, 6>{});
+  else
+    launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 3>{});
   return check_launch("grouped expert GEMM");
 }
 

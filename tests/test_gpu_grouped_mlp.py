@@ -113,6 +113,32 @@ def test_stage_parity(gpu_lib, name, T, k, heavy, align):
     assert rel_l2(save[:used][live], a_ref[:used][live]) < (1e-5 if cfg.fmt == "fp32" else 1e-4)
 
 
+@pytest.mark.parametrize("name,T,k,heavy", [
+    ("mini_mxfp8_decode", 16, 8, 0), ("mini_mxfp8_decode", 100, 2, 95), ("mini_bf16", 100, 2, 90),
+    ("mini_mxfp4", 120, 2, 100)])
+def test_decode_tiles(gpu_lib, name, T, k, heavy):
+    """Batches with at most eight rows per expert on average run 64-row
+    tiles with a deeper weight ring; an expert with more than 64 rows spans
+    several of them."""
+    cfg = configs.get(name)
+    assert T * k <= 8 * cfg.E
+    log(f"grouped MLP decode tiles {name} T={T} k={k} heavy={heavy}")
+    h = gen.host_inputs(cfg)
+    g = np.random.default_rng(T + 1)
+    x = gen.round_to_storage(g.standard_normal((T, cfg.H)).astype(np.float32), cfg.act_dtype)
+    h["x"] = x
+    idx = _routing(T, cfg.E, k, T + k, heavy)
+    counts, offsets, _, src = pm.permute_maps(idx, cfg.E, 1)
+    assert heavy == 0 or counts.max() > 64
+    ew = _weights_dev(cfg, h)
+    y, save = _run(cfg, dev(x, cfg.act_dtype), ew, offsets, src, len(src), T, act_save=True)
+    y_ref, a_ref = _oracle_rows(cfg, h, offsets, src, cfg.E)
+    err = rel_l2(y, y_ref)
+    log(f"  rel L2 {err:.2e}")
+    assert err < TOL[cfg.fmt]
+    assert rel_l2(save, a_ref) < 1e-4
+
+
 def test_fallback_tiles_bf16(gpu_lib):
     """F % 128 != 0 and H % 256 != 0 select the 256-row, 128-column tiles."""
     cfg = configs.MoEConfig(**{**configs.get("mini_bf16").__dict__, "name": "fallback_bf16",

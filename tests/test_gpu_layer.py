@@ -82,7 +82,8 @@ def test_single_expert_k1_is_dense_swiglu(gpu_lib):
 
 
 @pytest.mark.parametrize("name,T", [("mini_bf16", None), ("mini_bf16", 5),
-                                    ("mini_mxfp8_decode", None), ("dsv3_bf16_t4096", None),
+                                    ("mini_mxfp8_decode", None), ("mini_mxfp8_decode", 16),
+                                    ("dsv3_bf16_t4096", None),
                                     ("dsv3_mxfp8_decode_t64", None)])
 def test_shared_fold_matches_separate(gpu_lib, name, T):
     """The shared expert inside the routed fc1 / fc2 launches computes every
