@@ -111,7 +111,8 @@ const char* moe_last_error(void);
  * Limits: 1 <= E <= 512, E % n_group == 0, E / n_group >= 2 when
  * n_group > 1, 1 <= topk_group <= n_group, 1 <= k <= min(16,
  * topk_group * E / n_group), H % 32 == 0 (bf16) when the GEMM runs.
- * T == 0 is a no-op.
+ * T == 0 is a no-op (after the checks of E, n_group, topk_group and k; the
+ * pointers may then be NULL).
  */
 int moe_route(const void* x, int x_fmt, const void* w_router, const float* bias,
               const float* logits_in, int T, int H, int E, int n_group,
@@ -266,6 +267,8 @@ int moe_grouped_mlp_fwd(const void* a, const uint8_t* a_scales, int a_fmt,
  * h        [rows, F] out in a_fmt (F32, BF16, or MX codes [rows, F] /
  *          [rows, F/2]); h_scales [rows, F/32] out for MX (NULL otherwise).
  *          Rows outside every segment are not written.
+ * rows == 0 is a no-op after the checks of E, H, F and the formats; the
+ * pointers may then be NULL.
  */
 int moe_grouped_fc1_swiglu(const void* a, const uint8_t* a_scales, int a_fmt,
                            const int32_t* src_row, const void* w1,
@@ -279,6 +282,7 @@ int moe_grouped_fc1_swiglu(const void* a, const uint8_t* a_scales, int a_fmt,
  * h        [rows, F] in h_fmt with h_scales for MX (as fc1 writes them).
  * w2       [E, H, F] in w_fmt (== h_fmt) with w2_scales [E, H, F/32] for MX.
  * y        [rows, H] in y_fmt (F32 for the F32 layer, BF16 otherwise).
+ * rows == 0 is a no-op after the same checks; the pointers may then be NULL.
  */
 int moe_grouped_fc2(const void* h, const uint8_t* h_scales, int h_fmt,
                     const void* w2, const uint8_t* w2_scales, int w_fmt,

@@ -769,6 +769,7 @@ extern "C" int moe_grouped_fc1_swiglu(const void* a, const uint8_t* a_scales, in
   const int y_like = a_fmt == MOE_F32 ? MOE_F32 : MOE_BF16;
   int st = check_formats("moe_grouped_fc1_swiglu", a_fmt, w_fmt, y_like, H, F);
   if (st) return st;
+  if (rows == 0) return MOE_OK;  // nothing to read or write; pointers may be null
   MOE_REQUIRE(offsets && w1 && h && (rows == 0 || a), MOE_ERR_INVALID_ARG,
               "moe_grouped_fc1_swiglu: null pointer");
   if (is_mx(a_fmt))
@@ -793,7 +794,8 @@ extern "C" int moe_grouped_fc2(const void* h, const uint8_t* h_scales, int h_fmt
               "moe_grouped_fc2: need 1 <= E <= 1024, H > 0, F > 0, rows >= 0");
   int st = check_formats("moe_grouped_fc2", h_fmt, w_fmt, y_fmt, H, F);
   if (st) return st;
-  MOE_REQUIRE(offsets && w2 && y && (rows == 0 || h), MOE_ERR_INVALID_ARG,
+  if (rows == 0) return MOE_OK;  // nothing to read or write; pointers may be null
+  MOE_REQUIRE(offsets && w2 && (rows == 0 || (h && y)), MOE_ERR_INVALID_ARG,
               "moe_grouped_fc2: null pointer");
   if (is_mx(h_fmt))
     MOE_REQUIRE(h_scales && w2_scales, MOE_ERR_INVALID_ARG,
@@ -828,6 +830,7 @@ extern "C" int moe_grouped_fc1_swiglu_dense(const void* a, const uint8_t* a_scal
               "moe_grouped_fc1_swiglu_dense: fp32 layers run the shared expert separately");
   int st = check_formats("moe_grouped_fc1_swiglu_dense", a_fmt, w_fmt, MOE_BF16, H, F);
   if (st) return st;
+  if (rows + T == 0) return MOE_OK;
   MOE_REQUIRE(offsets && w1 && w1d && h && (rows + T == 0 || a) && (rows == 0 || src_row),
               MOE_ERR_INVALID_ARG, "moe_grouped_fc1_swiglu_dense: null pointer");
   if (is_mx(a_fmt))
@@ -859,7 +862,8 @@ extern "C" int moe_grouped_fc2_dense(const void* h, const uint8_t* h_scales, int
               "moe_grouped_fc2_dense: fp32 layers run the shared expert separately");
   int st = check_formats("moe_grouped_fc2_dense", h_fmt, w_fmt, y_fmt, H, F);
   if (st) return st;
-  MOE_REQUIRE(offsets && w2 && w2d && y && (rows + T == 0 || h), MOE_ERR_INVALID_ARG,
+  if (rows + T == 0) return MOE_OK;
+  MOE_REQUIRE(offsets && w2 && w2d && (rows + T == 0 || (h && y)), MOE_ERR_INVALID_ARG,
               "moe_grouped_fc2_dense: null pointer");
   if (is_mx(h_fmt))
     MOE_REQUIRE(h_scales && w2_scales && w2d_scales, MOE_ERR_INVALID_ARG,

@@ -385,6 +385,7 @@ extern "C" int moe_route(const void* x, int x_fmt, const void* w_router, const f
               "moe_route: topk_group must be in [1, n_group]");
   MOE_REQUIRE(k >= 1 && k <= 16 && k <= topk_group * (E / n_group), MOE_ERR_INVALID_ARG,
               "moe_route: k must be in [1, min(16, topk_group * E / n_group)]");
+  if (T == 0) return MOE_OK;  // nothing to read or write; pointers may be null
   MOE_REQUIRE(bias && topk_idx && topk_w, MOE_ERR_INVALID_ARG,
               "moe_route: bias, topk_idx and topk_w are required");
   if (!logits_in) {
@@ -399,7 +400,6 @@ extern "C" int moe_route(const void* x, int x_fmt, const void* w_router, const f
                   "moe_route: x and w_router must be 16-byte aligned");
     }
   }
-  if (T == 0) return MOE_OK;
   const dim3 sel_grid((T + 3) / 4), block(kThreads);
   if (logits_in) {
     hipLaunchKernelGGL(select_kernel, sel_grid, block, 0, stream, logits_in, 1, bias, T, E,

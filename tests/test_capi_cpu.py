@@ -76,6 +76,23 @@ def test_route_validation(lib):
     assert lib.moe_route_workspace(0, 64, 16) == 0
 
 
+def test_route_empty_batch_takes_null_pointers(lib):
+    assert lib.moe_route(None, 1, None, None, None, 0, 256, 8, 2, 1, 2, 1.0, None, None, None,
+                         None, 0, None) == OK
+    assert lib.moe_route(None, 1, None, None, None, 0, 256, 8, 3, 1, 2, 1.0, None, None, None,
+                         None, 0, None) == INVALID      # limits are still checked
+
+
+def test_grouped_fc_empty_calls_take_null_pointers(lib):
+    for f in (1, 2):
+        assert lib.moe_grouped_fc1_swiglu(None, None, f, None, None, None, f, None, 8, 256, 128, 0,
+                                          None, None, None, None) == OK
+        assert lib.moe_grouped_fc2(None, None, f, None, None, f, None, 8, 256, 128, 0, None, 1,
+                                   None) == OK
+    assert lib.moe_grouped_fc2(None, None, 2, None, None, 2, None, 8, 250, 128, 0, None, 1,
+                               None) == INVALID         # shapes are still checked
+
+
 def test_quantize_validation(lib):
     q = lambda **k: lib.moe_quantize_mx(k.get("inp", A), k.get("fi", 1), k.get("rows", 4),
                                         k.get("K", 64), k.get("axis", 0), k.get("fo", 2),
@@ -206,3 +223,23 @@ def test_backward_validation(lib):
     assert wg(f=3) == UNSUPPORTED
     assert wg(M=96) == INVALID
     assert wg(ks=1000) == INVALID
+
+
+def test_shared_fold_selection_and_buffers(lib):
+    """Host logic of MoEForward: the shared expert is folded into the routed
+    launches exactly when its width equals the routed experts', the layer is
+    not fp32 and the batch is not empty; folded, its rows follow the routed
+    rows in h and y (y_shared is a view of them)."""
+    kw = dict(H=256, F=128, E=8, n_group=2, topk_group=1, k=2, routed_scale=1.0, device="cpu")
+    fw = moe.MoEForward(T=4, fmt="bf16", F_shared=128, **kw)
+    assert fw.fuse_shared
+    assert fw.y_rows.shape == (fw.bound + 4, 256) and fw.h.shape == (fw.bound + 4, 128)
+    assert fw.y_shared.data_ptr() == fw.y_rows[fw.bound].data_ptr()
+    assert not moe.MoEForward(T=4, fmt="fp32", F_shared=128, **kw).fuse_shared
+    assert not moe.MoEForward(T=4, fmt="bf16", F_shared=256, **kw).fuse_shared
+    assert not moe.MoEForward(T=0, fmt="bf16", F_shared=128, **kw).fuse_shared
+    assert not moe.MoEForward(T=4, fmt="bf16", F_shared=128, fuse_shared=False, **kw).fuse_shared
+    with pytest.raises(ValueError):
+        moe.MoEForward(T=4, fmt="bf16", F_shared=256, fuse_shared=True, **kw)
+    with pytest.raises(RuntimeError):
+        fw.shared(None, None)

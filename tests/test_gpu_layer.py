@@ -64,6 +64,29 @@ def test_small_end_to_end(gpu_lib, name):
     assert err < TOL[cfg.fmt]
 
 
+@pytest.mark.parametrize("name", ["mini_bf16", "mini_mxfp8_decode", "mini_mxfp4"])
+def test_empty_and_single_token_batches(gpu_lib, name):
+    """T = 0 runs every stage as a no-op and returns an empty output; T = 1
+    matches the oracle."""
+    base = configs.get(name)
+    for T in (0, 1):
+        cfg = dataclasses.replace(base, T=T)
+        log(f"forward {name} T={T}")
+        h, fw, out = _forward_small(cfg)
+        assert out.shape == (T, cfg.H)
+        if T == 0:
+            continue
+        shared = (h["w1s"], h["w2s"]) if cfg.n_shared else None
+        ref = omlp.moe_forward(h["x"], h["w_router"], h["bias"], lambda e: h["w1"][e],
+                               lambda e: h["w2"][e], E=cfg.E, n_group=cfg.n_group,
+                               topk_group=cfg.topk_group, k=cfg.k, routed_scale=cfg.routed_scale,
+                               fmt=cfg.fmt, align=cfg.align, shared_w=shared)
+        nbad, unc = certified_tie_mismatches(ref["sel"], host(fw.topk_idx), ref["idx"], cfg.n_group,
+                                             cfg.topk_group)
+        assert unc == 0 and nbad == 0, (nbad, unc)
+        assert rel_l2(out, ref["out"]) < TOL[cfg.fmt]
+
+
 def test_single_expert_k1_is_dense_swiglu(gpu_lib):
     g = np.random.default_rng(0)
     T, H, F = 100, 256, 128
