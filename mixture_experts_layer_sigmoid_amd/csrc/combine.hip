@@ -143,8 +143,8 @@ extern "C" int moe_combine(const void* y, int y_fmt, const int32_t* row_map, con
 extern "C" int moe_unpermute(const void* dx_perm, int fmt, const int32_t* row_map, int T, int k,
                              int H, void* dx, int out_fmt, hipStream_t stream) {
   clear_error();
-  MOE_REQUIRE(T >= 0 && k >= 1 && H > 0 && H % 8 == 0, MOE_ERR_INVALID_ARG,
-              "moe_unpermute: need T >= 0, k >= 1, H a positive multiple of 8");
+  MOE_REQUIRE(T >= 0 && k >= 1 && k <= kMaxK && H > 0 && H % 8 == 0, MOE_ERR_INVALID_ARG,
+              "moe_unpermute: need T >= 0, 1 <= k <= 16, H a positive multiple of 8");
   MOE_REQUIRE((fmt == MOE_F32 || fmt == MOE_BF16) && (out_fmt == MOE_F32 || out_fmt == MOE_BF16),
               MOE_ERR_UNSUPPORTED, "moe_unpermute: formats must be MOE_F32 or MOE_BF16");
   if (T == 0) return MOE_OK;

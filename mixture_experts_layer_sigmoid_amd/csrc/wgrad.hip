@@ -19,11 +19,14 @@
 //     that tile just consumed, then written with 16-byte row stores. The
 //     stores are never waited for explicitly: the next wait is for loads
 //     issued before them, so they drain while the following item runs.
-//   * The dW rows of every expert are split into 8 slices, one per XCD
-//     (workgroups are dispatched to XCDs round-robin by index), so each XCD
-//     gets the same share of every expert and the skewed K lengths stay
-//     balanced across the chip. Inside an XCD the tiles run expert by
-//     expert; concurrent tiles share their operand rows in that XCD's L2.
+//   * Schedule over the 8 XCDs (workgroups are dispatched to XCDs
+//     round-robin by index): experts whose segment has at most 8 stages go
+//     whole to one XCD (the experts are cut into 8 contiguous runs of about
+//     equal cost), so an XCD reads their operands once; the dW rows of each
+//     longer expert are split into 8 slices, one per XCD, and run first, so
+//     the skewed K lengths stay balanced across the chip. Inside an XCD the
+//     tiles run expert by expert in groups of 8 row blocks; concurrent tiles
+//     share their operand blocks in that XCD's L2.
 //   * Operands come in the stage-major layout the segment quantizer writes
 //     ([stage][channel][128 K bytes], scales [stage][channel][4]): the
 //     128-channel block of one stage that a tile loads is 16 KB of

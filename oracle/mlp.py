@@ -80,7 +80,7 @@ def combine(y_rows: np.ndarray, row_map: np.ndarray, w: np.ndarray,
 
 def moe_forward(x, w_router, bias, w1_of, w2_of, *, E, n_group, topk_group, k,
                 routed_scale, fmt, align=1, shared_w=None, logits=None,
-                tokens=None):
+                tokens=None, idx=None, workers=1):
     """The layer forward.
 
     x: [T, H] fp32 values of the stored hidden states. w1_of(e) / w2_of(e)
@@ -88,26 +88,46 @@ def moe_forward(x, w_router, bias, w1_of, w2_of, *, E, n_group, topk_group, k,
     shared_w: None or (w1s [2Fs, H], w2s [H, Fs]). logits: optional fp32
     router logits to start from (stage-wise mode). tokens: optional subset of
     token indices whose outputs are evaluated (routing and maps always cover
-    all T tokens).
+    all T tokens). idx: optional [T, k] expert lists to use instead of the
+    oracle's own top-k (where two candidates are within rounding of each
+    other several selections are correct; the combine weights are then the
+    oracle's normalized scores of those experts). workers: experts evaluated
+    concurrently by that many threads (each expert's arithmetic is
+    unchanged; only independent experts overlap).
     """
     x = np.asarray(x, F32)
     T = x.shape[0]
     if logits is None:
         logits = _rt.router_logits(x, w_router)
-    idx, w, s, sel = _rt.route(logits, bias, n_group, topk_group, k, routed_scale)
+    if idx is None:
+        idx, w, s, sel = _rt.route(logits, bias, n_group, topk_group, k, routed_scale)
+    else:
+        idx = np.asarray(idx, np.int32)
+        s = _rt.sigmoid_scores(logits)
+        sel = _rt.selection_scores(s, bias)
+        w = _rt.combine_weights(s, idx, routed_scale)
     counts, offsets, row_map, src_row = _perm.permute_maps(idx, E, align)
     toks = np.arange(T) if tokens is None else np.asarray(tokens)
     xq = operand(x[toks], fmt, axis=-1)            # per-token quantization
     pos = {int(t): i for i, t in enumerate(toks)}
-    y = {}                                         # (t, j) -> y row
     sub_idx = idx[toks]
-    for e in np.unique(sub_idx):
+
+    def one_expert(e):
         tj = np.argwhere(sub_idx == e)             # (token position, slot) in order
-        if len(tj) == 0:
-            continue
         w1q = operand(w1_of(int(e)), fmt, axis=-1)
         w2q = operand(w2_of(int(e)), fmt, axis=-1)
         _, _, ye = expert_mlp(xq[tj[:, 0]], w1q, w2q, fmt)
+        return tj, ye
+
+    experts = [int(e) for e in np.unique(sub_idx)]
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            results = list(ex.map(one_expert, experts))
+    else:
+        results = [one_expert(e) for e in experts]
+    y = {}                                         # (t, j) -> y row
+    for tj, ye in results:
         for r, (p, j) in enumerate(tj):
             y[(int(p), int(j))] = ye[r]
     H = x.shape[1]

@@ -57,27 +57,61 @@ def device_inputs(cfg, seed=0, device="cuda"):
     return h, d
 
 
+def tie_margin(logits_gpu: np.ndarray, logits_orc: np.ndarray) -> float:
+    """How far one selection score (sel = fp32(sigmoid(logit)) + b) can move
+    between the two sides, from the largest measured logit difference d:
+    the sigmoid's slope is at most 1/4, and each side rounds s and s + b to
+    fp32 once (at most 2^-23 apiece for values below 2). Two candidates can
+    trade places only when the oracle's scores lie within twice this of each
+    other."""
+    d = float(np.max(np.abs(np.asarray(logits_gpu, np.float64) - np.asarray(logits_orc, np.float64)),
+                     initial=0.0))
+    return 0.25 * d + 2.0 ** -22
+
+
+def max_tie_tokens(T: int) -> int:
+    """Tokens whose routing may differ under certified near ties: 1e-4 of
+    the batch (at least one)."""
+    return max(1, -(-T // 10000))
+
+
 def certified_tie_mismatches(oracle_sel: np.ndarray, idx_gpu: np.ndarray, idx_orc: np.ndarray,
-                             n_group: int = 1, topk_group: int = 1, margin: float = 1e-5):
+                             n_group: int = 1, topk_group: int = 1, *, margin: float):
     """Tokens whose GPU and oracle expert lists differ. The router GEMM sums
-    H bf16 products in fp32 on the GPU and in fp64 in the oracle, so biased
-    scores may differ by about 1e-6; a mismatch is accepted ("certified")
-    only when the oracle's own scores show a near tie that explains it:
-    every swapped expert lies within `margin` of the oracle's k-th selected
-    score, or (grouped routing) the last kept and first dropped group scores
-    lie within 2*margin. Returns (n_mismatch, n_uncertified)."""
+    H products in fp32 on the GPU and in fp64 in the oracle, so selection
+    scores may differ by up to `margin` (tie_margin of the measured logits)
+    per side; a mismatch is accepted ("certified") only when the oracle's own
+    scores show a near tie that explains it: every swapped expert lies within
+    2 * margin of the oracle's k-th selected score (or, for a reordering of
+    the same experts, each swapped pair within 2 * margin of each other), or
+    (grouped routing) the last kept and the first dropped group scores, each
+    a sum of two selection scores, lie within 4 * margin + 2^-22.
+    margin = 0 accepts no mismatch. Returns (n_mismatch, n_uncertified,
+    mismatched token indices)."""
     from oracle import routing as rt
     bad = np.nonzero((idx_gpu != idx_orc).any(axis=1))[0]
     unc = 0
+    m_e = 2.0 * margin
+    m_g = 4.0 * margin + 2.0 ** -22
     for t in bad:
+        if margin <= 0:
+            unc += 1
+            continue
         sel = oracle_sel[t].astype(np.float64)
         kth = sel[idx_orc[t, -1]]
         swapped = set(int(e) for e in idx_gpu[t]) ^ set(int(e) for e in idx_orc[t])
-        ok = all(abs(sel[e] - kth) <= margin for e in swapped)
+        ok = all(abs(sel[e] - kth) <= m_e for e in swapped)
         if set(idx_gpu[t]) == set(idx_orc[t]):
-            ok = all(abs(sel[a] - sel[b]) <= margin for a, b in zip(idx_gpu[t], idx_orc[t]))
+            ok = all(abs(sel[a] - sel[b]) <= m_e for a, b in zip(idx_gpu[t], idx_orc[t]))
         if not ok and n_group > 1:
             gs = np.sort(rt.group_scores(oracle_sel[t:t + 1].astype(np.float32), n_group)[0])[::-1]
-            ok = abs(float(gs[topk_group - 1]) - float(gs[topk_group])) <= 2 * margin
+            ok = abs(float(gs[topk_group - 1]) - float(gs[topk_group])) <= m_g
         unc += 0 if ok else 1
-    return len(bad), unc
+    return len(bad), unc, bad
+
+
+def oracle_workers() -> int:
+    """Threads for the oracle's per-expert loop at full size (the host
+    cores this process may use, at most 16)."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))

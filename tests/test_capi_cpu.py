@@ -196,9 +196,11 @@ def test_backward_validation(lib):
     assert cb(of=2, H=72) == INVALID              # MX dy needs H % 32 == 0
     assert cb(of=2, ds=None) == INVALID           # MX dy needs its scales
     assert cb(dy=A + 2) == ALIGN
-    un = lambda **k: lib.moe_unpermute(A, k.get("f", 1), A, 4, 2, k.get("H", 64), A,
+    un = lambda **k: lib.moe_unpermute(A, k.get("f", 1), A, 4, k.get("k", 2), k.get("H", 64), A,
                                        k.get("of", 1), None)
     assert un(H=60) == INVALID
+    assert un(k=0) == INVALID
+    assert un(k=17) == INVALID                    # the summing kernel holds at most 16 slots
     assert un(of=3) == UNSUPPORTED
     qs = lambda **k: lib.moe_quantize_mx_segments(
         A, k.get("fi", 1), k.get("mode", 0), k.get("src", A), A, None, 4, k.get("rows", 128),

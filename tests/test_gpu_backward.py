@@ -9,9 +9,10 @@ Stages get the same seeded synthetic inputs on both sides:
 * the grouped weight-gradient GEMM on ragged segments (empty, shorter than
   one 128-row stage, several stages): relative L2 within the MXFP8 bar.
 End to end: the reduced skewed config (every expert, zero-row experts give
-exact zeros) and the full-size one on a sampled light expert plus the
-zero-row experts, with a property check of the un-permute on sampled
-tokens."""
+exact zeros) and the full-size one on its busiest expert (all 8192 rows), a
+mid-size and a light expert plus the zero-row experts, with a property
+check of the un-permute on sampled tokens and a repeat of the whole
+backward that must give the same bits."""
 import numpy as np
 import pytest
 import torch
@@ -19,7 +20,8 @@ import torch
 import mixture_experts_layer_sigmoid_amd as moe
 from moe_synth import configs, gen
 from oracle import backward as obw, mx as omx, permute as pm, routing as rt
-from tests.gpu_util import certified_tie_mismatches, dev, device_inputs, host, log, rel_l2
+from tests.gpu_util import (certified_tie_mismatches, dev, device_inputs, host, log, max_tie_tokens,
+                            rel_l2, tie_margin)
 
 pytestmark = pytest.mark.gpu
 
@@ -227,7 +229,7 @@ def test_wgrad_ragged_segments(gpu_lib, M, N, T):
 
 def _gpu_backward(cfg, x_d, wr_d, b_d, w1, w2, dout_d):
     ew = moe.ExpertWeights.from_dense(w1, w2, cfg.fmt, transposed=True)
-    fw = moe.MoEForward.for_config(cfg, save_act=True)
+    fw = moe.MoEForward.for_config(cfg, save_act=True, keep_logits=True)
     fw(x_d, wr_d, b_d, ew)
     bw = moe.MoEBackward(fw)
     bw(dout_d, x_d, ew)
@@ -276,40 +278,64 @@ def test_backward_full_size_sampled(gpu_lib):
                                dev(dout, "bf16"))
     log("  forward + backward done; oracle routing of all tokens")
     olog = rt.router_logits(x, wr)
-    oidx, ow, _, osel = rt.route(olog, b, cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
+    oidx, ow, os_, osel = rt.route(olog, b, cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
     idx = host(fw.topk_idx)
-    nbad, unc = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group)
-    assert unc == 0 and nbad <= max(2, cfg.T // 1000)
-    bad_tok = np.nonzero((idx != oidx).any(axis=1))[0]
-    counts = np.bincount(oidx.ravel(), minlength=cfg.E)
-    touched = set(int(e) for t in bad_tok for e in np.concatenate([idx[t], oidx[t]]))
+    nbad, unc, bad_tok = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group,
+                                                  margin=tie_margin(host(fw.logits), olog))
+    log(f"  routing: {nbad} certified near-tie tokens, {unc} uncertified")
+    assert unc == 0 and nbad <= max_tie_tokens(cfg.T)
+    # the oracle follows the GPU's expert lists (identical but for certified
+    # ties), with its own normalized scores as combine weights
+    w_or = rt.combine_weights(os_, idx, cfg.routed_scale)
+    counts = np.bincount(idx.ravel(), minlength=cfg.E)
     dw1_d, dw2_d = bw.dw1, bw.dw2
-    zero = [e for e in range(cfg.E) if counts[e] == 0 and e not in touched]
+    zero = [e for e in range(cfg.E) if counts[e] == 0]
     assert len(zero) >= 1
     for e in zero:
         assert not dw1_d[e].any().item() and not dw2_d[e].any().item(), e
-    # a light expert (one or two 32-row blocks): oracle backward of all its rows
-    cand = [e for e in range(cfg.E) if 20 <= counts[e] <= 60 and e not in touched]
-    e = cand[0]
-    tj = np.argwhere(oidx == e)
-    t, j = tj[:, 0], tj[:, 1]
-    log(f"  oracle backward of expert {e} ({len(t)} rows)")
-    w1 = wts["w1"][e].float().cpu().numpy()
-    w2 = wts["w2"][e].float().cpu().numpy()
-    dy = (ow[t, j][:, None].astype(np.float32) * dout[t]).astype(np.float32)
-    rows = host(fw.row_map)[t, j]
-    # the forward's saved fc1 output of these rows first (isolates fc1)
+    # the busiest expert (all its rows: several row tiles in the data-gradient
+    # GEMMs, weight-gradient tiles split across the XCDs), a mid-size one and
+    # a light one (one or two 32-row blocks): oracle backward of all their rows
+    nz = np.nonzero(counts)[0]
+    heavy = int(np.argmax(counts))
+    mid = int(nz[np.argsort(counts[nz], kind="stable")[len(nz) // 2]])
+    light = int([e for e in nz if 20 <= counts[e] <= 60][0])
+    row_map = host(fw.row_map)
     from oracle import mlp as omlp
-    a_ref = omlp.operand(x[t], cfg.fmt) @ omlp.operand(w1, cfg.fmt).T
-    e_a = rel_l2(host(fw.act_save[torch.from_numpy(rows).cuda()]), a_ref)
-    log(f"  expert {e}: saved fc1 output rel L2 {e_a:.2e}")
-    assert e_a < 1e-4
-    dx_e, dw1_e, dw2_e = obw.expert_backward(x[t], dy, w1, w2, cfg.fmt)
-    e_dx = rel_l2(host(bw.dx_perm[torch.from_numpy(rows).cuda()]), dx_e)
-    e_w1 = rel_l2(host(dw1_d[e]), dw1_e)
-    e_w2 = rel_l2(host(dw2_d[e]), dw2_e)
-    log(f"  expert {e}: dX rows {e_dx:.2e}, dW1 {e_w1:.2e}, dW2 {e_w2:.2e}")
-    assert e_dx < TOL and e_w1 < TOL and e_w2 < TOL
+    lock = __import__("threading").Lock()
+
+    def w_host(name_, e):
+        with lock:
+            u = wts[name_][e].view(torch.int16).cpu().numpy()
+        return gen.bf16_bits_to_f32(u.view(np.uint16))
+
+    def one(e):
+        tj = np.argwhere(idx == e)
+        t, j = tj[:, 0], tj[:, 1]
+        w1, w2 = w_host("w1", e), w_host("w2", e)
+        dy = (w_or[t, j][:, None].astype(np.float32) * dout[t]).astype(np.float32)
+        a_ref = omlp.operand(x[t], cfg.fmt) @ omlp.operand(w1, cfg.fmt).T
+        return (e, t, j, a_ref) + obw.expert_backward(x[t], dy, w1, w2, cfg.fmt)
+
+    log(f"  oracle backward of experts {heavy} ({counts[heavy]} rows), {mid} ({counts[mid]}), "
+        f"{light} ({counts[light]}), concurrently")
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=3) as ex:
+        results = list(ex.map(one, [heavy, mid, light]))
+    worst = 0.0
+    for e, t, j, a_ref, dx_e, dw1_e, dw2_e in results:
+        rows = torch.from_numpy(row_map[t, j]).cuda()
+        # the forward's saved fc1 output of these rows (isolates fc1)
+        e_a = rel_l2(host(fw.act_save[rows]), a_ref)
+        e_dx = rel_l2(host(bw.dx_perm[rows]), dx_e)
+        e_w1 = rel_l2(host(dw1_d[e]), dw1_e)
+        e_w2 = rel_l2(host(dw2_d[e]), dw2_e)
+        log(f"  expert {e} ({len(t)} rows): saved fc1 output {e_a:.2e}, dX rows {e_dx:.2e}, "
+            f"dW1 {e_w1:.2e}, dW2 {e_w2:.2e}")
+        assert e_a < 1e-4
+        assert e_dx < TOL and e_w1 < TOL and e_w2 < TOL
+        worst = max(worst, e_w1, e_w2)
+    log(f"  worst per-expert dW error {worst:.2e}")
     # un-permute property on sampled tokens: dx[t] = bf16(sum_j dX_rows[row_map[t, j]])
     g = np.random.default_rng(3)
     toks = g.choice(cfg.T, 64, replace=False)

@@ -19,6 +19,8 @@ from tests.gpu_util import dev, host, log, rel_l2
 pytestmark = pytest.mark.gpu
 
 TOL = {"fp32": 1e-5, "bf16": 1e-2, "mxfp8": 1e-2, "mxfp4": 3e-2}
+# the saved (unrounded) fc1 output against the oracle's fp32 product
+SAVE_TOL = {"fp32": 1e-5, "bf16": 1e-5, "mxfp8": 1e-4, "mxfp4": 1e-4}
 
 
 def _routing(T, E, k, seed, heavy=0):
@@ -108,9 +110,10 @@ def test_stage_parity(gpu_lib, name, T, k, heavy, align):
     assert (y[:used][~live] == 0).all(), "padding rows must be zero"
     assert (y[used:] == 7.0).all(), "rows past the segments are not written"
     # the saved fc1 output is the unrounded accumulator: equal to the oracle's
-    # fp32 product up to summation order (the MX matrix instructions add each
-    # 64-element block product at their own internal precision: ~1e-5)
-    assert rel_l2(save[:used][live], a_ref[:used][live]) < (1e-5 if cfg.fmt == "fp32" else 1e-4)
+    # fp32 product up to summation order for fp32 and bf16 (1e-5); the MX
+    # matrix instructions add each 64-element block product at their own
+    # internal precision (1e-4)
+    assert rel_l2(save[:used][live], a_ref[:used][live]) < SAVE_TOL[cfg.fmt]
 
 
 @pytest.mark.parametrize("name,T,k,heavy", [
@@ -136,11 +139,14 @@ def test_decode_tiles(gpu_lib, name, T, k, heavy):
     err = rel_l2(y, y_ref)
     log(f"  rel L2 {err:.2e}")
     assert err < TOL[cfg.fmt]
-    assert rel_l2(save, a_ref) < 1e-4
+    assert rel_l2(save, a_ref) < SAVE_TOL[cfg.fmt]
 
 
 def test_fallback_tiles_bf16(gpu_lib):
-    """F % 128 != 0 and H % 256 != 0 select the 256-row, 128-column tiles."""
+    """Widths that do not fill the kernel's tiles: F = 192 leaves the last fc1
+    column tile (128 h columns) half empty, so two of its four waves have no
+    columns, and fc2's 384 output columns end in a half-filled 256-column
+    tile."""
     cfg = configs.MoEConfig(**{**configs.get("mini_bf16").__dict__, "name": "fallback_bf16",
                                "H": 384, "F": 192, "E": 12, "T": 150, "n_group": 4, "topk_group": 2,
                                "k": 3, "F_shared": 192, "family": "fallback_bf16"})

@@ -4,9 +4,16 @@ grouped MLP [-> shared expert] -> combine) against the oracle.
 * Small and reduced configs: every output element, relative L2 within the
   format's tolerance (fp32 1e-5, bf16 and MXFP8 1e-2, MXFP4 3e-2).
 * Full-size configs, in the launch configuration the benchmark times: the
-  routing of every token (certified near ties only), counts, and sampled
-  output rows the oracle evaluates token by token with weights copied from
-  the seeded device generator.
+  routing of every token (certified near ties only, with the margin derived
+  from the measured logit error), counts and maps bit for bit against the
+  oracle's permute of the GPU's expert lists, the combine weights, and the
+  output of many tokens, every element: all 64 decode tokens; 256 tokens of
+  the 4096-token batch that together reach every expert; 64 tokens of the
+  MXFP4 batch; tokens of the skewed batch that include rows of its busiest
+  expert. Tie tokens are always among them, checked against the oracle
+  driven by the GPU's expert lists. Weights are copied from the seeded
+  device generator.
+* Repeated expert GEMM launches give identical bits (bf16, MXFP8, MXFP4).
 * Special case: one expert, k = 1 is a dense SwiGLU MLP.
 """
 import dataclasses
@@ -18,7 +25,9 @@ import torch
 import mixture_experts_layer_sigmoid_amd as moe
 from moe_synth import configs, gen
 from oracle import mlp as omlp, routing as rt
-from tests.gpu_util import certified_tie_mismatches, dev, device_inputs, host, log, rel_l2
+from oracle import permute as pm
+from tests.gpu_util import (certified_tie_mismatches, dev, device_inputs, host, log, max_tie_tokens,
+                            oracle_workers, rel_l2, tie_margin, ulp_diff_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +62,8 @@ def test_small_end_to_end(gpu_lib, name):
                            E=cfg.E, n_group=cfg.n_group, topk_group=cfg.topk_group, k=cfg.k,
                            routed_scale=cfg.routed_scale, fmt=cfg.fmt, align=cfg.align, shared_w=shared)
     idx = host(fw.topk_idx)
-    nbad, unc = certified_tie_mismatches(ref["sel"], idx, ref["idx"], cfg.n_group, cfg.topk_group)
+    nbad, unc, _ = certified_tie_mismatches(ref["sel"], idx, ref["idx"], cfg.n_group, cfg.topk_group,
+                                            margin=0.0)
     assert unc == 0 and nbad == 0, (nbad, unc)
     assert np.array_equal(host(fw.counts), ref["counts"])
     assert np.array_equal(host(fw.offsets), ref["offsets"])
@@ -81,8 +91,8 @@ def test_empty_and_single_token_batches(gpu_lib, name):
                                lambda e: h["w2"][e], E=cfg.E, n_group=cfg.n_group,
                                topk_group=cfg.topk_group, k=cfg.k, routed_scale=cfg.routed_scale,
                                fmt=cfg.fmt, align=cfg.align, shared_w=shared)
-        nbad, unc = certified_tie_mismatches(ref["sel"], host(fw.topk_idx), ref["idx"], cfg.n_group,
-                                             cfg.topk_group)
+        nbad, unc, _ = certified_tie_mismatches(ref["sel"], host(fw.topk_idx), ref["idx"],
+                                                cfg.n_group, cfg.topk_group, margin=0.0)
         assert unc == 0 and nbad == 0, (nbad, unc)
         assert rel_l2(out, ref["out"]) < TOL[cfg.fmt]
 
@@ -143,32 +153,34 @@ def test_shared_fold_matches_separate(gpu_lib, name, T):
         assert np.array_equal(a, b), nm
 
 
-@pytest.mark.parametrize("fuse", [False, True])
-def test_expert_gemms_run_to_run_identical(gpu_lib, fuse):
-    """Repeated fc1 / fc2 launches on the same inputs give the same bits
-    (the bf16 layer at full size: 256 experts of mostly one or two 32-row
-    blocks, the shape that once read activation rows before their loads had
-    landed)."""
-    cfg = configs.get("dsv3_bf16_t4096")
+@pytest.mark.parametrize("name,fuse", [("dsv3_bf16_t4096", False), ("dsv3_bf16_t4096", True),
+                                       ("dsv3_mxfp8_decode_t64", True), ("dsv4_mxfp4_t16384", False)])
+def test_expert_gemms_run_to_run_identical(gpu_lib, name, fuse):
+    """Repeated fc1 / fc2 launches on the same inputs give the same bits: the
+    bf16 layer at full size (256 experts of mostly one or two 32-row blocks,
+    the shape that once read activation rows before their loads had landed),
+    the MXFP8 decode batch (64-row tiles, deep weight ring) and the MXFP4
+    batch (block-scaled 4-bit operands, h MX-encoded in the epilogue)."""
+    cfg = configs.get(name)
     log(f"run-to-run fc1 / fc2 {cfg.name} fuse_shared={fuse}")
     x, wr, b, wts, sh = _full_setup(cfg)
     ew = moe.ExpertWeights.from_dense(wts["w1"], wts["w2"], cfg.fmt)
-    sw = moe.ExpertWeights.from_dense(sh["w1s"], sh["w2s"], cfg.fmt)
+    sw = moe.ExpertWeights.from_dense(sh["w1s"], sh["w2s"], cfg.fmt) if sh else None
     del wts
     fw = moe.MoEForward.for_config(cfg, fuse_shared=fuse)
     xd = dev(x, "bf16")
     fw(xd, dev(wr, "bf16"), dev(b), ew, sw)
     torch.cuda.synchronize()
-    h0, y0 = fw.h.clone(), fw.y_rows.clone()
+    bufs = [fw.h, fw.y_rows] + ([fw.h_sc] if fw.h_sc is not None else [])
+    first = [t.clone() for t in bufs]
     for rep in range(6):
-        fw.h.zero_()
-        fw.y_rows.zero_()
+        for t in bufs:
+            t.zero_()
         fw.experts_fc1(xd, ew, sw=sw)
         fw.experts_fc2(ew, sw=sw)
         torch.cuda.synchronize()
-        hb = (fw.h != h0).reshape(fw.h.shape[0], -1).any(dim=1)
-        yb = (fw.y_rows != y0).reshape(fw.y_rows.shape[0], -1).any(dim=1)
-        assert int(hb.sum()) == 0 and int(yb.sum()) == 0, (rep, int(hb.sum()), int(yb.sum()))
+        diff = [int((a != b).reshape(a.shape[0], -1).any(dim=1).sum()) for a, b in zip(bufs, first)]
+        assert sum(diff) == 0, (rep, diff)
 
 
 def _full_setup(cfg):
@@ -180,37 +192,94 @@ def _full_setup(cfg):
     return x, wr, b, wts, sh
 
 
-@pytest.mark.parametrize("name,n_sample", [("dsv3_bf16_t4096", 6), ("dsv3_mxfp8_decode_t64", 3),
-                                           ("dsv4_mxfp4_t16384", 3)])
-def test_full_size_sampled(gpu_lib, name, n_sample):
+def _covering_tokens(idx, E, n, seed):
+    """n tokens (or all, if fewer) that together route to every expert that
+    has rows: one token per expert, rarest experts first, then random
+    fill."""
+    g = np.random.default_rng(seed)
+    chosen = set()
+    counts = np.bincount(idx.ravel(), minlength=E)
+    for e in np.argsort(counts, kind="stable"):
+        if counts[e] == 0 or any(e in idx[t] for t in chosen):
+            continue
+        chosen.add(int(g.choice(np.nonzero((idx == e).any(axis=1))[0])))
+    rest = np.setdiff1d(np.arange(idx.shape[0]), np.array(sorted(chosen), dtype=np.int64))
+    fill = max(0, n - len(chosen))
+    chosen |= set(int(t) for t in g.choice(rest, min(fill, len(rest)), replace=False))
+    return np.array(sorted(chosen), dtype=np.int64)
+
+
+def _sample_tokens(name, idx, E, T):
+    g = np.random.default_rng(11)
+    if name == "dsv3_mxfp8_decode_t64":
+        return np.arange(T)                                   # every token
+    if name == "dsv3_bf16_t4096":
+        return _covering_tokens(idx, E, 256, 12)              # every expert reached
+    if name == "dsv4_mxfp4_t16384":
+        return np.sort(g.choice(T, 64, replace=False))
+    # skewed batch: 8 tokens of the busiest expert, 4 of a mid-size one, 4 more
+    counts = np.bincount(idx.ravel(), minlength=E)
+    heavy = int(np.argmax(counts))
+    nz = np.nonzero(counts)[0]
+    mid = int(nz[np.argsort(counts[nz])[len(nz) // 2]])
+    pick = lambda e, n: g.choice(np.nonzero((idx == e).any(axis=1))[0], n, replace=False)
+    toks = np.concatenate([pick(heavy, 8), pick(mid, 4), g.choice(T, 4, replace=False)])
+    return np.unique(toks)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["dsv3_mxfp8_decode_t64", "dsv3_bf16_t4096", "dsv4_mxfp4_t16384",
+                                  "dsv4_skew_mxfp8_t8192"])
+def test_full_size_forward(gpu_lib, name):
     cfg = configs.get(name)
     log(f"full-size forward {name}: generating weights on the device")
     x, wr, b, wts, sh = _full_setup(cfg)
     ew = moe.ExpertWeights.from_dense(wts["w1"], wts["w2"], cfg.fmt)
     sw = moe.ExpertWeights.from_dense(sh["w1s"], sh["w2s"], cfg.fmt) if sh else None
-    fw = moe.MoEForward.for_config(cfg)
+    fw = moe.MoEForward.for_config(cfg, keep_logits=True)
     out = host(fw(dev(x, "bf16"), dev(wr, "bf16"), dev(b), ew, sw))
     torch.cuda.synchronize()
+    del ew, sw
     log(f"  forward done; oracle routing of all {cfg.T} tokens")
     olog = rt.router_logits(x, wr)
-    oidx, ow, _, osel = rt.route(olog, b, cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
+    lo = host(fw.logits)
+    assert rel_l2(lo, olog) < 1e-6
+    margin = tie_margin(lo, olog)
+    oidx, ow, os_, osel = rt.route(olog, b, cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
     idx = host(fw.topk_idx)
-    nbad, unc = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group)
-    log(f"  routing: {nbad} certified near-tie tokens, {unc} uncertified")
-    assert unc == 0 and nbad <= max(2, cfg.T // 1000)
-    agree = np.nonzero((idx == oidx).all(axis=1))[0]
-    if nbad == 0:
-        assert np.array_equal(host(fw.counts), np.bincount(oidx.ravel(), minlength=cfg.E))
-    g = np.random.default_rng(11)
-    toks = np.unique(np.concatenate([agree[:1], agree[-1:], g.choice(agree, n_sample - 2, replace=False)]))
-    log(f"  oracle on sampled tokens {toks.tolist()}")
-    w1_host = lambda e: wts["w1"][e].float().cpu().numpy()
-    w2_host = lambda e: wts["w2"][e].float().cpu().numpy()
-    shared = (sh["w1s"].float().cpu().numpy(), sh["w2s"].float().cpu().numpy()) if sh else None
-    ref = omlp.moe_forward(x, wr, b, w1_host, w2_host, E=cfg.E, n_group=cfg.n_group,
-                           topk_group=cfg.topk_group, k=cfg.k, routed_scale=cfg.routed_scale,
-                           fmt=cfg.fmt, shared_w=shared, logits=olog, tokens=toks)
-    err = rel_l2(out[toks], ref["out"])
-    log(f"  {name}: sampled rel L2 {err:.3e} (tol {TOL[cfg.fmt]})")
+    nbad, unc, bad = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group,
+                                              margin=margin)
+    log(f"  routing: max |logit diff| gives margin {margin:.2e}; {nbad} certified near-tie tokens "
+        f"{bad.tolist()}, {unc} uncertified")
+    assert unc == 0 and nbad <= max_tie_tokens(cfg.T)
+    # maps bit for bit against the oracle's permute of the GPU's expert lists
+    counts, offsets, row_map, src = pm.permute_maps(idx, cfg.E, cfg.align)
+    assert np.array_equal(host(fw.counts), counts)
+    assert np.array_equal(host(fw.offsets), offsets)
+    assert np.array_equal(host(fw.row_map), row_map)
+    assert np.array_equal(host(fw.src_row)[: fw.bound], src)
+    # combine weights: the oracle's normalized scores of those experts
+    # (fp32 logits on the GPU, fp64 in the oracle)
+    assert ulp_diff_f32(host(fw.topk_w), rt.combine_weights(os_, idx, cfg.routed_scale)).max() <= 64
+    toks = np.union1d(_sample_tokens(name, idx, cfg.E, cfg.T), bad)
+    nexp = len(np.unique(idx[toks]))
+    log(f"  oracle on {len(toks)} tokens ({nexp} experts, {oracle_workers()} threads)")
+    lock = __import__("threading").Lock()
+
+    def w_host(name_, e):
+        with lock:
+            u = wts[name_][e].view(torch.int16).cpu().numpy()
+        return gen.bf16_bits_to_f32(u.view(np.uint16))
+    shared = (host(sh["w1s"]), host(sh["w2s"])) if sh else None
+    ref = omlp.moe_forward(x, wr, b, lambda e: w_host("w1", e), lambda e: w_host("w2", e), E=cfg.E,
+                           n_group=cfg.n_group, topk_group=cfg.topk_group, k=cfg.k,
+                           routed_scale=cfg.routed_scale, fmt=cfg.fmt, shared_w=shared, logits=olog,
+                           tokens=toks, idx=idx, workers=oracle_workers())
+    got = out[toks]
+    err = rel_l2(got, ref["out"])
+    per_tok = [rel_l2(got[i], ref["out"][i]) for i in range(len(toks))]
+    worst = int(np.argmax(per_tok))
+    log(f"  {name}: {len(toks)} tokens, every element: rel L2 {err:.3e} (tol {TOL[cfg.fmt]}); "
+        f"worst token {int(toks[worst])} {per_tok[worst]:.3e}")
     assert err < TOL[cfg.fmt]
     assert np.isfinite(out).all()

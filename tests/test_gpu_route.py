@@ -4,7 +4,9 @@
   indices must match bit for bit and weights within 2 fp32 ulps (both
   evaluate the sigmoid in fp64 and round once).
 * GEMM path: logits match the oracle's fp64 logits within fp32 accumulation
-  error; expert lists match except certified near ties. Covered at small
+  error; expert lists match except certified near ties (candidates whose
+  oracle scores lie within what the measured logit difference can move
+  them; at most 1e-4 of the tokens, at least one). Covered at small
   sizes and at the full hidden size with few tokens (the router GEMM split
   along H into many chunks) and with 4096 tokens.
 """
@@ -14,7 +16,8 @@ import torch
 
 from moe_synth import configs, gen
 from oracle import routing as rt
-from tests.gpu_util import certified_tie_mismatches, dev, log, rel_l2, ulp_diff_f32
+from tests.gpu_util import (certified_tie_mismatches, dev, log, max_tie_tokens, rel_l2, tie_margin,
+                            ulp_diff_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,8 +64,9 @@ def test_gemm_path_small(gpu_lib, name):
     olog = rt.router_logits(x, wr)
     assert rel_l2(lo, olog) < 1e-6
     oidx, ow, _, osel = rt.route(olog, b, cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
-    nbad, unc = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group)
-    assert unc == 0 and nbad <= max(1, cfg.T // 1000)
+    nbad, unc, _ = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group,
+                                            margin=tie_margin(lo, olog))
+    assert unc == 0 and nbad <= max_tie_tokens(cfg.T)
     same = (idx == oidx).all(axis=1)
     assert rel_l2(w[same], ow[same]) < 1e-5
 
@@ -79,9 +83,12 @@ def test_gemm_path_full_size(gpu_lib, name):
     olog = rt.router_logits(x, wr)
     assert rel_l2(lo, olog) < 1e-6
     oidx, ow, _, osel = rt.route(olog, b, cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
-    nbad, unc = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group)
-    log(f"  {name}: {nbad} mismatched tokens of {cfg.T}, {unc} uncertified")
-    assert unc == 0 and nbad <= max(2, cfg.T // 1000)
+    margin = tie_margin(lo, olog)
+    nbad, unc, bad = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group,
+                                              margin=margin)
+    log(f"  {name}: margin {margin:.2e}; {nbad} mismatched tokens of {cfg.T} {bad.tolist()}, "
+        f"{unc} uncertified")
+    assert unc == 0 and nbad <= max_tie_tokens(cfg.T)
     same = (idx == oidx).all(axis=1)
     assert rel_l2(w[same], ow[same]) < 1e-5
     # the same call again gives the same bits
@@ -103,7 +110,8 @@ def test_gemm_path_full_hidden(gpu_lib, name):
     olog = rt.router_logits(x, wr)
     assert rel_l2(lo, olog) < 1e-6
     oidx, ow, _, osel = rt.route(olog, b, cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
-    nbad, unc = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group)
-    assert unc == 0 and nbad <= max(1, cfg.T // 1000)
+    nbad, unc, _ = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group,
+                                            margin=tie_margin(lo, olog))
+    assert unc == 0 and nbad <= max_tie_tokens(cfg.T)
     same = (idx == oidx).all(axis=1)
     assert ulp_diff_f32(w[same], ow[same]).max() <= 64     # fp32 logits vs fp64 logits

@@ -149,3 +149,47 @@ def test_forward_subset_of_tokens_matches_full():
                           tokens=toks)
     # BLAS blocking differs with the row count, so equal to fp32 rounding
     assert brute.rel_l2(res["out"], full["out"][toks]) < 1e-6
+
+
+def test_given_routing_equals_dense_fp64_with_those_experts():
+    """The oracle driven by given expert lists (the certified-tie rule): with
+    one slot of every token replaced by another expert, the output equals the
+    dense fp64 evaluation with the oracle's normalized scores of exactly those
+    experts; with its own lists it is bit-identical to the plain run."""
+    cfg = configs.get("mini_fp32")
+    d, res = _layer(cfg)
+    again = mlp.moe_forward(d["x"], d["w_router"], d["bias"], lambda e: d["w1"][e],
+                            lambda e: d["w2"][e], E=cfg.E, n_group=cfg.n_group,
+                            topk_group=cfg.topk_group, k=cfg.k, routed_scale=cfg.routed_scale,
+                            fmt=cfg.fmt, idx=res["idx"])
+    assert np.array_equal(again["out"], res["out"]) and np.array_equal(again["w"], res["w"])
+    idx = res["idx"].copy()
+    for t in range(cfg.T):            # last slot -> the lowest expert not already chosen
+        idx[t, -1] = min(set(range(cfg.E)) - set(idx[t].tolist()))
+    got = mlp.moe_forward(d["x"], d["w_router"], d["bias"], lambda e: d["w1"][e],
+                          lambda e: d["w2"][e], E=cfg.E, n_group=cfg.n_group,
+                          topk_group=cfg.topk_group, k=cfg.k, routed_scale=cfg.routed_scale,
+                          fmt=cfg.fmt, idx=idx)
+    assert np.array_equal(got["idx"], idx)
+    s = res["s"].astype(np.float64)
+    pick = np.take_along_axis(s, idx.astype(np.int64), axis=1)
+    dw = np.zeros((cfg.T, cfg.E))
+    np.put_along_axis(dw, idx.astype(np.int64), pick / pick.sum(axis=1, keepdims=True) * cfg.routed_scale,
+                      axis=1)
+    ref = brute.dense_moe_fp64(d["x"], d["w1"], d["w2"], dw)
+    assert brute.rel_l2(got["out"], ref) < 2e-6
+    cnt, _, _, _ = brute.bf_permute(idx, cfg.E, 1)
+    assert np.array_equal(got["counts"], cnt)
+
+
+def test_expert_threads_do_not_change_bits():
+    """Evaluating experts on several threads gives the same bits as one."""
+    cfg = configs.get("mini_mxfp4")
+    d = gen.host_inputs(cfg)
+    kw = dict(E=cfg.E, n_group=cfg.n_group, topk_group=cfg.topk_group, k=cfg.k,
+              routed_scale=cfg.routed_scale, fmt=cfg.fmt)
+    one = mlp.moe_forward(d["x"], d["w_router"], d["bias"], lambda e: d["w1"][e],
+                          lambda e: d["w2"][e], **kw)
+    many = mlp.moe_forward(d["x"], d["w_router"], d["bias"], lambda e: d["w1"][e],
+                           lambda e: d["w2"][e], workers=4, **kw)
+    assert np.array_equal(one["out"], many["out"])
