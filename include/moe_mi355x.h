@@ -24,7 +24,8 @@
  * Conventions for every call
  *   - Pointers are device pointers owned by the caller unless stated; the
  *     library never allocates and keeps no state between calls. Scratch
- *     memory comes from the caller (size queries *_workspace).
+ *     memory comes from the caller (size queries *_workspace); the one
+ *     exception, moe_permute_noalloc, uses a fixed array of its own.
  *   - Tensors are dense and row-major; pointers to tensors must be 16-byte
  *     aligned, and row strides are whole rows (no padding between rows).
  *   - MX tensors: element codes [rows, K] bytes (E4M3) or [rows, K/2] bytes
@@ -188,6 +189,32 @@ int moe_permute(const int32_t* topk_idx, int T, int k, int E, int align,
                 int32_t* row_map, int32_t* src_row, void* rows_out,
                 void* scales_out, void* ws, size_t ws_bytes,
                 hipStream_t stream);
+
+/*
+ * moe_permute_noalloc — moe_permute for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, results and checks as moe_permute,
+ * without ws / ws_bytes: the histogram lives in a fixed 1 MiB array inside
+ * the library (one copy per GPU, held until the process ends, its device
+ * address looked up once per device on the first call there). The call
+ * allocates nothing.
+ * Limit: moe_permute_workspace(T, k, E) <= moe_permute_noalloc_max_bytes()
+ * (1 MiB: ceil(T * k / 1024) * E * 4 bytes), else MOE_ERR_WORKSPACE with
+ * nothing enqueued. The array keeps the last call's contents (the first
+ * kernel rewrites every entry it later reads, so nothing needs clearing).
+ * Calls that overlap on one GPU (different streams or threads) share the
+ * array and race: serialize them.
+ */
+int moe_permute_noalloc(const int32_t* topk_idx, int T, int k, int E, int align,
+                        const void* rows_in, int64_t row_bytes,
+                        const void* scales_in, int64_t scale_bytes,
+                        int32_t* counts, int32_t* offsets, int32_t* row_map,
+                        int32_t* src_row, void* rows_out, void* scales_out,
+                        hipStream_t stream);
+
+/* moe_permute_noalloc_max_bytes — size of moe_permute_noalloc's fixed
+ * histogram array (the largest moe_permute_workspace it accepts). */
+size_t moe_permute_noalloc_max_bytes(void);
 
 /*
  * moe_grouped_mlp_workspace — scratch bytes of moe_grouped_mlp_fwd (the

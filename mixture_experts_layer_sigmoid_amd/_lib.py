@@ -29,6 +29,8 @@ SIGNATURES = {
     "moe_permute_rows_bound": (_I64, [_I, _I, _I, _I]),
     "moe_permute_workspace": (_SZ, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _I, _I, _I, _I, _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_noalloc": (_I, [_P, _I, _I, _I, _I, _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_permute_noalloc_max_bytes": (_SZ, []),
     "moe_grouped_mlp_workspace": (_SZ, [_I, _I, _I, _I64, _I, _I]),
     "moe_grouped_mlp_fwd": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _P,
                                  _I, _P, _SZ, _P]),
@@ -135,6 +137,18 @@ def moe_permute(topk_idx, T, k, E, align, rows_in, row_bytes, scales_in, scale_b
         _ptr(counts), _ptr(offsets), _ptr(row_map), _ptr(src_row), _ptr(rows_out),
         _ptr(scales_out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def moe_permute_noalloc(topk_idx, T, k, E, align, rows_in, row_bytes, scales_in, scale_bytes,
+                        counts, offsets, row_map, src_row, rows_out, scales_out, stream=None):
+    _check("moe_permute_noalloc", load().moe_permute_noalloc(
+        _ptr(topk_idx), T, k, E, align, _ptr(rows_in), row_bytes, _ptr(scales_in), scale_bytes,
+        _ptr(counts), _ptr(offsets), _ptr(row_map), _ptr(src_row), _ptr(rows_out),
+        _ptr(scales_out), _stream(stream)))
+
+
+def moe_permute_noalloc_max_bytes() -> int:
+    return load().moe_permute_noalloc_max_bytes()
 
 
 def moe_grouped_mlp_workspace(E, H, F, rows, a_fmt, w_fmt) -> int:

@@ -25,6 +25,8 @@
 #include "common.h"
 
 #include <algorithm>
+#include <mutex>
+#include <string>
 
 namespace moe {
 namespace {
@@ -196,40 +198,48 @@ extern "C" size_t moe_permute_workspace(int T, int k, int E) {
   return static_cast<size_t>(nchunks_of(static_cast<int64_t>(T) * k)) * E * sizeof(int32_t);
 }
 
-extern "C" int moe_permute(const int32_t* topk_idx, int T, int k, int E, int align,
-                           const void* rows_in, int64_t row_bytes, const void* scales_in,
-                           int64_t scale_bytes, int32_t* counts, int32_t* offsets,
-                           int32_t* row_map, int32_t* src_row, void* rows_out, void* scales_out,
-                           void* ws, size_t ws_bytes, hipStream_t stream) {
-  clear_error();
+// Argument checks shared by moe_permute and moe_permute_noalloc (everything
+// but the workspace).
+static int check_permute(const char* fn, const int32_t* topk_idx, int T, int k, int E, int align,
+                         const void* rows_in, int64_t row_bytes, const void* scales_in,
+                         int64_t scale_bytes, int32_t* counts, int32_t* offsets, int32_t* row_map,
+                         int32_t* src_row, void* rows_out, void* scales_out) {
+  const std::string f(fn);
   MOE_REQUIRE(T >= 0 && k >= 1 && E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG,
-              "moe_permute: need T >= 0, k >= 1, 1 <= E <= 1024");
+              f + ": need T >= 0, k >= 1, 1 <= E <= 1024");
   MOE_REQUIRE(align == 1 || align == 16 || align == 32 || align == 64 || align == 128,
-              MOE_ERR_INVALID_ARG, "moe_permute: align must be 1, 16, 32, 64 or 128");
+              MOE_ERR_INVALID_ARG, f + ": align must be 1, 16, 32, 64 or 128");
   MOE_REQUIRE(static_cast<int64_t>(T) * k + static_cast<int64_t>(E) * align < (1ll << 31),
-              MOE_ERR_INVALID_ARG, "moe_permute: row count exceeds int32");
+              MOE_ERR_INVALID_ARG, f + ": row count exceeds int32");
   MOE_REQUIRE(counts && offsets && src_row && (T == 0 || (topk_idx && row_map)),
-              MOE_ERR_INVALID_ARG, "moe_permute: null map pointer");
+              MOE_ERR_INVALID_ARG, f + ": null map pointer");
   MOE_REQUIRE((rows_in == nullptr) == (rows_out == nullptr), MOE_ERR_INVALID_ARG,
-              "moe_permute: rows_in and rows_out go together");
+              f + ": rows_in and rows_out go together");
   MOE_REQUIRE((scales_in == nullptr) == (scales_out == nullptr), MOE_ERR_INVALID_ARG,
-              "moe_permute: scales_in and scales_out go together");
+              f + ": scales_in and scales_out go together");
   if (rows_in) {
-    MOE_REQUIRE(row_bytes > 0, MOE_ERR_INVALID_ARG, "moe_permute: row_bytes must be > 0");
+    MOE_REQUIRE(row_bytes > 0, MOE_ERR_INVALID_ARG, f + ": row_bytes must be > 0");
     MOE_REQUIRE(row_bytes % 16 == 0 && aligned16(rows_in) && aligned16(rows_out),
-                MOE_ERR_ALIGNMENT, "moe_permute: rows and row_bytes must be 16-byte aligned");
+                MOE_ERR_ALIGNMENT, f + ": rows and row_bytes must be 16-byte aligned");
   }
   if (scales_in)
-    MOE_REQUIRE(scale_bytes > 0, MOE_ERR_INVALID_ARG, "moe_permute: scale_bytes must be > 0");
-  const size_t need = moe_permute_workspace(T, k, E);
-  MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "moe_permute: workspace too small");
+    MOE_REQUIRE(scale_bytes > 0, MOE_ERR_INVALID_ARG, f + ": scale_bytes must be > 0");
+  return MOE_OK;
+}
 
+// The permutation's kernels on a histogram buffer `hist` of at least
+// moe_permute_workspace(T, k, E) bytes (fully written by the first kernel
+// before it is read, so its previous contents do not matter).
+static int permute_launch(const int32_t* topk_idx, int T, int k, int E, int align,
+                          const void* rows_in, int64_t row_bytes, const void* scales_in,
+                          int64_t scale_bytes, int32_t* counts, int32_t* offsets,
+                          int32_t* row_map, int32_t* src_row, void* rows_out, void* scales_out,
+                          int32_t* hist, hipStream_t stream, const char* fn) {
   const int64_t n = static_cast<int64_t>(T) * k;
   const int nchunks = nchunks_of(n);
   const int64_t bound = moe_permute_rows_bound(T, k, E, align);
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  int32_t* hist = static_cast<int32_t*>(ws);
   const int hgrid = std::max<int64_t>((nchunks + 3) / 4, std::min<int64_t>(1024, (bound + 255) / 256));
   hipLaunchKernelGGL(hist_kernel, dim3(hgrid), dim3(256), 0, stream, topk_idx, n, E, nbits,
                      nchunks, hist, src_row, bound);
@@ -248,5 +258,86 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int k, int E, int ali
                        static_cast<const uint8_t*>(scales_in), scale_bytes, src_row, bound,
                        static_cast<uint8_t*>(scales_out));
   }
-  return check_launch("moe_permute");
+  return check_launch(fn);
+}
+
+extern "C" int moe_permute(const int32_t* topk_idx, int T, int k, int E, int align,
+                           const void* rows_in, int64_t row_bytes, const void* scales_in,
+                           int64_t scale_bytes, int32_t* counts, int32_t* offsets,
+                           int32_t* row_map, int32_t* src_row, void* rows_out, void* scales_out,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  int st = check_permute("moe_permute", topk_idx, T, k, E, align, rows_in, row_bytes, scales_in,
+                         scale_bytes, counts, offsets, row_map, src_row, rows_out, scales_out);
+  if (st) return st;
+  const size_t need = moe_permute_workspace(T, k, E);
+  MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "moe_permute: workspace too small");
+  return permute_launch(topk_idx, T, k, E, align, rows_in, row_bytes, scales_in, scale_bytes,
+                        counts, offsets, row_map, src_row, rows_out, scales_out,
+                        static_cast<int32_t*>(ws), stream, "moe_permute");
+}
+
+// ---- moe_permute_noalloc: the histogram in a file-scope device array ----
+// Each GPU the library runs on holds its own copy of `scratch` (1 MiB) until
+// the process ends. Host code never passes the array's name to a kernel (in
+// host code it is a stand-in, not a device address): the device address is
+// looked up once per device with hipGetSymbolAddress, with that device
+// current, and kept.
+static constexpr size_t kNoAllocScratchBytes = size_t{1} << 20;
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / sizeof(int32_t)];
+
+namespace moe {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of `scratch` on the current device (looked up on the first
+// call on that device), or null with an error set
+int32_t* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    set_error("moe_permute_noalloc: no current HIP device (or device index >= 64)");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      set_error(std::string("moe_permute_noalloc: hipGetSymbolAddress(scratch) failed: ") +
+                hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = static_cast<int32_t*>(ptr);
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" size_t moe_permute_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int moe_permute_noalloc(const int32_t* topk_idx, int T, int k, int E, int align,
+                                   const void* rows_in, int64_t row_bytes, const void* scales_in,
+                                   int64_t scale_bytes, int32_t* counts, int32_t* offsets,
+                                   int32_t* row_map, int32_t* src_row, void* rows_out,
+                                   void* scales_out, hipStream_t stream) {
+  clear_error();
+  int st = check_permute("moe_permute_noalloc", topk_idx, T, k, E, align, rows_in, row_bytes,
+                         scales_in, scale_bytes, counts, offsets, row_map, src_row, rows_out,
+                         scales_out);
+  if (st) return st;
+  const size_t need = moe_permute_workspace(T, k, E);
+  MOE_REQUIRE(need <= kNoAllocScratchBytes, MOE_ERR_WORKSPACE,
+              "moe_permute_noalloc: T * k and E need " + std::to_string(need) +
+                  " bytes of histogram, above its fixed 1 MiB (ceil(T * k / 1024) * E * 4 must "
+                  "not exceed 1048576); use moe_permute with a workspace");
+  int32_t* hist = scratch_on_current_device();
+  if (!hist) return MOE_ERR_HIP;
+  return permute_launch(topk_idx, T, k, E, align, rows_in, row_bytes, scales_in, scale_bytes,
+                        counts, offsets, row_map, src_row, rows_out, scales_out, hist, stream,
+                        "moe_permute_noalloc");
 }
