@@ -1,7 +1,7 @@
 """Throughput of the routed MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--cpu-tokens N]
+                    [--no-cpu-baseline] [--cpu-experts M]
     python bench.py --copy-calibration MIB
 
 The second form only runs a plain device-to-device copy of MIB MiB a few
@@ -34,7 +34,10 @@ launch of that kernel measured with rocprofv3 counters (profiles/
 pmc_<stage>_<workload>.txt, scaled by the copy calibration), reported only
 while the kernel source is the one that was measured (its SHA-256 is
 recorded in that file), else null. The CPU baseline times the oracle (plain
-numpy) on the first --cpu-tokens tokens of the same batch.
+numpy, BLAS on every usable host core) on a bounded sample of the same
+batch: routing of every token, the expert MLPs of a few whole experts (all
+their rows), a share of the shared expert and the whole combine, scaled to
+the batch by the number of touched experts (see cpu_baseline).
 """
 from __future__ import annotations
 
@@ -173,46 +176,118 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
 
 
-def _host_threads():
+def host_info():
+    """Host facts printed with every record: usable cores and CPU model."""
+    cores = len(os.sched_getaffinity(0))
+    model = None
     try:
-        from threadpoolctl import threadpool_info
-        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
     except Exception:
-        return len(os.sched_getaffinity(0))
+        pass
+    return cores, model
 
 
-def cpu_baseline(cfg, x, wr, b, wts, sh, dout, n_tokens: int, backward: bool):
-    """Time the oracle on the first n_tokens tokens (weights held on the host
-    in their bf16 storage type and widened to fp32 by the oracle's weight
-    accessors, as the oracle consumes them)."""
+def cpu_baseline(cfg, x, wr, b, wts, sh, dout, backward: bool, budget_experts: int | None = None):
+    """Time the oracle (plain numpy) on a bounded sample of the same batch
+    and scale it to the whole batch.
+
+    The oracle's cost is a fixed part per touched expert (widening or MX
+    fake-quantizing its weights) plus a part per row, so a sample of whole
+    experts with all their rows scales to the batch by the count of touched
+    experts: routing of every token (timed in full), the expert MLPs (and
+    for the skewed workload the expert backward) of m experts picked at
+    evenly spaced row-count quantiles, the shared expert on a share of the
+    tokens, and the combine of every token. BLAS runs on every usable host
+    core."""
     import torch
+    from threadpoolctl import threadpool_limits
     from oracle import backward as obw, mlp as omlp, routing as rt
-    log(f"cpu baseline: copying weights to the host for {n_tokens} tokens")
-    w1h = wts["w1"].view(torch.int16).cpu().numpy().view(np.uint16)
-    w2h = wts["w2"].view(torch.int16).cpu().numpy().view(np.uint16)
-    shared = None
-    if sh is not None:
-        shared = (sh["w1s"].float().cpu().numpy(), sh["w2s"].float().cpu().numpy())
+    cores, model = host_info()
     widen = lambda u: (u.astype(np.uint32) << 16).view(np.float32)
-    xs = x[:n_tokens]
-    threads = _host_threads()
-    log(f"cpu baseline: oracle on {n_tokens} tokens, {threads} BLAS threads")
-    t0 = time.perf_counter()
-    ref = omlp.moe_forward(xs, wr, b, lambda e: widen(w1h[e]), lambda e: widen(w2h[e]), E=cfg.E,
-                           n_group=cfg.n_group, topk_group=cfg.topk_group, k=cfg.k,
-                           routed_scale=cfg.routed_scale, fmt=cfg.fmt, align=cfg.align,
-                           shared_w=shared)
-    what = f"oracle forward (routing, {cfg.k} routed experts"
-    what += " + shared expert" if shared else ""
-    what += ", combine)"
-    if backward:
-        obw.moe_backward(xs, dout[:n_tokens], ref["idx"], ref["w"], lambda e: widen(w1h[e]),
-                         lambda e: widen(w2h[e]), E=cfg.E, fmt=cfg.fmt)
-        what += " and backward (dX and every touched expert's dW)"
-    dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{what} of the first {n_tokens} tokens of the {cfg.T}-token batch; "
-                      f"{dt:.1f} s"}
+    w1_of = lambda e: widen(wts["w1"][e].view(torch.int16).cpu().numpy().view(np.uint16))
+    w2_of = lambda e: widen(wts["w2"][e].view(torch.int16).cpu().numpy().view(np.uint16))
+    T, k, fmt = cfg.T, cfg.k, cfg.fmt
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        logits = rt.router_logits(x, wr)
+        idx, w, s, sel = rt.route(logits, b, cfg.n_group, cfg.topk_group, k, cfg.routed_scale)
+        t_route = time.perf_counter() - t0
+        counts = np.bincount(idx.ravel(), minlength=cfg.E)
+        touched = np.nonzero(counts)[0]
+        if budget_experts is None:
+            budget_experts = {"bf16": 32, "mxfp8": 3, "mxfp4": 4}.get(fmt, 8)
+            if backward:
+                budget_experts = 1
+        m = max(1, min(budget_experts, len(touched)))
+        order = touched[np.argsort(counts[touched], kind="stable")]
+        picks = order[np.linspace(0, len(order) - 1, m + 2)[1:-1].round().astype(int)] if m < len(order) \
+            else order
+        log(f"cpu baseline: routing {t_route:.1f} s; expert sample {picks.tolist()} "
+            f"(rows {counts[picks].tolist()})")
+        t_exp = 0.0
+        for e in picks:
+            tj = np.argwhere(idx == e)
+            t_, j_ = tj[:, 0], tj[:, 1]
+            w1, w2 = w1_of(int(e)), w2_of(int(e))
+            t0 = time.perf_counter()
+            xq = omlp.operand(x[t_], fmt, axis=-1)
+            omlp.expert_mlp(xq, omlp.operand(w1, fmt, axis=-1), omlp.operand(w2, fmt, axis=-1), fmt)
+            if backward:
+                dy = (w[t_, j_][:, None].astype(np.float32) * dout[t_]).astype(np.float32)
+                obw.expert_backward(x[t_], dy, w1, w2, fmt)
+            t_exp += time.perf_counter() - t0
+        t_sh, n_sh = 0.0, 0
+        if sh is not None:
+            n_sh = min(T, 512)
+            w1s, w2s = sh["w1s"].float().cpu().numpy(), sh["w2s"].float().cpu().numpy()
+            t0 = time.perf_counter()
+            xq = omlp.operand(x[:n_sh], fmt, axis=-1)
+            omlp.expert_mlp(xq, omlp.operand(w1s, fmt), omlp.operand(w2s, fmt), fmt)
+            t_sh = time.perf_counter() - t0
+        y_rows = np.zeros((T * k, cfg.H), np.float32)
+        t0 = time.perf_counter()
+        omlp.combine(y_rows, np.arange(T * k).reshape(T, k), w)
+        t_comb = time.perf_counter() - t0
+        del y_rows
+    total = t_route + t_exp * len(touched) / len(picks) + (t_sh * T / n_sh if n_sh else 0.0) + t_comb
+    measured = t_route + t_exp + t_sh + t_comb
+    what = "forward" + (" and expert backward" if backward else "")
+    sample = (f"oracle {what}: routing of all {T} tokens ({t_route:.1f} s) + the expert MLPs of "
+              f"{len(picks)} of the {len(touched)} touched experts with all their rows "
+              f"({int(counts[picks].sum())} rows, {t_exp:.1f} s, scaled x{len(touched) / len(picks):.1f})"
+              + (f" + the shared expert on {n_sh} of {T} tokens ({t_sh:.1f} s, scaled x{T / n_sh:.1f})"
+                 if n_sh else "")
+              + f" + the combine of all tokens ({t_comb:.1f} s); {measured:.1f} s measured, "
+              f"{total:.1f} s estimated for the whole batch")
+    return {"value": round(T / total, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "cpu_model": model, "seconds_estimated": round(total, 1),
+            "seconds_measured": round(measured, 1)}
+
+
+def run_metadata():
+    """Date, source hash of the HIP library and the git commit (when the
+    tree carries its .git)."""
+    import datetime
+    import glob
+    import subprocess
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(HERE, "mixture_experts_layer_sigmoid_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    commit = None
+    try:
+        r = subprocess.run(["git", "-C", HERE, "rev-parse", "--short=12", "HEAD"], capture_output=True,
+                           text=True, timeout=10)
+        commit = r.stdout.strip() or None
+    except Exception:
+        pass
+    return {"date_utc": datetime.datetime.utcnow().strftime("%Y-%m-%dT%H:%M:%SZ"),
+            "git_commit": commit, "csrc_sha256": h.hexdigest()[:16]}
 
 
 def main():
@@ -222,7 +297,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_bf16_t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=None)
+    ap.add_argument("--cpu-experts", type=int, default=None,
+                    help="experts (with all their rows) in the CPU-baseline sample")
     ap.add_argument("--copy-calibration", type=int, default=None, metavar="MIB")
     args = ap.parse_args()
     if args.copy_calibration:
@@ -263,6 +339,8 @@ def main():
         del wts["w1"], wts["w2"]
     fw = moe.MoEForward.for_config(cfg, device=dev, save_act=backward)
     bw = moe.MoEBackward(fw) if backward else None
+    if bw is not None:
+        bw.stage_buffers()     # the backward is timed one C call per stage
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 
@@ -376,9 +454,12 @@ def main():
         "roofline": roof,
         "stages": stages,
     }
+    cores, model = host_info()
+    props = torch.cuda.get_device_properties(dev)
+    rec["run"] = {**run_metadata(), "gpu": props.name, "gpu_cus": props.multi_processor_count,
+                  "host_cores": cores, "cpu_model": model}
     if want_cpu:
-        n = args.cpu_tokens or (1 if backward else (96 if cfg.fmt == "bf16" else 2))
-        rec["cpu_baseline"] = cpu_baseline(cfg, x, wr, b, wts, sh, dout, min(n, cfg.T), backward)
+        rec["cpu_baseline"] = cpu_baseline(cfg, x, wr, b, wts, sh, dout, backward, args.cpu_experts)
     print(json.dumps(rec), flush=True)
 
 

@@ -19,7 +19,9 @@
  *   moe_route -> [moe_quantize_mx] -> moe_permute -> moe_grouped_mlp_fwd
  *   (routed experts; again with E = 1 for a shared expert) -> moe_combine
  * where moe_grouped_mlp_fwd is moe_grouped_fc1_swiglu followed by
- * moe_grouped_fc2.
+ * moe_grouped_fc2 (moe_grouped_fc1_swiglu_dense / moe_grouped_fc2_dense run
+ * the routed and the shared expert in the same launches). The backward of
+ * the routed experts is moe_grouped_mlp_bwd.
  *
  * Conventions for every call
  *   - Pointers are device pointers owned by the caller unless stated; the
@@ -362,9 +364,11 @@ int moe_combine(const void* y, int y_fmt, const int32_t* row_map,
  * ---- Backward of the routed expert path (TE DeepSeekV3Layer page,
  * Performance section, "Where the time goes": dGLU bwd and wgrad of the
  * fused grouped MLP in MXFP8; the local permute's reduce). Routing weights
- * are constants and quantizers pass gradients straight through. Call order:
- *   moe_combine_bwd -> moe_quantize_mx (dY rows) ->
- *   moe_grouped_fc2_dgrad_dswiglu -> moe_grouped_fc1_dgrad -> moe_unpermute
+ * are constants and quantizers pass gradients straight through.
+ * moe_grouped_mlp_bwd (at the end of this header) runs the whole backward
+ * in one call; its steps are also exported one by one, in this order:
+ *   moe_combine_bwd (dY rows, MX) -> moe_grouped_fc2_dgrad_dswiglu ->
+ *   moe_grouped_fc1_dgrad -> moe_unpermute ->
  *   moe_quantize_mx_segments (dY, h, dA, x) -> moe_grouped_wgrad (dW2, dW1)
  */
 
@@ -475,6 +479,53 @@ int moe_grouped_wgrad(const void* at, const uint8_t* at_scales, const void* bt,
                       const uint8_t* bt_scales, int fmt, const int32_t* kofs,
                       int E, int M, int N, int64_t kstride, void* dw,
                       hipStream_t stream);
+
+/*
+ * moe_grouped_mlp_bwd_workspace — scratch bytes of moe_grouped_mlp_bwd (0
+ * for unsupported arguments).
+ */
+size_t moe_grouped_mlp_bwd_workspace(int T, int k, int E, int H, int F,
+                                     int64_t rows, int fmt);
+
+/*
+ * moe_grouped_mlp_bwd — the whole backward of the routed expert path in one
+ * call (TE DeepSeekV3Layer page, Performance section, "Where the time
+ * goes": the fused grouped MLP's dGLU bwd and wgrad in MXFP8, the local
+ * permute's reduce). Routing weights are constants; quantizers pass
+ * gradients straight through. On `stream` it runs, in order:
+ *   dY rows = topk_w[t, j] * dout[t] (fp32, MX-encoded along H)
+ *   dH = dY . W2, dA = SwiGLU'(dH; A) with A = act_save (dA in MX along 2F
+ *     and in fp32)
+ *   dX rows = dA . W1 (bf16); dx[t] = sum_j dX rows[row_map[t, j]] (fp32 in
+ *     slot order, rounded to act_fmt)
+ *   dw2[e] = dY_e^T . h_e, dw1[e] = dA_e^T . x_e over the rows of each
+ *     expert segment, operands MX-quantized along those rows in blocks of 32
+ *     (dY formed again from dout and the routing weights, h recomputed from
+ *     act_save); an expert with no rows gets exact zeros.
+ * dout, x   [T, H] in act_fmt (MOE_BF16 or MOE_F32); dx [T, H] out in act_fmt.
+ * row_map [T, k], src_row [rows], offsets [E+1] (moe_permute's maps with
+ *          align 32, so every segment is a whole number of 32-row blocks),
+ *          topk_w [T, k] fp32 (moe_route's weights).
+ * act_save [rows, 2F] fp32: the forward's fc1 output (gate | up).
+ * w1t [E, H, 2F] and w2t [E, F, H]: the transposed weight copies, MX-
+ *          quantized along their contraction axis and packed by
+ *          moe_pack_weights (half = 0), with their packed scales.
+ * dw1 [E, 2F, H], dw2 [E, H, F] bf16 out.
+ * ws       moe_grouped_mlp_bwd_workspace(T, k, E, H, F, rows, fmt) bytes,
+ *          16-byte aligned.
+ * Limits: fmt MOE_MXFP8_E4M3; H % 128 == 0, F % 128 == 0, 1 <= E <= 1024,
+ * 1 <= k <= 16, T * k <= rows < 2^31. All checks run before the first
+ * kernel is enqueued. With T == 0, dout, x, row_map, topk_w and dx may be
+ * NULL (dw1 and dw2 are still written: all zeros).
+ */
+int moe_grouped_mlp_bwd(const void* dout, const void* x, int act_fmt,
+                        const int32_t* row_map, const int32_t* src_row,
+                        const float* topk_w, const int32_t* offsets,
+                        const float* act_save, const void* w1t,
+                        const uint8_t* w1t_scales, const void* w2t,
+                        const uint8_t* w2t_scales, int fmt, int T, int k, int E,
+                        int H, int F, int64_t rows, void* dx, void* dw1,
+                        void* dw2, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

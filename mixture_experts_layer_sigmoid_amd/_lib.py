@@ -49,6 +49,9 @@ SIGNATURES = {
     "moe_grouped_fc2_dgrad_dswiglu": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I64, _P, _P, _P, _P, _P]),
     "moe_grouped_fc1_dgrad": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I64, _P, _P]),
     "moe_grouped_wgrad": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _P]),
+    "moe_grouped_mlp_bwd_workspace": (_SZ, [_I, _I, _I, _I, _I, _I64, _I]),
+    "moe_grouped_mlp_bwd": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                 _I, _I64, _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -244,3 +247,17 @@ def moe_grouped_wgrad(at, at_scales, bt, bt_scales, fmt, kofs, E, M, N, kstride,
 def moe_pack_weights(w, w_scales, fmt, E, N, K, half, out, out_scales, stream=None):
     _check("moe_pack_weights", load().moe_pack_weights(
         _ptr(w), _ptr(w_scales), fmt, E, N, K, half, _ptr(out), _ptr(out_scales), _stream(stream)))
+
+
+def moe_grouped_mlp_bwd_workspace(T, k, E, H, F, rows, fmt) -> int:
+    return load().moe_grouped_mlp_bwd_workspace(T, k, E, H, F, rows, fmt)
+
+
+def moe_grouped_mlp_bwd(dout, x, act_fmt, row_map, src_row, topk_w, offsets, act_save, w1t,
+                        w1t_scales, w2t, w2t_scales, fmt, T, k, E, H, F, rows, dx, dw1, dw2, ws,
+                        stream=None):
+    _check("moe_grouped_mlp_bwd", load().moe_grouped_mlp_bwd(
+        _ptr(dout), _ptr(x), act_fmt, _ptr(row_map), _ptr(src_row), _ptr(topk_w), _ptr(offsets),
+        _ptr(act_save), _ptr(w1t), _ptr(w1t_scales), _ptr(w2t), _ptr(w2t_scales), fmt, T, k, E, H,
+        F, rows, _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))

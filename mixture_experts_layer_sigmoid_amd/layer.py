@@ -4,12 +4,19 @@ The object preallocates every buffer the pass needs (torch device memory)
 and then issues, on one stream:
 
     moe_route -> [moe_quantize_mx of x] -> moe_permute (maps only)
-      -> moe_grouped_mlp_fwd (routed experts, rows gathered through src_row)
-      -> [moe_grouped_mlp_fwd for the shared expert, E = 1]
+      -> moe_grouped_fc1_swiglu_dense -> moe_grouped_fc2_dense
+         (routed experts, rows gathered through src_row, and the shared
+         expert in the same launches)
       -> moe_combine
 
+Without a shared expert, or when it cannot share the routed launches (fp32
+layers, F_shared != F), the routed experts run through
+moe_grouped_fc1_swiglu / moe_grouped_fc2 and the shared expert through the
+same two calls with E = 1.
+
 MoEBackward runs the backward of the routed expert path (MXFP8), reusing
-the forward's routing and maps:
+the forward's routing and maps, as one moe_grouped_mlp_bwd call, whose
+steps are (and can also be issued one by one):
 
     moe_combine_bwd (dY rows, MX) -> moe_grouped_fc2_dgrad_dswiglu
       -> moe_grouped_fc1_dgrad -> moe_unpermute
@@ -284,7 +291,13 @@ class MoEBackward:
     save_act=True, MXFP8). Produces dx [T, H] (gradient through the routed
     experts) and the weight gradients dw1 [E, 2F, H], dw2 [E, H, F] (bf16).
     Routing weights are constants and the quantizers pass gradients straight
-    through."""
+    through.
+
+    Calling the object runs the whole backward as one moe_grouped_mlp_bwd
+    call on a preallocated workspace. The step methods (data_grad,
+    operands_dw2, gemm_dw2, operands_dw1, gemm_dw1) issue the same kernels
+    one C call at a time on buffers of their own (allocated on first use),
+    so each step can be timed or checked by itself."""
 
     def __init__(self, fwd: MoEForward):
         if fwd.fmt != "mxfp8":
@@ -294,7 +307,24 @@ class MoEBackward:
         self.fwd = fwd
         T, H, F, E, bound = fwd.T, fwd.H, fwd.F, fwd.E, max(1, fwd.bound)
         dev = fwd.topk_idx.device
-        u8, bf = dict(dtype=torch.uint8, device=dev), dict(dtype=torch.bfloat16, device=dev)
+        self.dev = dev
+        bf = dict(dtype=fwd.act_dtype, device=dev)
+        self.dx = torch.empty((T, H), **bf)
+        self.dw1 = torch.empty((E, 2 * F, H), dtype=torch.bfloat16, device=dev)
+        self.dw2 = torch.empty((E, H, F), dtype=torch.bfloat16, device=dev)
+        nws = L.moe_grouped_mlp_bwd_workspace(T, fwd.k, E, H, F, bound, FMT["mxfp8"])
+        if nws == 0:
+            raise ValueError("moe_grouped_mlp_bwd does not support these sizes")
+        self.ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+        self._staged = False
+
+    def stage_buffers(self):
+        """Buffers of the one-call-per-step path."""
+        if self._staged:
+            return
+        fwd, dev = self.fwd, self.dev
+        H, F, E, bound = fwd.H, fwd.F, fwd.E, max(1, fwd.bound)
+        u8 = dict(dtype=torch.uint8, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)
         self.dy_q = torch.empty((bound, H), **u8)
         self.dy_sc = torch.empty((bound, H // 32), **u8)
@@ -302,8 +332,7 @@ class MoEBackward:
         self.da = torch.empty((bound, 2 * F), **u8)
         self.da_sc = torch.empty((bound, 2 * F // 32), **u8)
         self.da_f32 = torch.empty((bound, 2 * F), **f32)
-        self.dx_perm = torch.empty((bound, H), **bf)
-        self.dx = torch.empty((T, H), **bf)
+        self.dx_perm = torch.empty((bound, H), dtype=torch.bfloat16, device=dev)
         ks = L.moe_segments_kstride(fwd.bound, E)
         self.kstride = ks
         self.kofs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
@@ -311,11 +340,11 @@ class MoEBackward:
         self.hT, self.hT_sc = torch.empty((F, ks), **u8), torch.empty((F, ks // 32), **u8)
         self.daT, self.daT_sc = torch.empty((2 * F, ks), **u8), torch.empty((2 * F, ks // 32), **u8)
         self.xT, self.xT_sc = torch.empty((H, ks), **u8), torch.empty((H, ks // 32), **u8)
-        self.dw1 = torch.empty((E, 2 * F, H), **bf)
-        self.dw2 = torch.empty((E, H, F), **bf)
+        self._staged = True
 
     def data_grad(self, dout, ew: ExpertWeights, stream=None):
         """dY rows -> dA (SwiGLU backward fused) -> dX rows -> dx."""
+        self.stage_buffers()
         f, fw = FMT["mxfp8"], self.fwd
         T, H, F, E, k, rows = fw.T, fw.H, fw.F, fw.E, fw.k, fw.bound
         L.moe_combine_bwd(dout, fw.act_fmt, fw.row_map, fw.src_row, fw.topk_w, T, k, H, rows,
@@ -325,7 +354,7 @@ class MoEBackward:
                                         self.da_f32, stream)
         L.moe_grouped_fc1_dgrad(self.da, self.da_sc, f, ew.w1t, ew.w1t_sc, fw.offsets, E, H, F,
                                 rows, self.dx_perm, stream)
-        L.moe_unpermute(self.dx_perm, L.MOE_BF16, fw.row_map, T, k, H, self.dx, L.MOE_BF16, stream)
+        L.moe_unpermute(self.dx_perm, L.MOE_BF16, fw.row_map, T, k, H, self.dx, fw.act_fmt, stream)
 
     def _seg(self, src, in_fmt, mode, scale, C, codes, scales, stream):
         fw = self.fwd
@@ -337,6 +366,7 @@ class MoEBackward:
         """The dW2 operands in the stage-major segment layout: dY rows formed
         as w * dout, h recomputed from the saved fc1 output, both MX
         quantized along the rows of each expert segment."""
+        self.stage_buffers()
         fw = self.fwd
         self._seg(dout, fw.act_fmt, 1, self.row_w, fw.H, self.dyT, self.dyT_sc, stream)
         self._seg(fw.act_save, L.MOE_F32, 2, None, fw.F, self.hT, self.hT_sc, stream)
@@ -349,6 +379,7 @@ class MoEBackward:
 
     def operands_dw1(self, x, stream=None):
         """The dW1 operands: dA (its fp32 copy) and the token rows x."""
+        self.stage_buffers()
         fw = self.fwd
         self._seg(self.da_f32, L.MOE_F32, 0, None, 2 * fw.F, self.daT, self.daT_sc, stream)
         self._seg(x, fw.act_fmt, 1, None, fw.H, self.xT, self.xT_sc, stream)
@@ -359,19 +390,20 @@ class MoEBackward:
         L.moe_grouped_wgrad(self.daT, self.daT_sc, self.xT, self.xT_sc, FMT["mxfp8"], self.kofs,
                             fw.E, 2 * fw.F, fw.H, self.kstride, self.dw1, stream)
 
-    def weight_grad_dw2(self, dout, stream=None):
+    def staged(self, dout, x, ew: ExpertWeights, stream=None):
+        """The whole backward one C call per step."""
+        self.data_grad(dout, ew, stream)
         self.operands_dw2(dout, stream)
         self.gemm_dw2(stream)
-
-    def weight_grad_dw1(self, x, stream=None):
         self.operands_dw1(x, stream)
         self.gemm_dw1(stream)
-
-    def weight_grad(self, dout, x, stream=None):
-        self.weight_grad_dw2(dout, stream)
-        self.weight_grad_dw1(x, stream)
+        return self.dx, self.dw1, self.dw2
 
     def __call__(self, dout, x, ew: ExpertWeights, stream=None):
-        self.data_grad(dout, ew, stream)
-        self.weight_grad(dout, x, stream)
+        """The whole backward in one moe_grouped_mlp_bwd call."""
+        fw = self.fwd
+        L.moe_grouped_mlp_bwd(dout, x, fw.act_fmt, fw.row_map, fw.src_row, fw.topk_w, fw.offsets,
+                              fw.act_save, ew.w1t, ew.w1t_sc, ew.w2t, ew.w2t_sc, FMT["mxfp8"], fw.T,
+                              fw.k, fw.E, fw.H, fw.F, max(1, fw.bound), self.dx, self.dw1,
+                              self.dw2, self.ws, stream)
         return self.dx, self.dw1, self.dw2

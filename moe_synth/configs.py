@@ -116,6 +116,18 @@ DSV4_SKEW_MXFP8 = MoEConfig(
     bias_kind="zipf", bias_range=0.0, backward=True, align=32, zipf_s=1.1,
     n_zero_experts=8)
 
+# One expert-parallel rank's share at DeepSeek-V3 dims ([TE-DSV3] Performance
+# section, setup: 8 experts per rank, top-k 8, 4096 tokens per rank): the 8
+# local experts each receive 4096 rows, here from 4096 tokens routed top-8
+# over exactly those 8 experts, MXFP8 forward and backward (the fused
+# grouped MLP's fc1+SwiGLU, fc2, dGLU and wgrad). No shared expert: the
+# pages time it with the dense GEMMs, not the grouped MLP.
+DSV3_EP_SHARE = MoEConfig(
+    name="dsv3_ep8_mxfp8_t4096", family="dsv3_ep8", T=4096, H=7168, F=2048,
+    E=8, n_group=1, topk_group=1, k=8, routed_scale=2.5, n_shared=0,
+    F_shared=0, fmt="mxfp8", x_std=1.0, router_std=1.0 / math.sqrt(7168),
+    bias_kind="uniform", bias_range=0.05, backward=True, align=32)
+
 # -- reduced shapes of the same structure, small enough for full parity ----
 # (several GEMM tiles along every axis, ragged token counts)
 MINI_BF16 = replace(
@@ -130,6 +142,9 @@ MINI_MXFP4 = replace(
 MINI_SKEW = replace(
     DSV4_SKEW_MXFP8, name="mini_skew_mxfp8", family="mini_skew", T=300,
     H=512, F=384, E=48, router_std=1.0 / math.sqrt(512), n_zero_experts=2)
+MINI_EP_SHARE = replace(
+    DSV3_EP_SHARE, name="mini_ep8_mxfp8", family="mini_ep8", T=300, H=512, F=256,
+    router_std=1.0 / math.sqrt(512))
 MINI_FP32 = replace(
     TINY_FP32, name="mini_fp32", family="mini_fp32", T=333, H=320, F=192,
     E=24, n_group=6, topk_group=3, k=5, x_std=1.0,
@@ -137,8 +152,8 @@ MINI_FP32 = replace(
 
 ALL = {c.name: c for c in (
     TINY_FP32, TINY_FP32_UNITX, DSV3_BF16, DSV3_MXFP8_DECODE, DSV4_MXFP4,
-    DSV4_SKEW_MXFP8, MINI_BF16, MINI_MXFP8_DECODE, MINI_MXFP4, MINI_SKEW,
-    MINI_FP32)}
+    DSV4_SKEW_MXFP8, DSV3_EP_SHARE, MINI_BF16, MINI_MXFP8_DECODE, MINI_MXFP4,
+    MINI_SKEW, MINI_EP_SHARE, MINI_FP32)}
 
 # The workload the headline throughput is quoted on.
 HEADLINE = DSV3_BF16

@@ -245,3 +245,35 @@ def test_shared_fold_selection_and_buffers(lib):
         moe.MoEForward(T=4, fmt="bf16", F_shared=256, fuse_shared=True, **kw)
     with pytest.raises(RuntimeError):
         fw.shared(None, None)
+
+
+def test_grouped_mlp_bwd_validation(lib):
+    """moe_grouped_mlp_bwd checks everything before its first kernel."""
+    T, k, E, H, F, rows = 64, 6, 48, 512, 384, 64 * 6 + 48 * 31
+    need = lib.moe_grouped_mlp_bwd_workspace(T, k, E, H, F, rows, 2)
+    assert need > 0
+    assert lib.moe_grouped_mlp_bwd_workspace(T, k, E, H, F, rows, 1) == 0    # MXFP8 only
+    assert lib.moe_grouped_mlp_bwd_workspace(T, k, E, 500, F, rows, 2) == 0  # H % 128
+    assert lib.moe_grouped_mlp_bwd_workspace(T, k, E, H, F, T * k - 1, 2) == 0
+
+    def call(**kw):
+        a = dict(dout=A, x=A, af=1, rm=A, src=A, tw=A, off=A, save=A, w1t=A, w1s=A, w2t=A, w2s=A,
+                 f=2, T=T, k=k, E=E, H=H, F=F, rows=rows, dx=A, dw1=A, dw2=A, ws=A, wsb=need)
+        a.update(kw)
+        return lib.moe_grouped_mlp_bwd(a["dout"], a["x"], a["af"], a["rm"], a["src"], a["tw"],
+                                       a["off"], a["save"], a["w1t"], a["w1s"], a["w2t"], a["w2s"],
+                                       a["f"], a["T"], a["k"], a["E"], a["H"], a["F"], a["rows"],
+                                       a["dx"], a["dw1"], a["dw2"], a["ws"], a["wsb"], None)
+    assert call(f=3) == UNSUPPORTED
+    assert call(af=2) == UNSUPPORTED
+    assert call(k=17) == INVALID
+    assert call(F=200) == INVALID
+    assert call(E=1025) == INVALID
+    assert call(rows=T * k - 1) == INVALID
+    assert call(src=None) == INVALID
+    assert call(dout=None) == INVALID
+    assert call(dw1=A + 8) == ALIGN
+    assert call(w1s=A + 2) == ALIGN
+    assert call(wsb=need - 1) == WS
+    assert call(ws=None) == WS
+    assert b"moe_grouped_mlp_bwd_workspace" in lib.moe_last_error()

@@ -13,6 +13,8 @@ exact zeros) and the full-size one on its busiest expert (all 8192 rows), a
 mid-size and a light expert plus the zero-row experts, with a property
 check of the un-permute on sampled tokens and a repeat of the whole
 backward that must give the same bits."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -227,21 +229,32 @@ def test_wgrad_ragged_segments(gpu_lib, M, N, T):
         assert rel_l2(got[e], ref) < TOL, e
 
 
-def _gpu_backward(cfg, x_d, wr_d, b_d, w1, w2, dout_d):
+def _gpu_backward(cfg, x_d, wr_d, b_d, w1, w2, dout_d, staged=False):
+    """Forward, then the backward: one moe_grouped_mlp_bwd call, or (staged)
+    one C call per step, keeping the intermediate buffers."""
     ew = moe.ExpertWeights.from_dense(w1, w2, cfg.fmt, transposed=True)
     fw = moe.MoEForward.for_config(cfg, save_act=True, keep_logits=True)
     fw(x_d, wr_d, b_d, ew)
     bw = moe.MoEBackward(fw)
-    bw(dout_d, x_d, ew)
+    if staged:
+        bw.staged(dout_d, x_d, ew)
+    else:
+        bw(dout_d, x_d, ew)
     torch.cuda.synchronize()
     return fw, bw, ew
 
 
-def test_backward_reduced_skewed(gpu_lib):
-    cfg = configs.get("mini_skew_mxfp8")
+@pytest.mark.parametrize("name", ["mini_skew_mxfp8", "mini_ep8_mxfp8"])
+def test_backward_reduced(gpu_lib, name):
+    """Every element of dx, dW1 and dW2 against the oracle: the skewed layer
+    (empty experts, experts of one 32-row block and of many) and the
+    expert-parallel share (8 experts of 300 rows each, segments padded to
+    320)."""
+    cfg = configs.get(name)
     log(f"backward end to end {cfg.name}")
     h, d = device_inputs(cfg)
-    fw, bw, _ = _gpu_backward(cfg, d["x"], d["w_router"], d["bias"], d["w1"], d["w2"], d["dout"])
+    # (the one-call moe_grouped_mlp_bwd)
+    fw, bw, ew = _gpu_backward(cfg, d["x"], d["w_router"], d["bias"], d["w1"], d["w2"], d["dout"])
     olog = rt.router_logits(h["x"], h["w_router"])
     oidx, ow, _, _ = rt.route(olog, h["bias"], cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
     assert np.array_equal(host(fw.topk_idx), oidx)
@@ -252,7 +265,10 @@ def test_backward_reduced_skewed(gpu_lib):
     log(f"  dx rel L2 {err:.2e}")
     assert err < TOL
     counts = np.bincount(oidx.ravel(), minlength=cfg.E)
-    assert (counts == 0).sum() >= 1, "the skewed routing leaves some experts without rows"
+    if cfg.bias_kind == "zipf":
+        assert (counts == 0).sum() >= 1, "the skewed routing leaves some experts without rows"
+    else:
+        assert (counts == cfg.T).all(), "top-8 of 8 experts: every expert gets every token"
     dw1, dw2 = host(bw.dw1), host(bw.dw2)
     for e in range(cfg.E):
         if counts[e] == 0:
@@ -264,18 +280,44 @@ def test_backward_reduced_skewed(gpu_lib):
     # per-expert bar for every expert with rows
     for e in np.nonzero(counts)[0]:
         assert rel_l2(dw1[e], ref["dw1"][e]) < TOL and rel_l2(dw2[e], ref["dw2"][e]) < TOL, e
+    # the same backward one C call per step gives the same bits
+    first = [t.clone() for t in (bw.dx, bw.dw1, bw.dw2)]
+    bw.staged(d["dout"], d["x"], ew)
+    torch.cuda.synchronize()
+    for name, a, b in zip(["dx", "dW1", "dW2"], first, (bw.dx, bw.dw1, bw.dw2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+
+
+def test_backward_empty_batch(gpu_lib):
+    """T = 0: moe_grouped_mlp_bwd writes exact zeros to every weight
+    gradient and nothing else."""
+    cfg = dataclasses.replace(configs.get("mini_skew_mxfp8"), T=0)
+    log("backward with T = 0")
+    h, d = device_inputs(dataclasses.replace(cfg, T=1))
+    ew = moe.ExpertWeights.from_dense(d["w1"], d["w2"], cfg.fmt, transposed=True)
+    fw = moe.MoEForward.for_config(cfg, save_act=True)
+    fw.route(d["x"][:0], d["w_router"], d["bias"])
+    fw.permute()                  # empty segments; every row is padding
+    fw.act_save.zero_()
+    bw = moe.MoEBackward(fw)
+    bw.dw1.fill_(3.0)
+    bw.dw2.fill_(3.0)
+    bw(d["dout"][:0], d["x"][:0], ew)
+    torch.cuda.synchronize()
+    assert not bw.dw1.any().item() and not bw.dw2.any().item()
 
 
 @pytest.mark.timeout(900)
-def test_backward_full_size_sampled(gpu_lib):
-    cfg = configs.get("dsv4_skew_mxfp8_t8192")
+@pytest.mark.parametrize("name", ["dsv4_skew_mxfp8_t8192", "dsv3_ep8_mxfp8_t4096"])
+def test_backward_full_size_sampled(gpu_lib, name):
+    cfg = configs.get(name)
     log(f"full-size backward {cfg.name}: generating weights on the device")
     x, wr, b = gen.host_x(cfg), gen.host_router(cfg), gen.host_bias(cfg)
     dout = gen.host_dout(cfg)
     wts = gen.device_expert_weights(cfg, "cuda")
     x_d = dev(x, "bf16")
     fw, bw, ew = _gpu_backward(cfg, x_d, dev(wr, "bf16"), dev(b), wts["w1"], wts["w2"],
-                               dev(dout, "bf16"))
+                               dev(dout, "bf16"), staged=True)
     log("  forward + backward done; oracle routing of all tokens")
     olog = rt.router_logits(x, wr)
     oidx, ow, os_, osel = rt.route(olog, b, cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
@@ -283,23 +325,29 @@ def test_backward_full_size_sampled(gpu_lib):
     nbad, unc, bad_tok = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group,
                                                   margin=tie_margin(host(fw.logits), olog))
     log(f"  routing: {nbad} certified near-tie tokens, {unc} uncertified")
-    assert unc == 0 and nbad <= max_tie_tokens(cfg.T)
+    assert unc == 0 and nbad <= max_tie_tokens(cfg.T, cfg.bias_kind)
     # the oracle follows the GPU's expert lists (identical but for certified
     # ties), with its own normalized scores as combine weights
     w_or = rt.combine_weights(os_, idx, cfg.routed_scale)
     counts = np.bincount(idx.ravel(), minlength=cfg.E)
     dw1_d, dw2_d = bw.dw1, bw.dw2
     zero = [e for e in range(cfg.E) if counts[e] == 0]
-    assert len(zero) >= 1
+    assert len(zero) >= 1 or cfg.bias_kind != "zipf"
     for e in zero:
         assert not dw1_d[e].any().item() and not dw2_d[e].any().item(), e
-    # the busiest expert (all its rows: several row tiles in the data-gradient
-    # GEMMs, weight-gradient tiles split across the XCDs), a mid-size one and
-    # a light one (one or two 32-row blocks): oracle backward of all their rows
+    # skewed batch: the busiest expert (all its rows: several row tiles in the
+    # data-gradient GEMMs, weight-gradient tiles split across the XCDs), a
+    # mid-size one and a light one (one or two 32-row blocks); expert-parallel
+    # share: two of its 8 experts of 4096 rows. Oracle backward of all their
+    # rows.
     nz = np.nonzero(counts)[0]
-    heavy = int(np.argmax(counts))
-    mid = int(nz[np.argsort(counts[nz], kind="stable")[len(nz) // 2]])
-    light = int([e for e in nz if 20 <= counts[e] <= 60][0])
+    if cfg.bias_kind == "zipf":
+        heavy = int(np.argmax(counts))
+        mid = int(nz[np.argsort(counts[nz], kind="stable")[len(nz) // 2]])
+        light = int([e for e in nz if 20 <= counts[e] <= 60][0])
+        check = [heavy, mid, light]
+    else:
+        check = [0, cfg.E - 3]
     row_map = host(fw.row_map)
     from oracle import mlp as omlp
     lock = __import__("threading").Lock()
@@ -317,11 +365,10 @@ def test_backward_full_size_sampled(gpu_lib):
         a_ref = omlp.operand(x[t], cfg.fmt) @ omlp.operand(w1, cfg.fmt).T
         return (e, t, j, a_ref) + obw.expert_backward(x[t], dy, w1, w2, cfg.fmt)
 
-    log(f"  oracle backward of experts {heavy} ({counts[heavy]} rows), {mid} ({counts[mid]}), "
-        f"{light} ({counts[light]}), concurrently")
+    log(f"  oracle backward of experts {check} (rows {counts[check].tolist()}), concurrently")
     from concurrent.futures import ThreadPoolExecutor
-    with ThreadPoolExecutor(max_workers=3) as ex:
-        results = list(ex.map(one, [heavy, mid, light]))
+    with ThreadPoolExecutor(max_workers=len(check)) as ex:
+        results = list(ex.map(one, check))
     worst = 0.0
     for e, t, j, a_ref, dx_e, dw1_e, dw2_e in results:
         rows = torch.from_numpy(row_map[t, j]).cuda()
@@ -346,20 +393,28 @@ def test_backward_full_size_sampled(gpu_lib):
         acc = (acc + rows_h[:, jj]).astype(np.float32)
     assert np.array_equal(host(bw.dx[torch.from_numpy(toks).cuda()]), _bf16(acc))
     assert np.isfinite(host(bw.dx)).all()
-    # a second backward of the same inputs gives the same bits (row
-    # fingerprints of the weight gradients, whole dA and dX rows)
+    # a second, staged backward of the same inputs gives the same bits (row
+    # fingerprints of the weight gradients, whole dA and dX rows), and the
+    # one-call backward (moe_grouped_mlp_bwd) the same dx and weight
+    # gradients as the staged calls
     del wts
     fp = lambda t: t.view(torch.int16).reshape(-1, t.shape[-1]).sum(dim=1, dtype=torch.int64)
     used = int(fw.offsets[-1].item())          # rows past the last segment are never written
-    first = (bw.da_f32[:used].clone(), bw.dx_perm[:used].clone(), fp(bw.dw1), fp(bw.dw2))
-    bw.dw1.zero_()
-    bw.dw2.zero_()
-    bw.dx_perm.zero_()
-    bw.da_f32.zero_()
+    first = (bw.da_f32[:used].clone(), bw.dx_perm[:used].clone(), fp(bw.dw1), fp(bw.dw2),
+             bw.dx.clone())
+    for t_ in (bw.dw1, bw.dw2, bw.dx_perm, bw.da_f32, bw.dx):
+        t_.zero_()
+    bw.staged(dev(dout, "bf16"), x_d, ew)
+    torch.cuda.synchronize()
+    again = (bw.da_f32[:used], bw.dx_perm[:used], fp(bw.dw1), fp(bw.dw2), bw.dx)
+    bits = lambda t: t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+    same = lambda a, b_: torch.equal(bits(a) if a.dtype != torch.int64 else a,
+                                     bits(b_) if b_.dtype != torch.int64 else b_)
+    for name, a, b_ in zip(["dA fp32", "dX rows", "dW1 rows", "dW2 rows", "dx"], first, again):
+        assert same(a, b_), name
+    for t_ in (bw.dw1, bw.dw2, bw.dx):
+        t_.zero_()
     bw(dev(dout, "bf16"), x_d, ew)
     torch.cuda.synchronize()
-    again = (bw.da_f32[:used], bw.dx_perm[:used], fp(bw.dw1), fp(bw.dw2))
-    bits = lambda t: t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
-    for name, a, b_ in zip(["dA fp32", "dX rows", "dW1 rows", "dW2 rows"], first, again):
-        assert torch.equal(bits(a) if a.dtype != torch.int64 else a,
-                           bits(b_) if b_.dtype != torch.int64 else b_), name
+    for name, a, b_ in zip(["dW1 rows", "dW2 rows", "dx"], first[2:], (fp(bw.dw1), fp(bw.dw2), bw.dx)):
+        assert same(a, b_), f"one-call backward: {name}"

@@ -9,8 +9,8 @@ grouped MLP [-> shared expert] -> combine) against the oracle.
   oracle's permute of the GPU's expert lists, the combine weights, and the
   output of many tokens, every element: all 64 decode tokens; 256 tokens of
   the 4096-token batch that together reach every expert; 64 tokens of the
-  MXFP4 batch; tokens of the skewed batch that include rows of its busiest
-  expert. Tie tokens are always among them, checked against the oracle
+  MXFP4 batch and of the expert-parallel share (8 experts x 4096 rows);
+  tokens of the skewed batch that include rows of its busiest expert. Tie tokens are always among them, checked against the oracle
   driven by the GPU's expert lists. Weights are copied from the seeded
   device generator.
 * Repeated expert GEMM launches give identical bits (bf16, MXFP8, MXFP4).
@@ -52,7 +52,8 @@ def _forward_small(cfg):
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "tiny_fp32_unitx", "mini_fp32", "mini_bf16",
-                                  "mini_mxfp8_decode", "mini_mxfp4", "mini_skew_mxfp8"])
+                                  "mini_mxfp8_decode", "mini_mxfp4", "mini_skew_mxfp8",
+                                  "mini_ep8_mxfp8"])
 def test_small_end_to_end(gpu_lib, name):
     cfg = configs.get(name)
     log(f"end-to-end {name}")
@@ -215,7 +216,7 @@ def _sample_tokens(name, idx, E, T):
         return np.arange(T)                                   # every token
     if name == "dsv3_bf16_t4096":
         return _covering_tokens(idx, E, 256, 12)              # every expert reached
-    if name == "dsv4_mxfp4_t16384":
+    if name in ("dsv4_mxfp4_t16384", "dsv3_ep8_mxfp8_t4096"):
         return np.sort(g.choice(T, 64, replace=False))
     # skewed batch: 8 tokens of the busiest expert, 4 of a mid-size one, 4 more
     counts = np.bincount(idx.ravel(), minlength=E)
@@ -229,7 +230,7 @@ def _sample_tokens(name, idx, E, T):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["dsv3_mxfp8_decode_t64", "dsv3_bf16_t4096", "dsv4_mxfp4_t16384",
-                                  "dsv4_skew_mxfp8_t8192"])
+                                  "dsv4_skew_mxfp8_t8192", "dsv3_ep8_mxfp8_t4096"])
 def test_full_size_forward(gpu_lib, name):
     cfg = configs.get(name)
     log(f"full-size forward {name}: generating weights on the device")
@@ -251,7 +252,7 @@ def test_full_size_forward(gpu_lib, name):
                                               margin=margin)
     log(f"  routing: max |logit diff| gives margin {margin:.2e}; {nbad} certified near-tie tokens "
         f"{bad.tolist()}, {unc} uncertified")
-    assert unc == 0 and nbad <= max_tie_tokens(cfg.T)
+    assert unc == 0 and nbad <= max_tie_tokens(cfg.T, cfg.bias_kind)
     # maps bit for bit against the oracle's permute of the GPU's expert lists
     counts, offsets, row_map, src = pm.permute_maps(idx, cfg.E, cfg.align)
     assert np.array_equal(host(fw.counts), counts)

@@ -66,7 +66,7 @@ def test_gemm_path_small(gpu_lib, name):
     oidx, ow, _, osel = rt.route(olog, b, cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
     nbad, unc, _ = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group,
                                             margin=tie_margin(lo, olog))
-    assert unc == 0 and nbad <= max_tie_tokens(cfg.T)
+    assert unc == 0 and nbad <= max_tie_tokens(cfg.T, cfg.bias_kind)
     same = (idx == oidx).all(axis=1)
     assert rel_l2(w[same], ow[same]) < 1e-5
 
@@ -88,7 +88,7 @@ def test_gemm_path_full_size(gpu_lib, name):
                                               margin=margin)
     log(f"  {name}: margin {margin:.2e}; {nbad} mismatched tokens of {cfg.T} {bad.tolist()}, "
         f"{unc} uncertified")
-    assert unc == 0 and nbad <= max_tie_tokens(cfg.T)
+    assert unc == 0 and nbad <= max_tie_tokens(cfg.T, cfg.bias_kind)
     same = (idx == oidx).all(axis=1)
     assert rel_l2(w[same], ow[same]) < 1e-5
     # the same call again gives the same bits
@@ -112,6 +112,6 @@ def test_gemm_path_full_hidden(gpu_lib, name):
     oidx, ow, _, osel = rt.route(olog, b, cfg.n_group, cfg.topk_group, cfg.k, cfg.routed_scale)
     nbad, unc, _ = certified_tie_mismatches(osel, idx, oidx, cfg.n_group, cfg.topk_group,
                                             margin=tie_margin(lo, olog))
-    assert unc == 0 and nbad <= max_tie_tokens(cfg.T)
+    assert unc == 0 and nbad <= max_tie_tokens(cfg.T, cfg.bias_kind)
     same = (idx == oidx).all(axis=1)
     assert ulp_diff_f32(w[same], ow[same]).max() <= 64     # fp32 logits vs fp64 logits
