@@ -19,12 +19,13 @@ Pages cited (by title):
 
 Modules: routing (router GEMM, sigmoid, grouped top-k, combine weights),
 permute (maps, gather, summing un-permute), mx (MX quantizer), mlp (expert
-MLP, combine, layer forward), backward (routed expert backward), zipf (the
-calibration that writes the skewed config's stored bias).
+MLP, combine, layer forward), backward (routed expert backward),
+router_train (router backward, sequence-wise balance loss, bias update), zipf
+(the calibration that writes the skewed config's stored bias).
 
 Parity pins: every function here is checked in tests/test_oracle_*.py
 against brute force, closed forms, invariants or library routines; see those
 files' docstrings. The pages print no worked numeric example, so no value is
 pinned to the pages themselves.
 """
-from . import mx, routing, permute, mlp, backward  # noqa: F401
+from . import mx, routing, permute, mlp, backward, router_train  # noqa: F401
