@@ -527,6 +527,59 @@ int moe_grouped_mlp_bwd(const void* dout, const void* x, int act_fmt,
                         int H, int F, int64_t rows, void* dx, void* dw1,
                         void* dw2, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * ---- Training steps around the routing (TE DeepSeekV3Layer page,
+ * Description, DeepSeekV3MoE item: sigmoid router with an aux-loss-free
+ * bias and grouped top-k; Changes section: optional sequence-wise aux
+ * loss). The pages give no formula; these are the DeepSeek-V3 rules.
+ */
+
+/* moe_route_bwd_workspace — scratch bytes of moe_route_bwd (0 if invalid;
+ * seq_len 0 when the balance loss is off). */
+size_t moe_route_bwd_workspace(int T, int H, int E, int seq_len);
+
+/*
+ * moe_route_bwd — the router backward of one layer pass. The expert lists
+ * are constants and the bias takes no gradient (it only selects):
+ *   dw[t, j]   = <dout[t], y[row_map[t, j]]>   (fp32)
+ *   ds[t, e_j] = routed_scale / S_t * (dw[t, j] - sum_i dw[t, i] s[t, e_i] / S_t),
+ *                s = sigmoid(logits), S_t = sum_j s[t, e_j]; 0 off the list
+ *   dlogits    = ds * s * (1 - s)
+ *                + (aux_alpha != 0) the sequence-wise balance-loss gradient:
+ *                loss = aux_alpha * mean over sequences of L = seq_len
+ *                consecutive tokens of sum_i f_i P_i, f_i = E / (k L) *
+ *                (tokens of the sequence selecting i), P_i = mean over the
+ *                sequence of s[t, i] / sum_m s[t, m]
+ *   dx_router  = dlogits . w_router   [T, H] bf16
+ *   dw_router  = dlogits^T . x        [E, H] fp32
+ * The two products run on bf16 matrix cores with dlogits rounded to bf16
+ * (fp32 accumulation).
+ * dout [T, H], x [T, H], w_router [E, H], y [rows, H] (the forward's expert
+ *          output rows, before weighting) in act_fmt = MOE_BF16.
+ * row_map, topk_idx [T, k] int32 and logits [T, E] fp32: the forward's.
+ * dlogits optional [T, E] fp32 out; aux_loss [1] fp32 out (required when
+ *          aux_alpha != 0).
+ * Limits: E a multiple of 8 in [8, 512], 1 <= k <= min(16, E), H % 8 == 0,
+ * seq_len dividing T when aux_alpha != 0. T == 0 is a no-op.
+ */
+int moe_route_bwd(const void* dout, const void* y, int act_fmt,
+                  const int32_t* row_map, const int32_t* topk_idx,
+                  const float* logits, const void* x, const void* w_router, int T,
+                  int k, int E, int H, float routed_scale, int seq_len,
+                  float aux_alpha, float* dlogits, float* aux_loss,
+                  void* dx_router, float* dw_router, void* ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+/*
+ * moe_bias_update — the aux-loss-free bias update after a step:
+ *   bias_out[e] = bias[e] + gamma * sign(T k / E - counts[e])
+ * with counts the per-expert loads moe_permute wrote (T k their sum); the
+ * sign is taken exactly in integers, the sum is one fp32 addition.
+ * bias_out may equal bias. 1 <= E <= 1024.
+ */
+int moe_bias_update(const int32_t* counts, int E, float gamma, const float* bias,
+                    float* bias_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

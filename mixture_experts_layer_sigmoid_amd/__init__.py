@@ -17,7 +17,9 @@ from ._lib import (  # noqa: F401
     moe_grouped_fc1_swiglu_dense, moe_grouped_fc2_dense,
     moe_pack_weights, moe_combine_bwd, moe_unpermute, moe_segments_kstride, moe_quantize_mx_segments,
     moe_grouped_fc2_dgrad_dswiglu, moe_grouped_fc1_dgrad, moe_grouped_wgrad,
-    moe_grouped_mlp_bwd, moe_grouped_mlp_bwd_workspace,
+    moe_grouped_mlp_bwd, moe_grouped_mlp_bwd_workspace, moe_route_bwd, moe_route_bwd_workspace,
+    moe_bias_update,
     SIGNATURES, LIB_PATH,
 )
-from .layer import MoEForward, MoEBackward, ExpertWeights, quantize_mx, quantize_mx_t, FMT  # noqa: F401
+from .layer import (MoEForward, MoEBackward, RouterBackward, ExpertWeights, bias_update,  # noqa: F401
+                    quantize_mx, quantize_mx_t, FMT)

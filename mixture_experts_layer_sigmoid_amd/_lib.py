@@ -49,6 +49,10 @@ SIGNATURES = {
     "moe_grouped_fc2_dgrad_dswiglu": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I64, _P, _P, _P, _P, _P]),
     "moe_grouped_fc1_dgrad": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I64, _P, _P]),
     "moe_grouped_wgrad": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I64, _P, _P]),
+    "moe_route_bwd_workspace": (_SZ, [_I, _I, _I, _I]),
+    "moe_route_bwd": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _F, _P, _P, _P,
+                           _P, _P, _SZ, _P]),
+    "moe_bias_update": (_I, [_P, _I, _F, _P, _P, _P]),
     "moe_grouped_mlp_bwd_workspace": (_SZ, [_I, _I, _I, _I, _I, _I64, _I]),
     "moe_grouped_mlp_bwd": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                  _I, _I64, _P, _P, _P, _P, _SZ, _P]),
@@ -261,3 +265,22 @@ def moe_grouped_mlp_bwd(dout, x, act_fmt, row_map, src_row, topk_w, offsets, act
         _ptr(act_save), _ptr(w1t), _ptr(w1t_scales), _ptr(w2t), _ptr(w2t_scales), fmt, T, k, E, H,
         F, rows, _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_route_bwd_workspace(T, H, E, seq_len) -> int:
+    return load().moe_route_bwd_workspace(T, H, E, seq_len)
+
+
+def moe_route_bwd(dout, y, act_fmt, row_map, topk_idx, logits, x, w_router, T, k, E, H,
+                  routed_scale, seq_len, aux_alpha, dlogits, aux_loss, dx_router, dw_router, ws,
+                  stream=None):
+    _check("moe_route_bwd", load().moe_route_bwd(
+        _ptr(dout), _ptr(y), act_fmt, _ptr(row_map), _ptr(topk_idx), _ptr(logits), _ptr(x),
+        _ptr(w_router), T, k, E, H, routed_scale, seq_len, aux_alpha, _ptr(dlogits),
+        _ptr(aux_loss), _ptr(dx_router), _ptr(dw_router), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_bias_update(counts, E, gamma, bias, bias_out, stream=None):
+    _check("moe_bias_update", load().moe_bias_update(
+        _ptr(counts), E, gamma, _ptr(bias), _ptr(bias_out), _stream(stream)))

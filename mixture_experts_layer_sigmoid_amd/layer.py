@@ -407,3 +407,46 @@ class MoEBackward:
                               fw.k, fw.E, fw.H, fw.F, max(1, fw.bound), self.dx, self.dw1,
                               self.dw2, self.ws, stream)
         return self.dx, self.dw1, self.dw2
+
+
+class RouterBackward:
+    """Router backward of one MoEForward pass (bf16 layer built with
+    keep_logits=True): the combine-weight gradient against the forward's
+    expert output rows, pulled back through the weight normalization and the
+    sigmoid into the logits (plus, with aux_alpha, the sequence-wise balance
+    loss over sequences of seq_len tokens), then into the hidden states
+    (dx [T, H] bf16) and the router weight (dw [E, H] fp32), in one
+    moe_route_bwd call."""
+
+    def __init__(self, fwd: MoEForward, seq_len: int = 0, aux_alpha: float = 0.0):
+        if fwd.logits is None:
+            raise ValueError("the forward must keep its router logits (keep_logits=True)")
+        if fwd.act_fmt != L.MOE_BF16:
+            raise ValueError("the router backward runs on bf16 layers")
+        self.fwd, self.seq_len, self.aux_alpha = fwd, seq_len, aux_alpha
+        T, H, E = fwd.T, fwd.H, fwd.E
+        dev = fwd.topk_idx.device
+        nws = L.moe_route_bwd_workspace(max(1, T), H, E, seq_len if aux_alpha else 0)
+        if nws == 0:
+            raise ValueError("moe_route_bwd does not support these sizes")
+        self.ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+        self.dlogits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        self.aux_loss = torch.zeros((1,), dtype=torch.float32, device=dev)
+        self.dx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.dw = torch.empty((E, H), dtype=torch.float32, device=dev)
+
+    def __call__(self, dout, x, w_router, stream=None):
+        fw = self.fwd
+        L.moe_route_bwd(dout, fw.y_rows, fw.act_fmt, fw.row_map, fw.topk_idx, fw.logits, x,
+                        w_router, fw.T, fw.k, fw.E, fw.H, fw.routed_scale, self.seq_len,
+                        self.aux_alpha, self.dlogits, self.aux_loss if self.aux_alpha else None,
+                        self.dx, self.dw, self.ws, stream)
+        return self.dx, self.dw
+
+
+def bias_update(fwd: MoEForward, bias: torch.Tensor, gamma: float, out=None, stream=None):
+    """The aux-loss-free bias update from the pass's expert loads
+    (moe_bias_update); in place unless `out` is given."""
+    out = bias if out is None else out
+    L.moe_bias_update(fwd.counts, fwd.E, gamma, bias, out, stream)
+    return out

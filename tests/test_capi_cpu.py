@@ -277,3 +277,27 @@ def test_grouped_mlp_bwd_validation(lib):
     assert call(wsb=need - 1) == WS
     assert call(ws=None) == WS
     assert b"moe_grouped_mlp_bwd_workspace" in lib.moe_last_error()
+
+
+def test_route_bwd_validation(lib):
+    T, k, E, H = 300, 8, 32, 512
+    need = lib.moe_route_bwd_workspace(T, H, E, 100)
+    assert need > 0 and lib.moe_route_bwd_workspace(T, H, E, 7) == 0    # 7 does not divide 300
+
+    def call(**kw):
+        a = dict(dout=A, y=A, af=1, rm=A, idx=A, lg=A, x=A, wr=A, T=T, k=k, E=E, H=H, sc=2.5, L=100,
+                 al=0.01, dl=None, loss=A, dx=A, dw=A, ws=A, wsb=need)
+        a.update(kw)
+        return lib.moe_route_bwd(a["dout"], a["y"], a["af"], a["rm"], a["idx"], a["lg"], a["x"],
+                                 a["wr"], a["T"], a["k"], a["E"], a["H"], a["sc"], a["L"], a["al"],
+                                 a["dl"], a["loss"], a["dx"], a["dw"], a["ws"], a["wsb"], None)
+    assert call(af=0) == UNSUPPORTED
+    assert call(E=36) == INVALID                 # E % 8
+    assert call(k=17) == INVALID
+    assert call(L=7) == INVALID
+    assert call(loss=None) == INVALID            # the balance loss needs its output
+    assert call(x=A + 4) == ALIGN
+    assert call(wsb=need - 1) == WS
+    assert call(T=0, dout=None, y=None) == OK    # empty batch: nothing to do
+    assert lib.moe_bias_update(A, 0, 1e-3, A, A, None) == INVALID
+    assert lib.moe_bias_update(None, 8, 1e-3, A, A, None) == INVALID
