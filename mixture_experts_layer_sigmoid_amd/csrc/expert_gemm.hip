@@ -90,6 +90,8 @@ struct XArgs {
   int64_t a_row_bytes;
   const uint8_t* a_sc;       // their MX scales [rows, K/32]
   int64_t a_sc_row_bytes;
+  uint32_t a_bytes;          // bytes of the activation matrix (< 4 GiB) and of its scales
+  uint32_t a_sc_bytes;
   const int32_t* gather;     // optional row -> token row (-1: padding row)
   const uint8_t* b;          // packed weights of expert 0
   int64_t b_exp_bytes;
@@ -336,16 +338,18 @@ void expert_gemm_kernel(XArgs p) {
     }
     if (p.gather && EPI == XEPI_SWIGLU)
       for (int r = tid; r < kRows; r += 256) s_src[r] = r < nrows && !dn ? p.gather[row0 + r] : 0;
-    const uint8_t* asc_src[kAScPerWave > 0 ? kAScPerWave : 1];
+    uint32_t asc_off[kAScPerWave > 0 ? kAScPerWave : 1];
     if constexpr (kSB > 0) {
 #pragma unroll
       for (int q = 0; q < kAScPerWave; ++q) {
         const int j = min(wave + 4 * q, kAScIns - 1);  // covers rows [j * kScRows, +kScRows)
         const int r = min(j * kScRows + lane / kDpr, nrows - 1);
         const int src = a_row(row0 + r);
-        asc_src[q] = p.a_sc + static_cast<int64_t>(src) * p.a_sc_row_bytes + (lane % kDpr) * 4;
+        asc_off[q] = static_cast<uint32_t>(src) * static_cast<uint32_t>(p.a_sc_row_bytes) + (lane % kDpr) * 4;
       }
     }
+    const __amdgpu_buffer_rsrc_t a_rs = buf_rsrc(p.a, p.a_bytes);
+    const __amdgpu_buffer_rsrc_t asc_rs = buf_rsrc(kSB > 0 ? p.a_sc : p.a, kSB > 0 ? p.a_sc_bytes : 0u);
     const int cbw = active ? cb0 : 0;
     const uint8_t* b_exp = dn ? p.d_b : p.b + static_cast<int64_t>(e) * p.b_exp_bytes;
     const uint8_t* b_src = b_exp + static_cast<int64_t>(cbw) * p.k_stages * kChunk + lane * 16;
@@ -388,11 +392,12 @@ void expert_gemm_kernel(XArgs p) {
       } else if constexpr (OPN < kB + NV) {
         constexpr int i = OPN - kB;
         uint8_t* st = smem + SL * S::kStage;
-        lds_load16(p.a + a_off[i] + static_cast<int64_t>(kt) * kStageBytes, st + (wave + 4 * i) * 1024);
+        lds_load16_buf(a_rs, a_off[i], static_cast<uint32_t>(kt) * kStageBytes, st + (wave + 4 * i) * 1024);
       } else {
         constexpr int q = OPN - kB - NV;
         uint8_t* st = smem + SL * S::kStage;
-        lds_load4(asc_src[q] + static_cast<int64_t>(kt) * kSB, st + S::kA + min(wave + 4 * q, kAScIns - 1) * 256);
+        lds_load4_buf(asc_rs, asc_off[q], static_cast<uint32_t>(kt) * kSB,
+                      st + S::kA + min(wave + 4 * q, kAScIns - 1) * 256);
       }
     };
     // a whole stage, activation operations first (the order the steps use)
@@ -414,9 +419,9 @@ void expert_gemm_kernel(XArgs p) {
 
     // MFMAs of one stage for the first NV row blocks. The (k-step, row
     // block) sequence is walked with the activation operands (and their MX
-    // scale words) read from LDS three steps ahead into a small register
-    // ring, so LDS latency hides behind the matrix instructions of the
-    // previous steps.
+    // scale words) read from LDS one or two steps ahead into a small
+    // register ring, so LDS latency hides behind the matrix instructions of
+    // the previous steps.
     // The weight loads of the stage P-1 ahead (kt_next, into register slot
     // NSL) are spread over the steps, so the memory pipeline works while the
     // matrix cores do. (The direct-to-LDS activation loads of that stage are
@@ -427,7 +432,10 @@ void expert_gemm_kernel(XArgs p) {
       constexpr int NV = decltype(nv_c)::value;
       constexpr int NSTEP = kSub * NV;
       constexpr int kB = 8 + (kSB > 0 ? 2 : 0);  // weight loads per stage
-      constexpr int D = 3;  // operand ring depth
+      // operand ring depth: reads D - 1 steps ahead (an E4M3 step's two
+      // 64-cycle MFMAs cover one LDS read; bf16 and E2M1 steps take 32 cycles
+      // per MFMA and read two steps ahead)
+      constexpr int D = OP == XOP_FP8 ? 2 : 3;
       const uint8_t* sa = smem + SL * S::kStage;
       const uint32_t* sasc = reinterpret_cast<const uint32_t*>(sa + S::kA);
       using AFrag = std::conditional_t<OP == XOP_BF16, bf16x8_t, i32x8_t>;
@@ -510,6 +518,9 @@ void expert_gemm_kernel(XArgs p) {
       constexpr int NV = decltype(nv_c)::value;
       constexpr int kPer = NV + kAScPerWave + 8 + (kSB > 0 ? 2 : 0);  // loads per stage
       static_assert((P - 2) * kPer <= 62, "vmcnt range");
+      // loads still allowed in flight at a step's wait: the weight loads of
+      // the stages after the next (none with a two-stage ring)
+      constexpr int kWait = P > 2 ? (P - 2) * kPer - NV - kAScPerWave : 0;
       static_for<P - 1>([&](auto s_c) {
         issue(min(static_cast<int>(decltype(s_c)::value), KT - 1), s_c, nv_c);
       });
@@ -518,7 +529,7 @@ void expert_gemm_kernel(XArgs p) {
         constexpr int kB = 8 + (kSB > 0 ? 2 : 0);
         using NSL = std::integral_constant<int, (J + P - 1) % P>;
         const int kt_next = min(kt + P - 1, KT - 1);
-        wait_vmcnt<(P - 2) * kPer - NV - kAScPerWave>();
+        wait_vmcnt<kWait>();
         lds_barrier();
         static_for<NV + kAScPerWave>([&](auto o_c) {
           issue_op(kt_next, NSL{}, nv_c, std::integral_constant<int, kB + decltype(o_c)::value>{});
@@ -694,11 +705,15 @@ void expert_gemm_kernel(XArgs p) {
           constexpr bool fp4 = OUTF == MOE_MXFP4_E2M1;
           constexpr int kBlkBytes = fp4 ? 16 : 32;
           const int nblk = width / 32;
-          for (int i = tid; i < prows * nblk; i += 256) {
-            const int row = i / nblk, blk = i % nblk;
+          // one item per (row, 32-column block, half): the gate half's or
+          // the up half's 32 gradients are formed, encoded and stored on
+          // their own (both at once hold 64 values in registers)
+          for (int i = tid; i < prows * nblk * 2; i += 256) {
+            const int half = i & 1, item = i >> 1;
+            const int row = item / nblk, blk = item % nblk;
             const int col = c_first + blk * 32;
             const int64_t grow = row0 + prow0 + row;
-            float dg[32], du[32];
+            float v[32];
 #pragma unroll
             for (int w8 = 0; w8 < 4; ++w8) {
               float gv[8], uv[8];
@@ -708,27 +723,20 @@ void expert_gemm_kernel(XArgs p) {
               for (int q = 0; q < 8; ++q) {
                 const float dh = cs[row * kCs + blk * 32 + w8 * 8 + q];
                 const float sg = sigmoidf_(gv[q]);
-                dg[w8 * 8 + q] = dh * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
-                du[w8 * 8 + q] = dh * (gv[q] * sg);
+                v[w8 * 8 + q] = half ? dh * (gv[q] * sg) : dh * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
               }
             }
             uint32_t words[8];
-            uint8_t* orow = p.out + grow * p.out_row_bytes;
-            uint8_t* srow = p.out_sc + grow * p.out_sc_row_bytes;
+            const int c = half ? F + col : col;
+            const uint32_t sb = mx_encode_block<fp4>(v, words);
+            u32x4_t* o = reinterpret_cast<u32x4_t*>(p.out + grow * p.out_row_bytes + (c / 32) * kBlkBytes);
+            o[0] = u32x4_t{words[0], words[1], words[2], words[3]};
+            if (!fp4) o[1] = u32x4_t{words[4], words[5], words[6], words[7]};
+            p.out_sc[grow * p.out_sc_row_bytes + c / 32] = static_cast<uint8_t>(sb);
+            if (p.da_f32) {
+              float* ob = p.da_f32 + grow * a2 + c;
 #pragma unroll
-            for (int part2 = 0; part2 < 2; ++part2) {
-              const float* v = part2 ? du : dg;
-              const int c = part2 ? F + col : col;
-              const uint32_t sb = mx_encode_block<fp4>(v, words);
-              u32x4_t* o = reinterpret_cast<u32x4_t*>(orow + (c / 32) * kBlkBytes);
-              o[0] = u32x4_t{words[0], words[1], words[2], words[3]};
-              if (!fp4) o[1] = u32x4_t{words[4], words[5], words[6], words[7]};
-              srow[c / 32] = static_cast<uint8_t>(sb);
-              if (p.da_f32) {
-                float* ob = p.da_f32 + grow * a2 + c;
-#pragma unroll
-                for (int w8 = 0; w8 < 4; ++w8) store8_f32(ob + w8 * 8, v + w8 * 8);
-              }
+              for (int w8 = 0; w8 < 4; ++w8) store8_f32(ob + w8 * 8, v + w8 * 8);
             }
           }
         }
@@ -817,6 +825,8 @@ int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const
   x.a_row_bytes = static_cast<int64_t>(K) * bits / 8;
   x.a_sc = a_scales;
   x.a_sc_row_bytes = K / 32;
+  x.a_bytes = static_cast<uint32_t>(a_rows * x.a_row_bytes);
+  x.a_sc_bytes = static_cast<uint32_t>(a_rows * (K / 32));
   x.gather = gather;
   x.b = static_cast<const uint8_t*>(wp);
   x.b_exp_bytes = static_cast<int64_t>(N) * K * bits / 8;
@@ -845,10 +855,11 @@ int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const
   const bool mx_out = kind != 1 && fmt != MOE_BF16;
   x.out_row_bytes = mx_out ? static_cast<int64_t>(outw) * bits / 8 : static_cast<int64_t>(outw) * 2;
   x.out_sc_row_bytes = outw / 32;
-  constexpr int OC = 1;
-  const dim3 grid(kNumCu * OC), block(256);
-  auto launch = [&](auto mn_c, auto pp_c) {
+  const dim3 block(256);
+  auto launch = [&](auto mn_c, auto pp_c, auto oc_c) {
     constexpr int MN = decltype(mn_c)::value, PP = decltype(pp_c)::value;
+    constexpr int OC = decltype(oc_c)::value;
+    const dim3 grid(kNumCu * OC);
     auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, x); };
     switch (kind * 3 + xop_of(fmt)) {
       case 0: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_SWIGLU, MOE_BF16>); break;
@@ -864,10 +875,11 @@ int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const
   };
   // decode batches (a few rows per expert on average): 64-row tiles and a
   // 6-deep ring keep more weight bytes in flight per wave
+  using I = std::integral_constant<int, 1>;
   if (kind != 2 && rows <= 8ll * E)
-    launch(std::integral_constant<int, 2>{}, std::integral_constant<int, 6>{});
+    launch(std::integral_constant<int, 2>{}, std::integral_constant<int, 6>{}, I{});
   else
-    launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 3>{});
+    launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 3>{}, I{});
   return check_launch("grouped expert GEMM");
 }
 

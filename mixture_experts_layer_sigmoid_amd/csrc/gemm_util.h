@@ -1,5 +1,5 @@
 // Device helpers shared by the grouped GEMM kernels: direct global->LDS
-// loads, vmcnt waits, the LDS-only workgroup barrier, the swizzled LDS row
+// loads (global and buffer forms), vmcnt waits, the LDS-only workgroup barrier, the swizzled LDS row
 // layout and the SwiGLU activation.
 #pragma once
 
@@ -14,6 +14,28 @@ __device__ __forceinline__ void lds_load16(const void* g, void* lds) {
 __device__ __forceinline__ void lds_load4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
                                    (void __attribute__((address_space(3)))*)lds, 4, 0, 0);
+}
+
+// Direct-to-LDS loads through a buffer resource (MUBUF form): lane l's 16
+// (or 4) bytes from base + voffset + soffset land at lds + 16 l (4 l). The
+// buffer form matters for the LDS operand reads that follow: while a
+// global (FLAT) direct-to-LDS load is outstanding the compiler cannot count
+// LDS reads in order and waits for all of them (lgkmcnt(0)) before every
+// use; with the buffer form its waits stay exact. Offsets past `bytes`
+// read as zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ void lds_load16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                               uint32_t soffset, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds, 16,
+                                           voffset, soffset, 0, 0);
+}
+__device__ __forceinline__ void lds_load4_buf(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                              uint32_t soffset, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds, 4,
+                                           voffset, soffset, 0, 0);
 }
 
 // Wait until at most n vector-memory operations of this wave are in flight.
