@@ -84,6 +84,7 @@ struct WArgs {
   const int32_t* kofs;     // [E + 1] segment starts (multiples of 128)
   int E, M, N;
   uint8_t* dw;             // [E, M, N] bf16
+  uint32_t at_bytes, at_sc_bytes, bt_bytes, bt_sc_bytes;  // operand sizes (< 4 GiB)
 };
 
 struct Tile {
@@ -240,19 +241,24 @@ void wgrad_kernel(WArgs p) {
 
   // one operand block (128 channel rows of stage g) into a slot: 16 KB
   // contiguous in the stage-major layout; 4 loads per wave (+1 scale load)
-  auto issue_block = [&](const uint8_t* codes, const uint8_t* scl, int64_t row0, bool scl_wave,
-                         uint8_t* slot) {
-    const uint8_t* c = codes + row0 * kRB;
+  // (buffer-form direct-to-LDS loads: the LDS operand reads after them keep
+  // exact waits, see gemm_util.h)
+  const __amdgpu_buffer_rsrc_t at_rs = buf_rsrc(p.at, p.at_bytes), at_sc_rs = buf_rsrc(p.at_sc, p.at_sc_bytes);
+  const __amdgpu_buffer_rsrc_t bt_rs = buf_rsrc(p.bt, p.bt_bytes), bt_sc_rs = buf_rsrc(p.bt_sc, p.bt_sc_bytes);
+  auto issue_block = [&](__amdgpu_buffer_rsrc_t codes, __amdgpu_buffer_rsrc_t scl, uint32_t row0,
+                         bool scl_wave, uint8_t* slot) {
+    const uint32_t c = row0 * kRB;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      lds_load16(c + ld_row[i] * kRB + ld_chunk[i], slot + (wave + 4 * i) * 1024);
-    if (scl_wave) lds_load4(scl + (row0 + sc_row) * 4, slot + kCodes + (wave & 1) * 256);
+      lds_load16_buf(codes, static_cast<uint32_t>(ld_row[i] * kRB + ld_chunk[i]), c,
+                     slot + (wave + 4 * i) * 1024);
+    if (scl_wave) lds_load4_buf(scl, static_cast<uint32_t>(sc_row * 4), row0 * 4, slot + kCodes + (wave & 1) * 256);
   };
   auto issue_a = [&](const Tile& t, int ks, uint8_t* slot) {
-    issue_block(p.at, p.at_sc, static_cast<int64_t>(t.g + ks) * p.M + t.m0, wave < 2, slot);
+    issue_block(at_rs, at_sc_rs, static_cast<uint32_t>(t.g + ks) * p.M + t.m0, wave < 2, slot);
   };
   auto issue_b = [&](const Tile& t, int ks, uint8_t* slot) {
-    issue_block(p.bt, p.bt_sc, static_cast<int64_t>(t.g + ks) * p.N + t.n0, wave >= 2, slot);
+    issue_block(bt_rs, bt_sc_rs, static_cast<uint32_t>(t.g + ks) * p.N + t.n0, wave >= 2, slot);
   };
 
   f32x16_t acc[2][2];  // [dW row block mi][dW column block ni]
@@ -414,6 +420,8 @@ extern "C" int moe_grouped_wgrad(const void* at, const uint8_t* at_scales, const
               "moe_grouped_wgrad: need M % 128 == 0 and N % 128 == 0");
   MOE_REQUIRE(at && bt && at_scales && bt_scales && kofs && dw, MOE_ERR_INVALID_ARG,
               "moe_grouped_wgrad: null pointer");
+  MOE_REQUIRE(kstride * std::max(M, N) < (int64_t{1} << 32), MOE_ERR_UNSUPPORTED,
+              "moe_grouped_wgrad: operand of 4 GiB or more");
   MOE_REQUIRE(aligned16(at) && aligned16(bt) && aligned16(dw) &&
                   (reinterpret_cast<uintptr_t>(at_scales) & 3u) == 0 &&
                   (reinterpret_cast<uintptr_t>(bt_scales) & 3u) == 0,
@@ -428,6 +436,10 @@ extern "C" int moe_grouped_wgrad(const void* at, const uint8_t* at_scales, const
   a.M = M;
   a.N = N;
   a.dw = static_cast<uint8_t*>(dw);
+  a.at_bytes = static_cast<uint32_t>(kstride * M);
+  a.at_sc_bytes = static_cast<uint32_t>(kstride / 32 * M);
+  a.bt_bytes = static_cast<uint32_t>(kstride * N);
+  a.bt_sc_bytes = static_cast<uint32_t>(kstride / 32 * N);
   hipLaunchKernelGGL(wgrad_kernel, dim3(kNumCu * kOcc), dim3(kNT), 0, stream, a);
   return check_launch("grouped wgrad");
 }
