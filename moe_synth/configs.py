@@ -31,7 +31,7 @@ class MoEConfig:
     routed_scale: float
     n_shared: int        # 0 or 1 shared expert
     F_shared: int
-    fmt: str             # 'fp32' | 'bf16' | 'mxfp8' | 'mxfp4'
+    fmt: str             # 'fp32' | 'bf16' | 'mxfp8' | 'mxfp4' | 'nvfp4'
     x_std: float
     router_std: float
     bias_kind: str       # 'uniform' | 'zipf'
@@ -41,6 +41,9 @@ class MoEConfig:
     zipf_s: float = 1.1
     n_zero_experts: int = 0
     x_rows_from: str = ""  # reuse the first T rows of another config's x
+    # NVFP4 layer: fixed tensor scales of the hidden states and of h
+    x_global: float = 0.0
+    h_global: float = 0.0
 
     @property
     def rows(self) -> int:
@@ -128,6 +131,14 @@ DSV3_EP_SHARE = MoEConfig(
     F_shared=0, fmt="mxfp8", x_std=1.0, router_std=1.0 / math.sqrt(7168),
     bias_kind="uniform", bias_range=0.05, backward=True, align=32)
 
+# The same layer with NVFP4 W4A4 ([SGL-NVFP4] title and Modifications: the
+# 4-bit format the pages run): E2M1 values, E4M3 scales per 16, one fp32
+# scale per tensor; the activation scales are fixed for the workload (2^-8
+# for N(0,1) hidden states: nothing saturates below 6 * 448 * 2^-8 = 10.5;
+# 2^-6 for h).
+DSV4_NVFP4 = replace(DSV4_MXFP4, name="dsv4_nvfp4_t16384", fmt="nvfp4",
+                     x_global=2.0 ** -8, h_global=2.0 ** -6)
+
 # -- reduced shapes of the same structure, small enough for full parity ----
 # (several GEMM tiles along every axis, ragged token counts)
 MINI_BF16 = replace(
@@ -145,6 +156,9 @@ MINI_SKEW = replace(
 MINI_EP_SHARE = replace(
     DSV3_EP_SHARE, name="mini_ep8_mxfp8", family="mini_ep8", T=300, H=512, F=256,
     router_std=1.0 / math.sqrt(512))
+MINI_NVFP4 = replace(
+    DSV4_NVFP4, name="mini_nvfp4", family="mini_mxfp4", T=500, H=512, F=256,
+    E=32, router_std=1.0 / math.sqrt(512))
 MINI_FP32 = replace(
     TINY_FP32, name="mini_fp32", family="mini_fp32", T=333, H=320, F=192,
     E=24, n_group=6, topk_group=3, k=5, x_std=1.0,
@@ -152,8 +166,8 @@ MINI_FP32 = replace(
 
 ALL = {c.name: c for c in (
     TINY_FP32, TINY_FP32_UNITX, DSV3_BF16, DSV3_MXFP8_DECODE, DSV4_MXFP4,
-    DSV4_SKEW_MXFP8, DSV3_EP_SHARE, MINI_BF16, MINI_MXFP8_DECODE, MINI_MXFP4,
-    MINI_SKEW, MINI_EP_SHARE, MINI_FP32)}
+    DSV4_SKEW_MXFP8, DSV3_EP_SHARE, DSV4_NVFP4, MINI_BF16, MINI_MXFP8_DECODE,
+    MINI_MXFP4, MINI_SKEW, MINI_EP_SHARE, MINI_NVFP4, MINI_FP32)}
 
 # The workload the headline throughput is quoted on.
 HEADLINE = DSV3_BF16

@@ -19,7 +19,9 @@ Readings taken where the pages are silent:
     fp32, plus the shared expert's output with unit weight;
   * MX layers: x is MX-quantized per token along H before fc1, h per row
     along F before fc2; the GEMMs see the dequantized values; expert and
-    shared weights are MX-quantized along their contraction axis;
+    shared weights are MX-quantized along their contraction axis; the NVFP4
+    layer likewise with NVFP4 blocks of 16 (oracle.nvfp4), each expert
+    weight matrix with its own tensor scale, x and h with fixed ones;
   * the GEMMs accumulate in fp32; bf16 storage rounding of intermediates is
     not emulated.
 """
@@ -28,6 +30,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import mx as _mx
+from . import nvfp4 as _nv
 from . import permute as _perm
 from . import routing as _rt
 
@@ -47,21 +50,26 @@ def swiglu(a: np.ndarray, F: int) -> np.ndarray:
     return (silu(a[:, :F]) * a[:, F:]).astype(F32)
 
 
-def operand(v: np.ndarray, fmt: str, axis: int = -1) -> np.ndarray:
+def operand(v: np.ndarray, fmt: str, axis: int = -1, g=None) -> np.ndarray:
     """Values a GEMM sees for a stored operand: MX-dequantized for MX
-    layers (blocks along the contraction axis), unchanged otherwise."""
+    layers (blocks along the contraction axis), NVFP4-dequantized for the
+    NVFP4 layer (tensor scale g; by default the tensor's own, as for a
+    weight matrix), unchanged otherwise."""
     if fmt in ("mxfp8", "mxfp4"):
         return _mx.fake_quant(v, _mx.fmt_of(fmt), axis)
+    if fmt == "nvfp4":
+        return _nv.fake_quant(v, g, axis)
     return np.asarray(v, F32)
 
 
-def expert_mlp(xq: np.ndarray, w1q: np.ndarray, w2q: np.ndarray, fmt: str):
+def expert_mlp(xq: np.ndarray, w1q: np.ndarray, w2q: np.ndarray, fmt: str, h_global=None):
     """One expert on its rows. xq [n, H], w1q [2F, H], w2q [H, F] are the
-    operand values. Returns (a [n, 2F], h [n, F], y [n, H]) in fp32."""
+    operand values. Returns (a [n, 2F], h [n, F], y [n, H]) in fp32.
+    h_global: the tensor scale of h (NVFP4 layer)."""
     F = w1q.shape[0] // 2
     a = (np.asarray(xq, F32) @ np.asarray(w1q, F32).T).astype(F32)
     h = swiglu(a, F)
-    hq = operand(h, fmt, axis=-1)
+    hq = operand(h, fmt, axis=-1, g=h_global)
     y = (hq @ np.asarray(w2q, F32).T).astype(F32)
     return a, h, y
 
@@ -80,7 +88,7 @@ def combine(y_rows: np.ndarray, row_map: np.ndarray, w: np.ndarray,
 
 def moe_forward(x, w_router, bias, w1_of, w2_of, *, E, n_group, topk_group, k,
                 routed_scale, fmt, align=1, shared_w=None, logits=None,
-                tokens=None, idx=None, workers=1):
+                tokens=None, idx=None, workers=1, act_globals=None):
     """The layer forward.
 
     x: [T, H] fp32 values of the stored hidden states. w1_of(e) / w2_of(e)
@@ -93,8 +101,10 @@ def moe_forward(x, w_router, bias, w1_of, w2_of, *, E, n_group, topk_group, k,
     other several selections are correct; the combine weights are then the
     oracle's normalized scores of those experts). workers: experts evaluated
     concurrently by that many threads (each expert's arithmetic is
-    unchanged; only independent experts overlap).
+    unchanged; only independent experts overlap). act_globals: (g_x, g_h),
+    the tensor scales of the hidden states and of h in the NVFP4 layer.
     """
+    gx, gh = act_globals if act_globals is not None else (None, None)
     x = np.asarray(x, F32)
     T = x.shape[0]
     if logits is None:
@@ -108,7 +118,7 @@ def moe_forward(x, w_router, bias, w1_of, w2_of, *, E, n_group, topk_group, k,
         w = _rt.combine_weights(s, idx, routed_scale)
     counts, offsets, row_map, src_row = _perm.permute_maps(idx, E, align)
     toks = np.arange(T) if tokens is None else np.asarray(tokens)
-    xq = operand(x[toks], fmt, axis=-1)            # per-token quantization
+    xq = operand(x[toks], fmt, axis=-1, g=gx)      # per-token quantization
     pos = {int(t): i for i, t in enumerate(toks)}
     sub_idx = idx[toks]
 
@@ -116,7 +126,7 @@ def moe_forward(x, w_router, bias, w1_of, w2_of, *, E, n_group, topk_group, k,
         tj = np.argwhere(sub_idx == e)             # (token position, slot) in order
         w1q = operand(w1_of(int(e)), fmt, axis=-1)
         w2q = operand(w2_of(int(e)), fmt, axis=-1)
-        _, _, ye = expert_mlp(xq[tj[:, 0]], w1q, w2q, fmt)
+        _, _, ye = expert_mlp(xq[tj[:, 0]], w1q, w2q, fmt, gh)
         return tj, ye
 
     experts = [int(e) for e in np.unique(sub_idx)]
@@ -139,7 +149,7 @@ def moe_forward(x, w_router, bias, w1_of, w2_of, *, E, n_group, topk_group, k,
     ys = None
     if shared_w is not None:
         w1s, w2s = shared_w
-        _, _, ys = expert_mlp(xq, operand(w1s, fmt), operand(w2s, fmt), fmt)
+        _, _, ys = expert_mlp(xq, operand(w1s, fmt), operand(w2s, fmt), fmt, gh)
     out = combine(y_sub, rm_sub, w[toks], ys)
     return dict(logits=logits, s=s, sel=sel, idx=idx, w=w, counts=counts,
                 offsets=offsets, row_map=row_map, src_row=src_row, out=out,

@@ -193,3 +193,46 @@ def test_expert_threads_do_not_change_bits():
     many = mlp.moe_forward(d["x"], d["w_router"], d["bias"], lambda e: d["w1"][e],
                            lambda e: d["w2"][e], workers=4, **kw)
     assert np.array_equal(one["out"], many["out"])
+
+
+def test_nvfp4_forward_against_brute_quantized_dense():
+    """NVFP4 layer: operands re-quantized by the linear-search NVFP4
+    quantizer of tests/test_oracle_nvfp4.py (each weight matrix with its own
+    tensor scale, x and h with the layer's fixed ones) and the layer
+    evaluated densely in fp64."""
+    from tests.test_oracle_nvfp4 import _brute_block
+    from oracle import nvfp4
+    cfg = configs.get("mini_nvfp4")
+    T = 6
+    d = gen.host_inputs(cfg)
+    d["x"] = d["x"][:T]
+    F32 = np.float32
+
+    def bq(v, g):
+        v = np.asarray(v, F32)
+        out = np.empty(v.shape, np.float64)
+        for r in range(v.shape[0]):
+            for b in range(v.shape[1] // 16):
+                c, s = _brute_block(v[r, 16 * b:16 * b + 16], F32(g))
+                vals = brute.e2m1_table()[c] * brute.e4m3_table()[s]
+                out[r, 16 * b:16 * b + 16] = (vals.astype(F32) * F32(g)).astype(F32)
+        return out
+
+    experts = [0, 5]
+    w1 = d["w1"][experts]
+    w2 = d["w2"][experts]
+    wr = d["w_router"][experts]
+    res = mlp.moe_forward(d["x"], wr, d["bias"][experts], lambda e: w1[e], lambda e: w2[e],
+                          E=2, n_group=1, topk_group=1, k=1, routed_scale=1.0, fmt=cfg.fmt,
+                          act_globals=(cfg.x_global, cfg.h_global))
+    xq = bq(d["x"], cfg.x_global)
+    w1q = [bq(w, nvfp4.global_scale(w)) for w in w1]
+    w2q = [bq(w, nvfp4.global_scale(w)) for w in w2]
+    out = np.zeros((T, cfg.H))
+    for t in range(T):
+        e = res["idx"][t, 0]
+        a = xq[t] @ w1q[e].T
+        h = a[:cfg.F] / (1 + np.exp(-a[:cfg.F])) * a[cfg.F:]
+        hq = bq(h.astype(F32)[None], cfg.h_global)[0]
+        out[t] = res["w"][t, 0] * (hq @ w2q[e].T)
+    assert brute.rel_l2(res["out"], out) < 2e-3
