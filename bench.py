@@ -51,10 +51,12 @@ import time
 import numpy as np
 
 METRIC = "MoE layer tokens/s + TFLOP/s (% MFMA peak) at DSV3 dims, 4096 tok, 1 GPU"
-PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "fp32": 157.3}
+# the NVFP4 GEMMs run bf16 matrix instructions on exact bf16 operand values
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "fp32": 157.3, "nvfp4": 2500.0}
 PEAK_HBM_GBS = 8000.0
 # bytes per stored element (MX: code + one scale byte per 32 elements)
-ELEM_BYTES = {"bf16": 2.0, "fp32": 4.0, "mxfp8": 1 + 1 / 32, "mxfp4": 0.5 + 1 / 32}
+ELEM_BYTES = {"bf16": 2.0, "fp32": 4.0, "mxfp8": 1 + 1 / 32, "mxfp4": 0.5 + 1 / 32,
+              "nvfp4": 0.5 + 1 / 16}
 
 
 def log(msg):
@@ -74,7 +76,7 @@ def stage_work(cfg, counts: np.ndarray, backward: bool, kpad: int = 0, fused_sha
     qb = wb                                     # layer-format activation rows
     work = {}
     work["route"] = (T * H * ab + E * H * ab + T * k * 8, 2.0 * T * H * E)
-    if cfg.fmt in ("mxfp8", "mxfp4"):
+    if cfg.fmt in ("mxfp8", "mxfp4", "nvfp4"):
         work["quantize_x"] = (T * H * ab + T * H * qb, 0.0)
     work["permute"] = (T * k * 4 * 3 + E * 8, 0.0)
     save = R * 2 * F * 4 if backward else 0
@@ -212,6 +214,7 @@ def cpu_baseline(cfg, x, wr, b, wts, sh, dout, backward: bool, budget_experts: i
     w1_of = lambda e: widen(wts["w1"][e].view(torch.int16).cpu().numpy().view(np.uint16))
     w2_of = lambda e: widen(wts["w2"][e].view(torch.int16).cpu().numpy().view(np.uint16))
     T, k, fmt = cfg.T, cfg.k, cfg.fmt
+    gx, gh = (cfg.x_global, cfg.h_global) if fmt == "nvfp4" else (None, None)
     with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         logits = rt.router_logits(x, wr)
@@ -220,9 +223,9 @@ def cpu_baseline(cfg, x, wr, b, wts, sh, dout, backward: bool, budget_experts: i
         counts = np.bincount(idx.ravel(), minlength=cfg.E)
         touched = np.nonzero(counts)[0]
         if budget_experts is None:
-            budget_experts = {"bf16": 32, "mxfp8": 3, "mxfp4": 4}.get(fmt, 8)
+            budget_experts = {"bf16": 32, "mxfp8": 3, "mxfp4": 4, "nvfp4": 4}.get(fmt, 8)
             if backward:
-                budget_experts = 1
+                budget_experts = 2
         m = max(1, min(budget_experts, len(touched)))
         order = touched[np.argsort(counts[touched], kind="stable")]
         picks = order[np.linspace(0, len(order) - 1, m + 2)[1:-1].round().astype(int)] if m < len(order) \
@@ -235,8 +238,9 @@ def cpu_baseline(cfg, x, wr, b, wts, sh, dout, backward: bool, budget_experts: i
             t_, j_ = tj[:, 0], tj[:, 1]
             w1, w2 = w1_of(int(e)), w2_of(int(e))
             t0 = time.perf_counter()
-            xq = omlp.operand(x[t_], fmt, axis=-1)
-            omlp.expert_mlp(xq, omlp.operand(w1, fmt, axis=-1), omlp.operand(w2, fmt, axis=-1), fmt)
+            xq = omlp.operand(x[t_], fmt, axis=-1, g=gx)
+            omlp.expert_mlp(xq, omlp.operand(w1, fmt, axis=-1), omlp.operand(w2, fmt, axis=-1), fmt,
+                            gh)
             if backward:
                 dy = (w[t_, j_][:, None].astype(np.float32) * dout[t_]).astype(np.float32)
                 obw.expert_backward(x[t_], dy, w1, w2, fmt)
@@ -335,7 +339,7 @@ def main():
     ew = moe.ExpertWeights.from_dense(wts["w1"], wts["w2"], cfg.fmt, transposed=backward)
     sw = moe.ExpertWeights.from_dense(sh["w1s"], sh["w2s"], cfg.fmt) if sh else None
     want_cpu = not args.no_cpu_baseline
-    if moe.layer.is_mx(cfg.fmt) and not want_cpu:
+    if cfg.fmt != "bf16" and not want_cpu:
         del wts["w1"], wts["w2"]
     fw = moe.MoEForward.for_config(cfg, device=dev, save_act=backward)
     bw = moe.MoEBackward(fw) if backward else None
@@ -348,7 +352,7 @@ def main():
     if backward:
         names += ["combine_bwd", "fc2_dgrad_dswiglu", "fc1_dgrad", "unpermute", "operands_dw2",
                   "wgrad_dw2", "operands_dw1", "wgrad_dw1"]
-    if not moe.layer.is_mx(cfg.fmt):
+    if not (moe.layer.is_mx(cfg.fmt) or cfg.fmt == "nvfp4"):
         names.remove("quantize_x")
     if not cfg.n_shared or fw.fuse_shared:
         names.remove("shared")      # none, or inside fc1_swiglu / fc2

@@ -70,7 +70,9 @@ typedef enum moe_format {
   MOE_F32 = 0,               /* IEEE binary32                              */
   MOE_BF16 = 1,              /* bfloat16                                   */
   MOE_MXFP8_E4M3 = 2,        /* E4M3 codes + E8M0 scales per 32 along K    */
-  MOE_MXFP4_E2M1 = 3         /* E2M1 codes (packed) + E8M0 scales per 32   */
+  MOE_MXFP4_E2M1 = 3,        /* E2M1 codes (packed) + E8M0 scales per 32   */
+  MOE_NVFP4_E2M1 = 4         /* E2M1 codes (packed) + E4M3 scales per 16
+                                + one fp32 scale per tensor               */
 } moe_format;
 
 /* Version of this ABI (MOE_ABI_VERSION of the built library). */
@@ -241,8 +243,14 @@ size_t moe_grouped_mlp_workspace(int E, int H, int F, int64_t rows, int a_fmt,
  * 2 j + l / 32 of row R(cb, l).
  * w        [E, N, K] in fmt (BF16 values, or MX codes with w_scales
  *          [E, N, K/32]); out (and out_scales) the same number of bytes.
- * Limits: N % 64 == 0; K a multiple of 64 (BF16), 128 (E4M3), 256 (E2M1);
- * half == 0 or N == 2 * half with half % 32 == 0.
+ * NVFP4 (fmt MOE_NVFP4_E2M1; codes [E, N, K/2], w_scales [E, N, K/16] as
+ * moe_quantize_nvfp4 writes them): 64-value stages s; for (e, cb, s, l)
+ * 16 bytes = for k-step j < 4 the 4 code bytes at byte 32 s + 8 j +
+ * 4 (l / 32) of row R(cb, l); scales for (e, cb, s, r < 32) 4 bytes = the
+ * E4M3 scales of row R(cb, r)'s 16-blocks 4 s + j (both lane halves read
+ * the same word).
+ * Limits: N % 64 == 0; K a multiple of 64 (BF16, NVFP4), 128 (E4M3), 256
+ * (E2M1); half == 0 or N == 2 * half with half % 32 == 0.
  */
 int moe_pack_weights(const void* w, const uint8_t* w_scales, int fmt, int E,
                      int N, int K, int half, void* out, uint8_t* out_scales,
@@ -346,6 +354,70 @@ int moe_grouped_fc2_dense(const void* h, const uint8_t* h_scales, int h_fmt,
                           const int32_t* offsets, int E, int H, int F, int64_t rows,
                           void* y, int y_fmt, const void* w2d,
                           const uint8_t* w2d_scales, int T, hipStream_t stream);
+
+/*
+ * NVFP4 W4A4 expert MLP (sglang "Mistral Large 3 NVFP4 TRTLLM MoE support"
+ * page, title and Modifications: W4A4 NVFP4 MoE). Format: E2M1 codes two per
+ * byte (even element low nibble), one E4M3 scale per 16 consecutive values
+ * along K, one fp32 scale g per tensor; value = e2m1 * e4m3 * g. The block
+ * rule: s = E4M3 RNE(min(amax16 / fp32(6 g), 448)), codes = E2M1 RNE of
+ * clamp(v / fp32(s g), -6, 6) with v's sign bit (zero codes when s is 0).
+ * A weight matrix's g = amax / 2688 (1 for an all-zero matrix); the
+ * activations of a layer take fixed scales (x_g, h_g) from the caller.
+ */
+
+/*
+ * moe_nvfp4_tensor_scale — g[i] = fp32(amax(tensor i) / 2688), or 1 when
+ * tensor i is all zero, for n_tensors consecutive tensors of
+ * elems_per_tensor elements each of `in` (MOE_BF16 or MOE_F32, device).
+ * g: [n_tensors] fp32 device (its bytes are used as scratch first).
+ */
+int moe_nvfp4_tensor_scale(const void* in, int in_fmt, int n_tensors,
+                           int64_t elems_per_tensor, float* g, hipStream_t stream);
+
+/*
+ * moe_quantize_nvfp4 — NVFP4 block quantization of [rows, K] (MOE_BF16 or
+ * MOE_F32, row-major, device) along K; row r uses the tensor scale
+ * g[r / rows_per_tensor]. Outputs (each optional, at least one given):
+ * codes [rows, K/2] packed E2M1 (8-byte aligned), scales [rows, K/16] E4M3,
+ * vals [rows, K] bf16 = e2m1 * e4m3 (exact; the operand the NVFP4 GEMMs
+ * take for activations, the tensor scale left out). K % 16 == 0. The
+ * codes depend only on the input bits and g (IEEE fp32 divisions).
+ */
+int moe_quantize_nvfp4(const void* in, int in_fmt, int64_t rows, int K,
+                       int64_t rows_per_tensor, const float* g, uint8_t* codes,
+                       uint8_t* scales, void* vals, hipStream_t stream);
+
+/*
+ * moe_grouped_fc1_swiglu_nvfp4 — per expert segment (as
+ * moe_grouped_fc1_swiglu), with NVFP4 activations and weights:
+ *   A = x_g * w1_g[e] * (Xv_e . W1v_e^T)   (fp32 accumulate of exact products)
+ *   h = silu(A[:, :F]) * A[:, F:], NVFP4-quantized along F with scale h_g.
+ * a_vals   [rows or T, H] bf16 operand values of x (moe_quantize_nvfp4's
+ *          vals with tensor scale x_g), gathered through src_row as in
+ *          moe_grouped_fc1_swiglu when src_row is non-NULL.
+ * w1, w1_scales  NVFP4 [E, 2F, H] packed by moe_pack_weights (half = F);
+ *          w1_g [E] fp32 device: each expert matrix's tensor scale.
+ * h_vals   [rows, F] bf16 out: operand values of h (code * scale, h's
+ *          tensor scale h_g left out). Rows outside every segment are not
+ *          written.
+ * Limits: 1 <= E <= 1024, H % 128 == 0, F % 64 == 0; x_g, h_g > 0.
+ */
+int moe_grouped_fc1_swiglu_nvfp4(const void* a_vals, const int32_t* src_row,
+                                 const void* w1, const uint8_t* w1_scales,
+                                 const float* w1_g, float x_g, float h_g,
+                                 const int32_t* offsets, int E, int H, int F,
+                                 int64_t rows, void* h_vals, hipStream_t stream);
+
+/*
+ * moe_grouped_fc2_nvfp4 — per expert segment y = h_g * w2_g[e] *
+ * (Hv_e . W2v_e^T) in bf16 [rows, H]; h_vals as fc1 writes them, w2 /
+ * w2_scales NVFP4 [E, H, F] packed by moe_pack_weights (half = 0), w2_g
+ * [E] fp32 device. Same limits as the fc1 entry.
+ */
+int moe_grouped_fc2_nvfp4(const void* h_vals, const void* w2, const uint8_t* w2_scales,
+                          const float* w2_g, float h_g, const int32_t* offsets, int E,
+                          int H, int F, int64_t rows, void* y, hipStream_t stream);
 
 /*
  * moe_combine — weighted top-k reduce back to token order (TE

@@ -13,7 +13,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 
-MOE_F32, MOE_BF16, MOE_MXFP8_E4M3, MOE_MXFP4_E2M1 = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_MXFP8_E4M3, MOE_MXFP4_E2M1, MOE_NVFP4_E2M1 = 0, 1, 2, 3, 4
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_ALIGNMENT", -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
 
@@ -53,6 +53,10 @@ SIGNATURES = {
     "moe_route_bwd": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _F, _P, _P, _P,
                            _P, _P, _SZ, _P]),
     "moe_bias_update": (_I, [_P, _I, _F, _P, _P, _P]),
+    "moe_nvfp4_tensor_scale": (_I, [_P, _I, _I, _I64, _P, _P]),
+    "moe_quantize_nvfp4": (_I, [_P, _I, _I64, _I, _I64, _P, _P, _P, _P, _P]),
+    "moe_grouped_fc1_swiglu_nvfp4": (_I, [_P, _P, _P, _P, _P, _F, _F, _P, _I, _I, _I, _I64, _P, _P]),
+    "moe_grouped_fc2_nvfp4": (_I, [_P, _P, _P, _P, _F, _P, _I, _I, _I, _I64, _P, _P]),
     "moe_grouped_mlp_bwd_workspace": (_SZ, [_I, _I, _I, _I, _I, _I64, _I]),
     "moe_grouped_mlp_bwd": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                  _I, _I64, _P, _P, _P, _P, _SZ, _P]),
@@ -284,3 +288,27 @@ def moe_route_bwd(dout, y, act_fmt, row_map, topk_idx, logits, x, w_router, T, k
 def moe_bias_update(counts, E, gamma, bias, bias_out, stream=None):
     _check("moe_bias_update", load().moe_bias_update(
         _ptr(counts), E, gamma, _ptr(bias), _ptr(bias_out), _stream(stream)))
+
+
+def moe_nvfp4_tensor_scale(inp, in_fmt, n_tensors, elems_per_tensor, g, stream=None):
+    _check("moe_nvfp4_tensor_scale", load().moe_nvfp4_tensor_scale(
+        _ptr(inp), in_fmt, n_tensors, elems_per_tensor, _ptr(g), _stream(stream)))
+
+
+def moe_quantize_nvfp4(inp, in_fmt, rows, K, rows_per_tensor, g, codes, scales, vals, stream=None):
+    _check("moe_quantize_nvfp4", load().moe_quantize_nvfp4(
+        _ptr(inp), in_fmt, rows, K, rows_per_tensor, _ptr(g), _ptr(codes), _ptr(scales),
+        _ptr(vals), _stream(stream)))
+
+
+def moe_grouped_fc1_swiglu_nvfp4(a_vals, src_row, w1, w1_scales, w1_g, x_g, h_g, offsets, E, H, F,
+                                 rows, h_vals, stream=None):
+    _check("moe_grouped_fc1_swiglu_nvfp4", load().moe_grouped_fc1_swiglu_nvfp4(
+        _ptr(a_vals), _ptr(src_row), _ptr(w1), _ptr(w1_scales), _ptr(w1_g), x_g, h_g,
+        _ptr(offsets), E, H, F, rows, _ptr(h_vals), _stream(stream)))
+
+
+def moe_grouped_fc2_nvfp4(h_vals, w2, w2_scales, w2_g, h_g, offsets, E, H, F, rows, y, stream=None):
+    _check("moe_grouped_fc2_nvfp4", load().moe_grouped_fc2_nvfp4(
+        _ptr(h_vals), _ptr(w2), _ptr(w2_scales), _ptr(w2_g), h_g, _ptr(offsets), E, H, F, rows,
+        _ptr(y), _stream(stream)))

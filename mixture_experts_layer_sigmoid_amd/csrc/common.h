@@ -32,6 +32,7 @@ constexpr int kNumCu = 256;
 
 // ---- device-side scalar helpers ---------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));

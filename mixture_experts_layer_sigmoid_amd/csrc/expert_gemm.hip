@@ -51,6 +51,7 @@
 #include "expert_gemm.h"
 #include "gemm_util.h"
 #include "mx_codec.h"
+#include "nvfp4_codec.h"
 
 #include <algorithm>
 #include <string>
@@ -61,7 +62,7 @@ namespace {
 
 constexpr int kMaxGroups = 1024;
 constexpr int kStageBytes = 128;        // bytes of K per row per stage
-constexpr int kChunk = 4096;            // packed bytes per (column block, stage)
+constexpr int kPiece = 1024;            // one 16-byte-per-lane weight load
 constexpr int kTileCols = 256;          // weight rows per tile (8 column blocks)
 constexpr int kCs = kTileCols + 4;      // padded fp32 row stride of the epilogue tile
 // Scheduling cost of a tile = kTileCost + its rows: streaming a tile's
@@ -74,15 +75,27 @@ constexpr int kTileCost = 220;
 constexpr int kDenseParts = 8;
 constexpr int kMaxVirt = kMaxGroups + kDenseParts;
 
-enum { XOP_BF16 = 0, XOP_FP8 = 1, XOP_FP4 = 2 };
+enum { XOP_BF16 = 0, XOP_FP8 = 1, XOP_FP4 = 2, XOP_NVFP4 = 3 };
 enum { XEPI_SWIGLU = 0, XEPI_PLAIN = 1, XEPI_DSWIGLU = 2 };
 
-// k-steps of one stage and MX scale bytes per row per stage
+// Per operand format: k-steps of one stage (128 bytes of the activation
+// row), MX scale bytes of an activation row per stage, 1 KB weight loads per
+// column block and stage, packed weight-scale bytes per (column block,
+// stage). XOP_NVFP4: bf16 activation values (code * scale) against E2M1
+// weights with E4M3 scales per 16, converted to bf16 in registers (a stage
+// is 64 values: 32 bytes of codes per weight row, one 1 KB load).
 template <int OP>
 struct XOp {
+  static constexpr bool kBf16A = OP == XOP_BF16 || OP == XOP_NVFP4;
   static constexpr int kSub = OP == XOP_FP8 ? 2 : 4;
-  static constexpr int kScaleBytes = OP == XOP_BF16 ? 0 : (OP == XOP_FP8 ? 4 : 8);
-  static constexpr int kPackedScaleBytes = OP == XOP_BF16 ? 0 : 64 * kSub;  // per (cb, stage)
+  static constexpr int kScaleBytes = kBf16A ? 0 : (OP == XOP_FP8 ? 4 : 8);
+  static constexpr int kPieces = OP == XOP_NVFP4 ? 1 : 4;
+  static constexpr int kChunkW = kPieces * kPiece;                        // per (cb, stage)
+  // packed weight-scale bytes per (cb, stage): one byte per row and MX block
+  // (the two lane halves read different blocks); NVFP4 4 bytes per row, the
+  // same word for both lane halves (a k-step is one 16-block)
+  static constexpr int kPackedScaleBytes = OP == XOP_BF16 ? 0 : (OP == XOP_NVFP4 ? 128 : 64 * kSub);
+  static constexpr int kBLoads = 2 * kPieces + (OP == XOP_BF16 ? 0 : 2);   // per wave and stage
 };
 
 struct XArgs {
@@ -111,6 +124,11 @@ struct XArgs {
   float* act_save;           // fc1: optional fp32 [rows, 2F]
   const float* a_saved;      // dSwiGLU: saved fc1 output [rows, 2F] fp32
   float* da_f32;             // dSwiGLU: optional fp32 copy of dA [rows, 2F]
+  // NVFP4: tensor scale of the activations, per-expert tensor scales of the
+  // weights (applied to the fp32 accumulators) and of the output h (fc1)
+  float a_g;
+  const float* w_g;
+  float out_g;
   // optional dense expert (the shared expert) run by the same launch: it
   // takes d_rows rows, A rows d_a_row0.. and output rows d_row0.., packed
   // weights d_b / d_b_sc; null d_b: none
@@ -352,13 +370,14 @@ void expert_gemm_kernel(XArgs p) {
     const __amdgpu_buffer_rsrc_t asc_rs = buf_rsrc(kSB > 0 ? p.a_sc : p.a, kSB > 0 ? p.a_sc_bytes : 0u);
     const int cbw = active ? cb0 : 0;
     const uint8_t* b_exp = dn ? p.d_b : p.b + static_cast<int64_t>(e) * p.b_exp_bytes;
-    const uint8_t* b_src = b_exp + static_cast<int64_t>(cbw) * p.k_stages * kChunk + lane * 16;
-    const int64_t b_blk = static_cast<int64_t>(p.k_stages) * kChunk;   // next column block
+    const uint8_t* b_src = b_exp + static_cast<int64_t>(cbw) * p.k_stages * O::kChunkW + lane * 16;
+    const int64_t b_blk = static_cast<int64_t>(p.k_stages) * O::kChunkW;   // next column block
     const uint8_t* bsc_src = nullptr;
     int64_t bsc_blk = 0;
-    if constexpr (kSB > 0) {
+    if constexpr (OP != XOP_BF16) {
       const uint8_t* bsc_exp = dn ? p.d_b_sc : p.b_sc + static_cast<int64_t>(e) * p.b_sc_exp_bytes;
-      bsc_src = bsc_exp + static_cast<int64_t>(cbw) * p.k_stages * O::kPackedScaleBytes + lane * kSub;
+      bsc_src = bsc_exp + static_cast<int64_t>(cbw) * p.k_stages * O::kPackedScaleBytes +
+                (OP == XOP_NVFP4 ? (lane & 31) * 4 : lane * kSub);
       bsc_blk = static_cast<int64_t>(p.k_stages) * O::kPackedScaleBytes;
     }
 
@@ -379,13 +398,14 @@ void expert_gemm_kernel(XArgs p) {
       constexpr int SL = decltype(slot_c)::value;
       constexpr int NV = decltype(nv_c)::value;
       constexpr int OPN = decltype(op_c)::value;
-      constexpr int kB = 8 + (kSB > 0 ? 2 : 0);
-      if constexpr (OPN < 8) {
-        constexpr int c = OPN / 4, q = OPN % 4;
-        const uint8_t* bp = b_src + static_cast<int64_t>(kt) * kChunk;
-        bq[SL][c][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(bp + c * b_blk + q * 1024));
+      constexpr int kB = O::kBLoads;
+      constexpr int kW = 2 * O::kPieces;
+      if constexpr (OPN < kW) {
+        constexpr int c = OPN / O::kPieces, q = OPN % O::kPieces;
+        const uint8_t* bp = b_src + static_cast<int64_t>(kt) * O::kChunkW;
+        bq[SL][c][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(bp + c * b_blk + q * kPiece));
       } else if constexpr (OPN < kB) {
-        constexpr int c = OPN - 8;
+        constexpr int c = OPN - kW;
         const uint8_t* sp = bsc_src + static_cast<int64_t>(kt) * O::kPackedScaleBytes + c * bsc_blk;
         if constexpr (OP == XOP_FP8) bs[SL][c] = *reinterpret_cast<const uint16_t*>(sp);
         else bs[SL][c] = *reinterpret_cast<const uint32_t*>(sp);
@@ -403,7 +423,7 @@ void expert_gemm_kernel(XArgs p) {
     // a whole stage, activation operations first (the order the steps use)
     auto issue = [&](int kt, auto slot_c, auto nv_c) {
       constexpr int NV = decltype(nv_c)::value;
-      constexpr int kB = 8 + (kSB > 0 ? 2 : 0);
+      constexpr int kB = O::kBLoads;
       constexpr int kPer = kB + NV + kAScPerWave;
       static_for<kPer>([&](auto op_c) {
         issue_op(kt, slot_c, nv_c, std::integral_constant<int, (decltype(op_c)::value + kB) % kPer>{});
@@ -431,21 +451,22 @@ void expert_gemm_kernel(XArgs p) {
       constexpr int SL = decltype(slot_c)::value;
       constexpr int NV = decltype(nv_c)::value;
       constexpr int NSTEP = kSub * NV;
-      constexpr int kB = 8 + (kSB > 0 ? 2 : 0);  // weight loads per stage
+      constexpr int kB = O::kBLoads;  // weight loads per stage
       // operand ring depth: reads D - 1 steps ahead (an E4M3 step's two
       // 64-cycle MFMAs cover one LDS read; bf16 and E2M1 steps take 32 cycles
       // per MFMA and read two steps ahead)
       constexpr int D = OP == XOP_FP8 ? 2 : 3;
       const uint8_t* sa = smem + SL * S::kStage;
       const uint32_t* sasc = reinterpret_cast<const uint32_t*>(sa + S::kA);
-      using AFrag = std::conditional_t<OP == XOP_BF16, bf16x8_t, i32x8_t>;
+      using AFrag = std::conditional_t<O::kBf16A, bf16x8_t, i32x8_t>;
       AFrag afr[D];
       uint32_t asw[D];
+      bf16x8_t bcv[2];   // NVFP4: this k-step's weight operands converted to bf16
       auto fetch = [&](auto st_c) {
         constexpr int ST = decltype(st_c)::value;
         constexpr int s = ST / NV, i = ST % NV, buf = ST % D;
         const int row = 32 * i + (lane & 31);
-        if constexpr (OP == XOP_BF16) {
+        if constexpr (O::kBf16A) {
           afr[buf] = *reinterpret_cast<const bf16x8_t*>(sa + swz<128>(row, 2 * s + g));
         } else {
           if constexpr (OP == XOP_FP8) {
@@ -475,6 +496,28 @@ void expert_gemm_kernel(XArgs p) {
           const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, bq[SL][1][s]);
           acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], b0, acc[i][0], 0, 0, 0);
           acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], b1, acc[i][1], 0, 0, 0);
+        } else if constexpr (OP == XOP_NVFP4) {
+          // the lane's 8 codes of k-step s (dword s of its 16-byte load) times
+          // their E4M3 block scale (byte s of its scale word): E2M1 -> fp32
+          // with unit scale (exact), one fp32 product per value (exact: at
+          // most 6 significant bits), the high halves packed as bf16 (exact);
+          // converted once per k-step for all row blocks
+          if constexpr (i == 0) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const uint32_t w = bq[SL][c][0][s];
+              const float sc = e4m3_value((bs[SL][c] >> (8 * s)) & 0xFFu);
+              uint32_t pk[4];
+              static_for<4>([&](auto b_c) {
+                const f32x2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, decltype(b_c)::value);
+                pk[decltype(b_c)::value] = __builtin_amdgcn_perm(__float_as_uint(f[1] * sc),
+                                                                 __float_as_uint(f[0] * sc), 0x07060302u);
+              });
+              bcv[c] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+            }
+          }
+          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], bcv[0], acc[i][0], 0, 0, 0);
+          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], bcv[1], acc[i][1], 0, 0, 0);
         } else {
           i32x8_t b0, b1;
           if constexpr (OP == XOP_FP8) {
@@ -516,7 +559,7 @@ void expert_gemm_kernel(XArgs p) {
     // follow in a short tail. ----
     auto run = [&](auto nv_c) {
       constexpr int NV = decltype(nv_c)::value;
-      constexpr int kPer = NV + kAScPerWave + 8 + (kSB > 0 ? 2 : 0);  // loads per stage
+      constexpr int kPer = NV + kAScPerWave + O::kBLoads;  // loads per stage
       static_assert((P - 2) * kPer <= 62, "vmcnt range");
       // loads still allowed in flight at a step's wait: the weight loads of
       // the stages after the next (none with a two-stage ring)
@@ -526,7 +569,7 @@ void expert_gemm_kernel(XArgs p) {
       });
       auto step = [&](int kt, auto j_c) {
         constexpr int J = decltype(j_c)::value;
-        constexpr int kB = 8 + (kSB > 0 ? 2 : 0);
+        constexpr int kB = O::kBLoads;
         using NSL = std::integral_constant<int, (J + P - 1) % P>;
         const int kt_next = min(kt + P - 1, KT - 1);
         wait_vmcnt<kWait>();
@@ -559,6 +602,9 @@ void expert_gemm_kernel(XArgs p) {
     // ---- epilogue in passes of up to 128 rows through an fp32 LDS tile ----
     // C layout of a 32x32 MFMA: lane l, element r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
     float* cs = reinterpret_cast<float*>(smem);
+    // NVFP4: the accumulators hold sums of (code * scale) products; the
+    // activation and the expert's weight tensor scales multiply them here
+    const float gs = OP == XOP_NVFP4 ? p.a_g * p.w_g[e] : 1.f;
     constexpr int kPassRB = kPassRows / 32 < MAXNV ? kPassRows / 32 : MAXNV;
     for (int pass = 0; pass * kPassRB < nrb; ++pass) {
       const int prow0 = pass * kPassRB * 32;
@@ -576,7 +622,7 @@ void expert_gemm_kernel(XArgs p) {
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int row = (i - pass * kPassRB) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                cs[row * kCs + hcol] = silu_mul(acc[i][0][r], acc[i][1][r]);
+                cs[row * kCs + hcol] = silu_mul(acc[i][0][r] * gs, acc[i][1][r] * gs);
               }
             } else {
               // gate | up (SwiGLU with the fp32 save) or the plain tile
@@ -587,7 +633,7 @@ void expert_gemm_kernel(XArgs p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                   const int row = (i - pass * kPassRB) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                  cs[row * kCs + col] = acc[i][c][r];
+                  cs[row * kCs + col] = OP == XOP_NVFP4 ? acc[i][c][r] * gs : acc[i][c][r];
                 }
               }
             }
@@ -616,6 +662,26 @@ void expert_gemm_kernel(XArgs p) {
               store8_f32(ar, gp);
               store8_f32(ar + F, gp + 128);
             }
+          }
+        } else if constexpr (OUTF == MOE_NVFP4_E2M1) {
+          // h (formed in registers above, columns [0, 128) of the tile) in
+          // blocks of 16 -> NVFP4 with the tensor scale of h; stored as the
+          // operand values code * scale (bf16, exact) that fc2 consumes
+          const int nblk = width / 16;
+          const float d6 = 6.f * p.out_g;
+          for (int i = tid; i < prows * nblk; i += 256) {
+            const int row = i / nblk, blk = i % nblk;
+            const bool zero = p.gather && s_src[prow0 + row] < 0;
+            const float* gp = cs + row * kCs + blk * 16;
+            float v[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = zero ? 0.f : gp[q];
+            uint32_t cw[2], vw[8];
+            nvfp4_encode_block(v, p.out_g, d6, cw, vw);
+            const int64_t grow = row0 + prow0 + row;
+            u32x4_t* o = reinterpret_cast<u32x4_t*>(p.out + grow * p.out_row_bytes + (hc0 + blk * 16) * 2);
+            o[0] = u32x4_t{vw[0], vw[1], vw[2], vw[3]};
+            o[1] = u32x4_t{vw[4], vw[5], vw[6], vw[7]};
           }
         } else {
           constexpr bool fp4 = OUTF == MOE_MXFP4_E2M1;
@@ -799,10 +865,58 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restr
   }
 }
 
+// NVFP4 weights for the bf16 k-steps (16 values): packed[e][cb][s][lane]
+// 16 bytes = for k-step ks < 4 the 4 code bytes of row R(cb, lane) at byte
+// 32 s + 8 ks + 4 (lane / 32) (the lane's 8 values of the k-step); scales
+// [e][cb][s][r < 32] 4 bytes = for ks < 4 the E4M3 scale of row R(cb, r)'s
+// block 4 s + ks (one block of 16 per k-step, read by both lane halves):
+// as many bytes as the unpacked scales.
+__global__ __launch_bounds__(256) void pack_nvfp4_codes_kernel(const uint8_t* __restrict__ w, int64_t E,
+                                                               int N, int64_t kbytes, int half,
+                                                               uint8_t* __restrict__ out) {
+  const int ncb = N / 32;
+  const int64_t S = kbytes / 32;     // 64-value stages
+  const int64_t total = E * ncb * S * 64;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += 256ll * gridDim.x) {
+    const int lane = static_cast<int>(i & 63);
+    const int64_t rest = i >> 6;
+    const int64_t s = rest % S;
+    const int64_t cbe = rest / S;
+    const int cb = static_cast<int>(cbe % ncb);
+    const int64_t e = cbe / ncb;
+    const uint8_t* row = w + (e * N + packed_row(cb, lane, half)) * kbytes + 32 * s + 4 * (lane >> 5);
+    u32x4_t v;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) v[ks] = *reinterpret_cast<const uint32_t*>(row + 8 * ks);
+    *reinterpret_cast<u32x4_t*>(out + i * 16) = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_nvfp4_scales_kernel(const uint8_t* __restrict__ sc, int64_t E,
+                                                                int N, int64_t kblocks, int half,
+                                                                uint8_t* __restrict__ out) {
+  const int ncb = N / 32;
+  const int64_t S = kblocks / 4;
+  const int64_t total = E * ncb * S * 32;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += 256ll * gridDim.x) {
+    const int r = static_cast<int>(i & 31);
+    const int64_t rest = i >> 5;
+    const int64_t s = rest % S;
+    const int64_t cbe = rest / S;
+    const int cb = static_cast<int>(cbe % ncb);
+    const int64_t e = cbe / ncb;
+    const uint8_t* src = sc + (e * N + packed_row(cb, r, half)) * kblocks + 4 * s;
+    reinterpret_cast<uint32_t*>(out)[i] = static_cast<uint32_t>(src[0]) | (static_cast<uint32_t>(src[1]) << 8) |
+                                          (static_cast<uint32_t>(src[2]) << 16) |
+                                          (static_cast<uint32_t>(src[3]) << 24);
+  }
+}
+
 }  // namespace
 
 int xop_of(int fmt) {
-  return fmt == MOE_BF16 ? XOP_BF16 : (fmt == MOE_MXFP8_E4M3 ? XOP_FP8 : XOP_FP4);
+  return fmt == MOE_BF16 ? XOP_BF16
+                         : (fmt == MOE_MXFP8_E4M3 ? XOP_FP8 : (fmt == MOE_NVFP4_E2M1 ? XOP_NVFP4 : XOP_FP4));
 }
 
 // Launch of one grouped expert GEMM with packed weights (expert_gemm.h).
@@ -810,8 +924,14 @@ int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const
                 const void* wp, const uint8_t* wp_scales, const int32_t* offsets, int E, int N,
                 int K, int64_t rows, int half, void* out, uint8_t* out_scales, float* act_save,
                 const float* a_saved, float* da_f32, hipStream_t stream,
-                const DenseExpert* dense) {
-  const int bits = fmt == MOE_BF16 ? 16 : (fmt == MOE_MXFP8_E4M3 ? 8 : 4);
+                const DenseExpert* dense, const NvScales* nv) {
+  // bits of an activation element and of a stored weight element (the
+  // NVFP4 activation operand arrives as bf16 values code * scale)
+  const bool nvfp4 = fmt == MOE_NVFP4_E2M1;
+  const int bits = fmt == MOE_BF16 || nvfp4 ? 16 : (fmt == MOE_MXFP8_E4M3 ? 8 : 4);
+  const int wbits = fmt == MOE_BF16 ? 16 : (fmt == MOE_MXFP8_E4M3 ? 8 : 4);
+  MOE_REQUIRE(!nvfp4 || (nv && kind != 2 && !(dense && dense->rows > 0)), MOE_ERR_UNSUPPORTED,
+              "grouped expert GEMM: NVFP4 runs fc1 / fc2 of routed experts only, with its scales");
   // activation row offsets are 32-bit inside the kernel; a gathered source
   // has at most `rows` rows as well
   const int64_t a_rows =
@@ -829,9 +949,9 @@ int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const
   x.a_sc_bytes = static_cast<uint32_t>(a_rows * (K / 32));
   x.gather = gather;
   x.b = static_cast<const uint8_t*>(wp);
-  x.b_exp_bytes = static_cast<int64_t>(N) * K * bits / 8;
+  x.b_exp_bytes = static_cast<int64_t>(N) * K * wbits / 8;
   x.b_sc = wp_scales;
-  x.b_sc_exp_bytes = static_cast<int64_t>(N) * (K / 32);
+  x.b_sc_exp_bytes = static_cast<int64_t>(N) * (K / (nvfp4 ? 16 : 32));
   x.ncb = N / 32;
   x.n_tiles = kind == 0 ? (N / 2 + 127) / 128 : (N + kTileCols - 1) / kTileCols;
   x.k_stages = static_cast<int>(x.a_row_bytes / kStageBytes);
@@ -844,6 +964,11 @@ int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const
   x.act_save = act_save;
   x.a_saved = a_saved;
   x.da_f32 = da_f32;
+  if (nvfp4) {
+    x.a_g = nv->a_g;
+    x.w_g = nv->w_g;
+    x.out_g = nv->out_g;
+  }
   if (dense && dense->rows > 0) {
     x.d_b = static_cast<const uint8_t*>(dense->w);
     x.d_b_sc = dense->w_scales;
@@ -852,7 +977,7 @@ int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const
     x.d_a_row0 = dense->a_row0;
   }
   const int outw = kind == 0 ? half : (kind == 1 ? N : 2 * half);  // output row elements
-  const bool mx_out = kind != 1 && fmt != MOE_BF16;
+  const bool mx_out = kind != 1 && (fmt == MOE_MXFP8_E4M3 || fmt == MOE_MXFP4_E2M1);
   x.out_row_bytes = mx_out ? static_cast<int64_t>(outw) * bits / 8 : static_cast<int64_t>(outw) * 2;
   x.out_sc_row_bytes = outw / 32;
   const dim3 block(256);
@@ -861,15 +986,17 @@ int expert_gemm(int kind, const void* a, const uint8_t* a_scales, int fmt, const
     constexpr int OC = decltype(oc_c)::value;
     const dim3 grid(kNumCu * OC);
     auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, x); };
-    switch (kind * 3 + xop_of(fmt)) {
+    switch (kind * 4 + xop_of(fmt)) {
       case 0: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_SWIGLU, MOE_BF16>); break;
       case 1: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_SWIGLU, MOE_MXFP8_E4M3>); break;
       case 2: go(expert_gemm_kernel<MN, PP, OC, XOP_FP4, XEPI_SWIGLU, MOE_MXFP4_E2M1>); break;
-      case 3: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_PLAIN, MOE_BF16>); break;
-      case 4: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_PLAIN, MOE_BF16>); break;
-      case 5: go(expert_gemm_kernel<MN, PP, OC, XOP_FP4, XEPI_PLAIN, MOE_BF16>); break;
-      case 6: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_DSWIGLU, MOE_BF16>); break;
-      case 7: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_DSWIGLU, MOE_MXFP8_E4M3>); break;
+      case 3: go(expert_gemm_kernel<MN, PP, OC, XOP_NVFP4, XEPI_SWIGLU, MOE_NVFP4_E2M1>); break;
+      case 4: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_PLAIN, MOE_BF16>); break;
+      case 5: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_PLAIN, MOE_BF16>); break;
+      case 6: go(expert_gemm_kernel<MN, PP, OC, XOP_FP4, XEPI_PLAIN, MOE_BF16>); break;
+      case 7: go(expert_gemm_kernel<MN, PP, OC, XOP_NVFP4, XEPI_PLAIN, MOE_BF16>); break;
+      case 8: go(expert_gemm_kernel<MN, PP, OC, XOP_BF16, XEPI_DSWIGLU, MOE_BF16>); break;
+      case 9: go(expert_gemm_kernel<MN, PP, OC, XOP_FP8, XEPI_DSWIGLU, MOE_MXFP8_E4M3>); break;
       default: go(expert_gemm_kernel<MN, PP, OC, XOP_FP4, XEPI_DSWIGLU, MOE_MXFP4_E2M1>); break;
     }
   };
@@ -892,8 +1019,26 @@ extern "C" int moe_pack_weights(const void* w, const uint8_t* w_scales, int fmt,
                                 hipStream_t stream) {
   clear_error();
   MOE_REQUIRE(E >= 1 && N > 0 && K > 0, MOE_ERR_INVALID_ARG, "moe_pack_weights: need E, N, K > 0");
-  MOE_REQUIRE(fmt == MOE_BF16 || fmt == MOE_MXFP8_E4M3 || fmt == MOE_MXFP4_E2M1, MOE_ERR_UNSUPPORTED,
-              "moe_pack_weights: fmt must be MOE_BF16 or an MX format");
+  MOE_REQUIRE(fmt == MOE_BF16 || fmt == MOE_MXFP8_E4M3 || fmt == MOE_MXFP4_E2M1 ||
+                  fmt == MOE_NVFP4_E2M1,
+              MOE_ERR_UNSUPPORTED, "moe_pack_weights: fmt must be MOE_BF16, an MX format or NVFP4");
+  if (fmt == MOE_NVFP4_E2M1) {
+    MOE_REQUIRE(N % 64 == 0 && K % 64 == 0, MOE_ERR_INVALID_ARG,
+                "moe_pack_weights: NVFP4 needs N % 64 == 0 and K % 64 == 0");
+    MOE_REQUIRE(half == 0 || (half > 0 && N == 2 * half && half % 32 == 0), MOE_ERR_INVALID_ARG,
+                "moe_pack_weights: gate/up pairing needs N == 2 * half and half % 32 == 0");
+    MOE_REQUIRE(w && out && w_scales && out_scales, MOE_ERR_INVALID_ARG, "moe_pack_weights: null pointer");
+    MOE_REQUIRE(aligned16(w) && aligned16(out) && (reinterpret_cast<uintptr_t>(out_scales) & 3u) == 0,
+                MOE_ERR_ALIGNMENT, "moe_pack_weights: w and out must be 16-byte, out_scales 4-byte aligned");
+    const int64_t items = static_cast<int64_t>(E) * (N / 32) * (K / 64) * 64;
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>(65536, (items + 255) / 256));
+    hipLaunchKernelGGL(pack_nvfp4_codes_kernel, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint8_t*>(w), static_cast<int64_t>(E), N,
+                       static_cast<int64_t>(K / 2), half, static_cast<uint8_t*>(out));
+    hipLaunchKernelGGL(pack_nvfp4_scales_kernel, dim3(grid), dim3(256), 0, stream, w_scales,
+                       static_cast<int64_t>(E), N, static_cast<int64_t>(K / 16), half, out_scales);
+    return check_launch("moe_pack_weights");
+  }
   const int bits = fmt == MOE_BF16 ? 16 : (fmt == MOE_MXFP8_E4M3 ? 8 : 4);
   const int64_t kbytes = static_cast<int64_t>(K) * bits / 8;
   MOE_REQUIRE(N % 64 == 0 && kbytes % kStageBytes == 0, MOE_ERR_INVALID_ARG,

@@ -389,3 +389,57 @@ extern "C" int moe_grouped_fc1_dgrad(const void* da, const uint8_t* da_scales, i
   if (rows == 0) return MOE_OK;
   return fc2_impl(da, da_scales, fmt, w1t, w1t_scales, offsets, E, H, 2 * F, rows, dx_perm, stream);
 }
+
+// ---------------------------------------------------------------------------
+// NVFP4 W4A4 grouped MLP (page "Mistral Large 3 NVFP4 TRTLLM MoE support",
+// title and Modifications): E2M1 weights with E4M3 scales per 16 and one fp32
+// scale per expert matrix, streamed 4-bit and converted to exact bf16 values
+// in registers for bf16 matrix instructions; activations as bf16 operand
+// values code * scale; every tensor scale applied to the fp32 accumulators.
+
+static int check_nvfp4(const char* fn, int E, int H, int F, int64_t rows) {
+  std::string f(fn);
+  MOE_REQUIRE(E >= 1 && E <= kMaxGroups && H > 0 && F > 0 && rows >= 0, MOE_ERR_INVALID_ARG,
+              f + ": need 1 <= E <= 1024, H > 0, F > 0, rows >= 0");
+  MOE_REQUIRE(H % 128 == 0 && F % 64 == 0, MOE_ERR_INVALID_ARG,
+              f + ": NVFP4 needs H % 128 == 0 and F % 64 == 0");
+  return MOE_OK;
+}
+
+extern "C" int moe_grouped_fc1_swiglu_nvfp4(const void* a_vals, const int32_t* src_row,
+                                            const void* w1, const uint8_t* w1_scales,
+                                            const float* w1_g, float x_g, float h_g,
+                                            const int32_t* offsets, int E, int H, int F,
+                                            int64_t rows, void* h_vals, hipStream_t stream) {
+  clear_error();
+  int st = check_nvfp4("moe_grouped_fc1_swiglu_nvfp4", E, H, F, rows);
+  if (st) return st;
+  if (rows == 0) return MOE_OK;
+  MOE_REQUIRE(a_vals && w1 && w1_scales && w1_g && offsets && h_vals, MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc1_swiglu_nvfp4: null pointer");
+  MOE_REQUIRE(aligned16(a_vals) && aligned16(w1) && aligned16(h_vals) && scale_aligned(w1_scales),
+              MOE_ERR_ALIGNMENT,
+              "moe_grouped_fc1_swiglu_nvfp4: tensors 16-byte, weight scales 4-byte aligned");
+  MOE_REQUIRE(x_g > 0.f && h_g > 0.f, MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc1_swiglu_nvfp4: tensor scales must be positive");
+  const NvScales nv{x_g, w1_g, h_g};
+  return expert_gemm(0, a_vals, nullptr, MOE_NVFP4_E2M1, src_row, w1, w1_scales, offsets, E, 2 * F, H,
+                     rows, F, h_vals, nullptr, nullptr, nullptr, nullptr, stream, nullptr, &nv);
+}
+
+extern "C" int moe_grouped_fc2_nvfp4(const void* h_vals, const void* w2, const uint8_t* w2_scales,
+                                     const float* w2_g, float h_g, const int32_t* offsets, int E,
+                                     int H, int F, int64_t rows, void* y, hipStream_t stream) {
+  clear_error();
+  int st = check_nvfp4("moe_grouped_fc2_nvfp4", E, H, F, rows);
+  if (st) return st;
+  if (rows == 0) return MOE_OK;
+  MOE_REQUIRE(h_vals && w2 && w2_scales && w2_g && offsets && y, MOE_ERR_INVALID_ARG,
+              "moe_grouped_fc2_nvfp4: null pointer");
+  MOE_REQUIRE(aligned16(h_vals) && aligned16(w2) && aligned16(y) && scale_aligned(w2_scales),
+              MOE_ERR_ALIGNMENT, "moe_grouped_fc2_nvfp4: tensors 16-byte, weight scales 4-byte aligned");
+  MOE_REQUIRE(h_g > 0.f, MOE_ERR_INVALID_ARG, "moe_grouped_fc2_nvfp4: tensor scale must be positive");
+  const NvScales nv{h_g, w2_g, 0.f};
+  return expert_gemm(1, h_vals, nullptr, MOE_NVFP4_E2M1, nullptr, w2, w2_scales, offsets, E, H, F,
+                     rows, 0, y, nullptr, nullptr, nullptr, nullptr, stream, nullptr, &nv);
+}

@@ -12,7 +12,9 @@ and then issues, on one stream:
 Without a shared expert, or when it cannot share the routed launches (fp32
 layers, F_shared != F), the routed experts run through
 moe_grouped_fc1_swiglu / moe_grouped_fc2 and the shared expert through the
-same two calls with E = 1.
+same two calls with E = 1. The NVFP4 layer quantizes x with
+moe_quantize_nvfp4 (operand values, fixed tensor scale) and runs
+moe_grouped_fc1_swiglu_nvfp4 -> moe_grouped_fc2_nvfp4 (no shared expert).
 
 MoEBackward runs the backward of the routed expert path (MXFP8), reusing
 the forward's routing and maps, as one moe_grouped_mlp_bwd call, whose
@@ -37,7 +39,8 @@ import torch
 
 from . import _lib as L
 
-FMT = {"fp32": L.MOE_F32, "bf16": L.MOE_BF16, "mxfp8": L.MOE_MXFP8_E4M3, "mxfp4": L.MOE_MXFP4_E2M1}
+FMT = {"fp32": L.MOE_F32, "bf16": L.MOE_BF16, "mxfp8": L.MOE_MXFP8_E4M3, "mxfp4": L.MOE_MXFP4_E2M1,
+       "nvfp4": L.MOE_NVFP4_E2M1}
 
 
 def is_mx(fmt: str) -> bool:
@@ -76,12 +79,37 @@ def quantize_mx_t(t: torch.Tensor, fmt: str, stream=None):
     return codes, scales
 
 
+def quantize_nvfp4(t: torch.Tensor, g: torch.Tensor, rows_per_tensor: int, codes=True,
+                   vals=False, stream=None):
+    """NVFP4-quantize a [..., K] fp32/bf16 tensor along its last axis with
+    moe_quantize_nvfp4; row r uses tensor scale g[r // rows_per_tensor].
+    Returns (codes uint8 [..., K/2] or None, scales uint8 [..., K/16] or
+    None, vals bf16 [..., K] or None)."""
+    K = t.shape[-1]
+    rows = t.numel() // K
+    lead = t.shape[:-1]
+    c = torch.empty(lead + (K // 2,), dtype=torch.uint8, device=t.device) if codes else None
+    sc = torch.empty(lead + (K // 16,), dtype=torch.uint8, device=t.device) if codes else None
+    v = torch.empty(lead + (K,), dtype=torch.bfloat16, device=t.device) if vals else None
+    L.moe_quantize_nvfp4(t, L.fmt_of_dtype(t), rows, K, rows_per_tensor, g, c, sc, v, stream)
+    return c, sc, v
+
+
+def nvfp4_tensor_scales(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """fp32 [E] tensor scales (amax / 2688) of the E matrices of w [E, N, K]
+    (moe_nvfp4_tensor_scale)."""
+    E = w.shape[0]
+    g = torch.empty((E,), dtype=torch.float32, device=w.device)
+    L.moe_nvfp4_tensor_scale(w, L.fmt_of_dtype(w), E, w[0].numel(), g, stream)
+    return g
+
+
 def pack_weights(codes: torch.Tensor, scales, fmt: str, half: int = 0, stream=None):
     """moe_pack_weights of [E, N, K] stored weights (bf16 values or MX codes
     with [E, N, K/32] scales) into the grouped GEMMs' streaming order.
     Returns (packed uint8 [E, bytes per expert], packed scales or None)."""
     E, N = codes.shape[0], codes.shape[1]
-    K = codes.shape[2] * (2 if fmt == "mxfp4" else 1)
+    K = codes.shape[2] * (2 if fmt in ("mxfp4", "nvfp4") else 1)
     nbytes = codes[0].numel() * codes.element_size()
     out = torch.empty((E, nbytes), dtype=torch.uint8, device=codes.device)
     out_sc = torch.empty_like(scales) if scales is not None else None
@@ -97,7 +125,9 @@ class ExpertWeights:
     moe_pack_weights, w1 with its gate/up halves paired. With
     `transposed`, also the copies the backward's data-gradient GEMMs
     contract over: w1t [E, H, 2F] (blocks along 2F) and w2t [E, F, H]
-    (blocks along H), quantized from the same masters and packed."""
+    (blocks along H), quantized from the same masters and packed. NVFP4:
+    E2M1 codes with E4M3 scales per 16 values along K, packed, and each
+    expert matrix's fp32 tensor scale in w1_g / w2_g [E]."""
     w1: torch.Tensor
     w2: torch.Tensor
     w1_sc: torch.Tensor | None = None
@@ -106,6 +136,8 @@ class ExpertWeights:
     w2t: torch.Tensor | None = None
     w1t_sc: torch.Tensor | None = None
     w2t_sc: torch.Tensor | None = None
+    w1_g: torch.Tensor | None = None
+    w2_g: torch.Tensor | None = None
 
     @staticmethod
     def from_dense(w1: torch.Tensor, w2: torch.Tensor, fmt: str, stream=None,
@@ -123,6 +155,18 @@ class ExpertWeights:
             p1, _ = pack_weights(w1, None, fmt, F, stream)
             p2, _ = pack_weights(w2, None, fmt, 0, stream)
             return ExpertWeights(p1, p2)
+        if fmt == "nvfp4":
+            if transposed:
+                raise ValueError("the NVFP4 layer runs the forward only")
+            gs, packed = [], []
+            for w, half in ((w1, F), (w2, 0)):
+                g = nvfp4_tensor_scales(w, stream)
+                c, sc, _ = quantize_nvfp4(w, g, w.shape[1], stream=stream)
+                packed.append(pack_weights(c, sc, fmt, half, stream))
+                gs.append(g)
+                del c, sc
+            (p1, q1), (p2, q2) = packed
+            return ExpertWeights(p1, p2, q1, q2, w1_g=gs[0], w2_g=gs[1])
         c1, s1 = quantize_mx(w1, fmt, stream)
         c2, s2 = quantize_mx(w2, fmt, stream)
         p1, q1 = pack_weights(c1, s1, fmt, F, stream)
@@ -145,11 +189,12 @@ class ExpertWeights:
 class MoEForward:
     def __init__(self, *, T, H, F, E, n_group, topk_group, k, routed_scale, fmt,
                  F_shared=0, align=1, device="cuda", keep_logits=False, save_act=False,
-                 fuse_shared=None):
+                 fuse_shared=None, x_global=0.0, h_global=0.0):
         """fuse_shared: run the shared expert inside the routed fc1 / fc2
         launches (its tiles fill the matrix cores while the routed tiles
         stream weights). Default: whenever the shared expert has the routed
-        experts' width and the layer is not fp32."""
+        experts' width and the layer is not fp32. x_global / h_global: the
+        NVFP4 layer's fixed tensor scales of the hidden states and of h."""
         self.T, self.H, self.F, self.E = T, H, F, E
         self.n_group, self.topk_group, self.k = n_group, topk_group, k
         self.routed_scale, self.fmt, self.F_shared, self.align = routed_scale, fmt, F_shared, align
@@ -172,9 +217,19 @@ class MoEForward:
         if is_mx(fmt):
             self.xq = torch.empty((T, code_cols(H, fmt)), dtype=torch.uint8, device=dev)
             self.xq_sc = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+        elif fmt == "nvfp4":
+            if not (x_global > 0 and h_global > 0):
+                raise ValueError("the NVFP4 layer needs positive x_global and h_global")
+            if F_shared:
+                raise ValueError("the NVFP4 layer has no shared expert")
+            # operand values of x (code * scale) and its tensor scale
+            self.xq = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            self.xq_sc = None
+            self.x_g = torch.full((1,), x_global, dtype=torch.float32, device=dev)
         else:
             self.xq = self.xq_sc = None
-        can_fuse = bool(F_shared) and F_shared == F and fmt != "fp32" and T > 0
+        self.x_global, self.h_global = x_global, h_global
+        can_fuse = bool(F_shared) and F_shared == F and fmt not in ("fp32", "nvfp4") and T > 0
         if fuse_shared is None:
             fuse_shared = can_fuse
         if fuse_shared and not can_fuse:
@@ -203,6 +258,7 @@ class MoEForward:
         if is_mx(self.fmt):
             return (torch.empty((rows, code_cols(F, self.fmt)), dtype=torch.uint8, device=dev),
                     torch.empty((rows, F // 32), dtype=torch.uint8, device=dev))
+        # bf16 values (NVFP4: operand values code * scale)
         return torch.empty((rows, F), dtype=self.act_dtype, device=dev), None
 
     def route(self, x, w_router, bias, logits_in=None, stream=None):
@@ -214,6 +270,9 @@ class MoEForward:
         if is_mx(self.fmt):
             L.moe_quantize_mx(x, self.act_fmt, self.T, self.H, 0, FMT[self.fmt], self.xq, self.xq_sc,
                               stream)
+        elif self.fmt == "nvfp4" and self.T > 0:
+            L.moe_quantize_nvfp4(x, self.act_fmt, self.T, self.H, self.T, self.x_g, None, None,
+                                 self.xq, stream)
 
     def permute(self, stream=None):
         L.moe_permute(self.topk_idx, self.T, self.k, self.E, self.align, None, 0, None, 0,
@@ -223,6 +282,13 @@ class MoEForward:
     def experts_fc1(self, x, ew: ExpertWeights, stream=None, sw: ExpertWeights | None = None):
         """Routed fc1 + SwiGLU; with fuse_shared also the shared expert's
         (sw required)."""
+        if self.fmt == "nvfp4":
+            if self.act_save is not None:
+                raise ValueError("the NVFP4 layer keeps no fc1 output")
+            L.moe_grouped_fc1_swiglu_nvfp4(self.xq, self.src_row, ew.w1, ew.w1_sc, ew.w1_g,
+                                           self.x_global, self.h_global, self.offsets, self.E,
+                                           self.H, self.F, self.bound, self.h, stream)
+            return
         a, a_sc = (self.xq, self.xq_sc) if is_mx(self.fmt) else (x, None)
         f = FMT[self.fmt]
         if self.fuse_shared:
@@ -236,6 +302,10 @@ class MoEForward:
                                      self.h_sc, stream)
 
     def experts_fc2(self, ew: ExpertWeights, stream=None, sw: ExpertWeights | None = None):
+        if self.fmt == "nvfp4":
+            L.moe_grouped_fc2_nvfp4(self.h, ew.w2, ew.w2_sc, ew.w2_g, self.h_global, self.offsets,
+                                    self.E, self.H, self.F, self.bound, self.y_rows, stream)
+            return
         f = FMT[self.fmt]
         if self.fuse_shared:
             L.moe_grouped_fc2_dense(self.h, self.h_sc, f, ew.w2, ew.w2_sc, f, self.offsets,
@@ -283,7 +353,8 @@ class MoEForward:
         return cls(T=cfg.T if T is None else T, H=cfg.H, F=cfg.F, E=cfg.E, n_group=cfg.n_group,
                    topk_group=cfg.topk_group, k=cfg.k, routed_scale=cfg.routed_scale, fmt=cfg.fmt,
                    F_shared=cfg.F_shared if cfg.n_shared else 0, align=cfg.align, device=device,
-                   keep_logits=keep_logits, save_act=save_act, fuse_shared=fuse_shared)
+                   keep_logits=keep_logits, save_act=save_act, fuse_shared=fuse_shared,
+                   x_global=cfg.x_global, h_global=cfg.h_global)
 
 
 class MoEBackward:

@@ -301,3 +301,48 @@ def test_route_bwd_validation(lib):
     assert call(T=0, dout=None, y=None) == OK    # empty batch: nothing to do
     assert lib.moe_bias_update(A, 0, 1e-3, A, A, None) == INVALID
     assert lib.moe_bias_update(None, 8, 1e-3, A, A, None) == INVALID
+
+
+def test_nvfp4_validation(lib):
+    """NVFP4 quantizer, tensor scale, pack and the W4A4 fc1 / fc2 entries."""
+    q = lambda **k: lib.moe_quantize_nvfp4(k.get("inp", A), k.get("fi", 1), k.get("rows", 4),
+                                           k.get("K", 64), k.get("rpt", 4), k.get("g", A),
+                                           k.get("c", A), k.get("s", A), k.get("v"), None)
+    assert q(K=40) == INVALID                    # blocks of 16
+    assert q(rpt=0) == INVALID
+    assert q(fi=2) == UNSUPPORTED
+    assert q(c=None, s=None) == INVALID          # no output
+    assert q(c=A + 4) == ALIGN
+    assert q(v=A + 8) == ALIGN
+    assert q(g=None) == INVALID
+    assert q(rows=0, inp=None, g=None) == OK
+    ts = lambda **k: lib.moe_nvfp4_tensor_scale(k.get("inp", A), k.get("fi", 1), k.get("n", 2),
+                                                k.get("per", 64), k.get("g", A), None)
+    assert ts(n=0) == INVALID
+    assert ts(per=0) == INVALID
+    assert ts(fi=3) == UNSUPPORTED
+    assert ts(g=None) == INVALID
+    pk = lambda **k: lib.moe_pack_weights(A, k.get("sc", A), 4, 2, k.get("N", 128), k.get("K", 128),
+                                          k.get("half", 64), A, k.get("osc", A), None)
+    assert pk(K=96) == INVALID                   # 64-value stages
+    assert pk(N=96, half=48) == INVALID
+    assert pk(sc=None) == INVALID
+    assert pk(osc=A + 2) == ALIGN
+    f1 = lambda **k: lib.moe_grouped_fc1_swiglu_nvfp4(
+        k.get("a", A), None, A, k.get("ws", A), A, k.get("xg", 2.0 ** -8), 2.0 ** -6, A, 8,
+        k.get("H", 256), k.get("F", 128), k.get("rows", 100), k.get("h", A), None)
+    assert f1(H=192) == INVALID
+    assert f1(F=96) == INVALID
+    assert f1(xg=0.0) == INVALID
+    assert f1(h=A + 8) == ALIGN
+    assert f1(ws=A + 1) == ALIGN
+    assert f1(rows=0, a=None, h=None) == OK
+    f2 = lambda **k: lib.moe_grouped_fc2_nvfp4(A, A, A, A, k.get("hg", 2.0 ** -6), A, k.get("E", 8),
+                                               256, 128, 100, k.get("y", A), None)
+    assert f2(E=0) == INVALID
+    assert f2(hg=-1.0) == INVALID
+    assert f2(y=A + 2) == ALIGN
+    # the generic grouped entries do not take NVFP4 (its tensor scales are
+    # arguments of the NVFP4 entries only)
+    assert lib.moe_grouped_fc2(A, A, 4, A, A, 4, A, 8, 256, 128, 100, A, 1, None) == UNSUPPORTED
+    assert lib.moe_quantize_mx(A, 1, 4, 64, 0, 4, A, A, None) == UNSUPPORTED
