@@ -223,7 +223,10 @@ def cpu_baseline(cfg, x, wr, b, wts, sh, dout, backward: bool, budget_experts: i
         counts = np.bincount(idx.ravel(), minlength=cfg.E)
         touched = np.nonzero(counts)[0]
         if budget_experts is None:
-            budget_experts = {"bf16": 32, "mxfp8": 3, "mxfp4": 4, "nvfp4": 4}.get(fmt, 8)
+            # bf16: the whole batch (every touched expert, the shared expert on
+            # every token: a few seconds); MX / NVFP4 fake-quantization makes
+            # the oracle far slower per expert, so those take a sample
+            budget_experts = {"bf16": cfg.E, "mxfp8": 3, "mxfp4": 4, "nvfp4": 4}.get(fmt, 8)
             if backward:
                 budget_experts = 2
         m = max(1, min(budget_experts, len(touched)))
@@ -247,7 +250,7 @@ def cpu_baseline(cfg, x, wr, b, wts, sh, dout, backward: bool, budget_experts: i
             t_exp += time.perf_counter() - t0
         t_sh, n_sh = 0.0, 0
         if sh is not None:
-            n_sh = min(T, 512)
+            n_sh = T if fmt == "bf16" else min(T, 512)
             w1s, w2s = sh["w1s"].float().cpu().numpy(), sh["w2s"].float().cpu().numpy()
             t0 = time.perf_counter()
             xq = omlp.operand(x[:n_sh], fmt, axis=-1)

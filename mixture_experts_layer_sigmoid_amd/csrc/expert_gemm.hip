@@ -306,6 +306,20 @@ void expert_gemm_kernel(XArgs p) {
   const int64_t t_first = boundary(xs.xcd) + xs.slot;
   const int64_t t_end = boundary(xs.xcd + 1);
 
+  // Per-lane LDS offsets of the activation operands inside one stage tile:
+  // chunk 2q + g (16 bytes; q = k-step for bf16 / E2M1, 2 k-step + half for
+  // E4M3) of row lane % 32 of row block 0, in the swizzled layout (the key
+  // depends on row % 16 only, so row block i adds 4 KB), and the row's MX
+  // scale words. Every step re-derives its slot's addresses from these
+  // (opaque copies), so the compiler keeps five base registers and folds the
+  // rest into the LDS instructions' immediate offsets instead of holding one
+  // address register per (slot, row block, k-step).
+  uint32_t lofs[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    lofs[q] = (lane & 31) * kStageBytes + (((2 * q + g) ^ swz_key<128>(lane & 31)) << 4);
+  uint32_t lsc = S::kA + (lane & 31) * kDpr * 4;
+
   for (int64_t t = t_first; t < t_end; t += xs.nslots) {
     // ---- decode: virtual expert, then column tile (slow) and row tile (fast) ----
     int lo = 0, hi = V;
@@ -456,8 +470,12 @@ void expert_gemm_kernel(XArgs p) {
       // 64-cycle MFMAs cover one LDS read; bf16 and E2M1 steps take 32 cycles
       // per MFMA and read two steps ahead)
       constexpr int D = OP == XOP_FP8 ? 2 : 3;
-      const uint8_t* sa = smem + SL * S::kStage;
-      const uint32_t* sasc = reinterpret_cast<const uint32_t*>(sa + S::kA);
+      // this slot's per-lane operand offsets; the row block's offset (32
+      // rows = 4 KB) and the scale word's are immediates of the LDS reads
+      uint32_t vo[4], vs;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vo[q] = lofs[q] + SL * S::kStage;
+      vs = lsc + SL * S::kStage;
       using AFrag = std::conditional_t<O::kBf16A, bf16x8_t, i32x8_t>;
       AFrag afr[D];
       uint32_t asw[D];
@@ -465,19 +483,20 @@ void expert_gemm_kernel(XArgs p) {
       auto fetch = [&](auto st_c) {
         constexpr int ST = decltype(st_c)::value;
         constexpr int s = ST / NV, i = ST % NV, buf = ST % D;
-        const int row = 32 * i + (lane & 31);
+        constexpr int ri = 32 * kStageBytes * i;
         if constexpr (O::kBf16A) {
-          afr[buf] = *reinterpret_cast<const bf16x8_t*>(sa + swz<128>(row, 2 * s + g));
+          afr[buf] = *reinterpret_cast<const bf16x8_t*>(smem + vo[s] + ri);
         } else {
           if constexpr (OP == XOP_FP8) {
-            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz<128>(row, 4 * s + g));
-            const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sa + swz<128>(row, 4 * s + 2 + g));
+            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(smem + vo[2 * s] + ri);
+            const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(smem + vo[2 * s + 1] + ri);
             afr[buf] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
           } else {
-            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz<128>(row, 2 * s + g));
+            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(smem + vo[s] + ri);
             afr[buf] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
           }
-          asw[buf] = sasc[row * kDpr + ((2 * s + g) >> 2)];
+          // word (2 s + g) / 4 = s / 2 of the row's scale dwords
+          asw[buf] = *reinterpret_cast<const uint32_t*>(smem + vs + 4 * (32 * kDpr * i + (s >> 1)));
         }
       };
       static_for<(NSTEP < D - 1 ? NSTEP : D - 1)>([&](auto st_c) { fetch(st_c); });
@@ -572,6 +591,7 @@ void expert_gemm_kernel(XArgs p) {
         constexpr int kB = O::kBLoads;
         using NSL = std::integral_constant<int, (J + P - 1) % P>;
         const int kt_next = min(kt + P - 1, KT - 1);
+        asm volatile("" : "+v"(lofs[0]), "+v"(lofs[1]), "+v"(lofs[2]), "+v"(lofs[3]), "+v"(lsc));
         wait_vmcnt<kWait>();
         lds_barrier();
         static_for<NV + kAScPerWave>([&](auto o_c) {

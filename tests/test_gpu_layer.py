@@ -155,13 +155,15 @@ def test_shared_fold_matches_separate(gpu_lib, name, T):
 
 
 @pytest.mark.parametrize("name,fuse", [("dsv3_bf16_t4096", False), ("dsv3_bf16_t4096", True),
-                                       ("dsv3_mxfp8_decode_t64", True), ("dsv4_mxfp4_t16384", False)])
+                                       ("dsv3_mxfp8_decode_t64", True), ("dsv4_mxfp4_t16384", False),
+                                       ("dsv3_ep8_mxfp8_t4096", False)])
 def test_expert_gemms_run_to_run_identical(gpu_lib, name, fuse):
     """Repeated fc1 / fc2 launches on the same inputs give the same bits: the
     bf16 layer at full size (256 experts of mostly one or two 32-row blocks,
     the shape that once read activation rows before their loads had landed),
-    the MXFP8 decode batch (64-row tiles, deep weight ring) and the MXFP4
-    batch (block-scaled 4-bit operands, h MX-encoded in the epilogue)."""
+    the MXFP8 decode batch (64-row tiles, deep weight ring), the MXFP4
+    batch (block-scaled 4-bit operands, h MX-encoded in the epilogue) and the
+    expert-parallel share (MXFP8, full 256-row tiles over 4096-row experts)."""
     cfg = configs.get(name)
     log(f"run-to-run fc1 / fc2 {cfg.name} fuse_shared={fuse}")
     x, wr, b, wts, sh = _full_setup(cfg)
@@ -172,10 +174,17 @@ def test_expert_gemms_run_to_run_identical(gpu_lib, name, fuse):
     xd = dev(x, "bf16")
     fw(xd, dev(wr, "bf16"), dev(b), ew, sw)
     torch.cuda.synchronize()
-    bufs = [fw.h, fw.y_rows] + ([fw.h_sc] if fw.h_sc is not None else [])
+    # the rows the GEMMs write: every expert segment and, when folded, the
+    # shared expert's rows from `bound` on (the slack rows between the last
+    # segment and `bound` that the aligned permute reserves are never written)
+    nrow, nb = int(fw.offsets[-1]), fw.bound
+    full = [fw.h, fw.y_rows] + ([fw.h_sc] if fw.h_sc is not None else [])
+    bufs = [t[:nrow] for t in full]
+    if fuse and sh is not None:
+        bufs += [t[nb:nb + cfg.T] for t in full]
     first = [t.clone() for t in bufs]
     for rep in range(6):
-        for t in bufs:
+        for t in full:
             t.zero_()
         fw.experts_fc1(xd, ew, sw=sw)
         fw.experts_fc2(ew, sw=sw)
