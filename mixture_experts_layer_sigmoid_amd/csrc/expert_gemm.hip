@@ -155,7 +155,8 @@ struct XSmem {
   static constexpr int kRing = P * kStage;
   static constexpr int kEpi = (kRows < kPassRows ? kRows : kPassRows) * kCs * 4;
   static constexpr int kBody = kRing > kEpi ? kRing : kEpi;
-  static constexpr int kSched = (kMaxVirt + 2) * 4 + kRows * 4 + (kMaxVirt + 1) * 4 + kMaxVirt * 2;
+  static constexpr int kSched = (kMaxVirt + 2) * 4 + kRows * 4 + (kMaxVirt + 1) * 4 + kMaxVirt * 2 +
+                                (kMaxGroups + 1) * 4;
   static constexpr int kTotal = kBody + kSched;
 };
 
@@ -200,6 +201,7 @@ void expert_gemm_kernel(XArgs p) {
   int32_t* s_tot = s_src + kRows;
   int32_t* s_cost = s_tot + 1;                                    // [V+1] cost prefix
   int16_t* s_vmap = reinterpret_cast<int16_t*>(s_cost + kMaxVirt + 1);  // [V] -> expert / E + part
+  int32_t* s_off = reinterpret_cast<int32_t*>(s_vmap + kMaxVirt);       // [E+1] segment offsets
   int32_t* part = reinterpret_cast<int32_t*>(smem);  // scan scratch (before any load)
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -218,6 +220,9 @@ void expert_gemm_kernel(XArgs p) {
     s_vmap[e + x] = static_cast<int16_t>(e);
   }
   if (dense && tid < kDenseParts) s_vmap[(tid + 1) * E / kDenseParts + tid] = static_cast<int16_t>(E + tid);
+  // the segment offsets, read from LDS by every tile's set-up (no global
+  // memory round trip per tile)
+  for (int e = tid; e <= E; e += 256) s_off[e] = p.offsets[e];
   __syncthreads();
   // rows of virtual expert v (a routed segment, or a part of the dense rows)
   auto vrows = [&](int v) {
@@ -226,7 +231,7 @@ void expert_gemm_kernel(XArgs p) {
       const int x = e - E;
       return p.d_rows * (x + 1) / kDenseParts - p.d_rows * x / kDenseParts;
     }
-    const int n_e = min(p.offsets[e + 1], (int)p.rows) - p.offsets[e];
+    const int n_e = min(s_off[e + 1], (int)p.rows) - s_off[e];
     return n_e < 0 ? 0 : n_e;
   };
 
@@ -336,7 +341,7 @@ void expert_gemm_kernel(XArgs p) {
     const int nt = static_cast<int>(local / mtiles);
     const int mt = static_cast<int>(local % mtiles);
     const int dlo = dn ? p.d_rows * (e - E) / kDenseParts : 0;   // first dense row of the part
-    const int seg_lo = dn ? p.d_row0 + dlo : p.offsets[e];
+    const int seg_lo = dn ? p.d_row0 + dlo : s_off[e];
     const int n_e = vrows(v);
     // A row of output row r: the gathered token row, the row itself, or for
     // the dense expert its own A rows
