@@ -195,6 +195,11 @@ void expert_gemm_kernel(XArgs p) {
   // same LDS words)
   constexpr int kAScPerWave = kSB > 0 ? (kAScIns + 3) / 4 : 0;
   static_assert(kAIns >= 1, "tile needs at least 32 rows");
+  // Plain epilogue (bf16 rows out): the weights are the matrix
+  // instructions' first operand and the activation rows the second, so the
+  // accumulators hold, per lane, one row and 16 of its columns; rows are
+  // written straight from registers, with no LDS round trip.
+  constexpr bool kRowsInLanes = EPI == XEPI_PLAIN;
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::kTotal];
   int32_t* s_mt = reinterpret_cast<int32_t*>(smem + S::kBody);   // [V+1] row-tile prefix
   int32_t* s_src = s_mt + (kMaxVirt + 1);                         // [kRows] source rows
@@ -518,8 +523,13 @@ void expert_gemm_kernel(XArgs p) {
         if constexpr (OP == XOP_BF16) {
           const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, bq[SL][0][s]);
           const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, bq[SL][1][s]);
-          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], b0, acc[i][0], 0, 0, 0);
-          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], b1, acc[i][1], 0, 0, 0);
+          if constexpr (kRowsInLanes) {
+            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, afr[buf], acc[i][0], 0, 0, 0);
+            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, afr[buf], acc[i][1], 0, 0, 0);
+          } else {
+            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], b0, acc[i][0], 0, 0, 0);
+            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], b1, acc[i][1], 0, 0, 0);
+          }
         } else if constexpr (OP == XOP_NVFP4) {
           // the lane's 8 codes of k-step s (dword s of its 16-byte load) times
           // their E4M3 block scale (byte s of its scale word): E2M1 -> fp32
@@ -540,8 +550,13 @@ void expert_gemm_kernel(XArgs p) {
               bcv[c] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
             }
           }
-          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], bcv[0], acc[i][0], 0, 0, 0);
-          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], bcv[1], acc[i][1], 0, 0, 0);
+          if constexpr (kRowsInLanes) {
+            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bcv[0], afr[buf], acc[i][0], 0, 0, 0);
+            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bcv[1], afr[buf], acc[i][1], 0, 0, 0);
+          } else {
+            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], bcv[0], acc[i][0], 0, 0, 0);
+            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[buf], bcv[1], acc[i][1], 0, 0, 0);
+          }
         } else {
           i32x8_t b0, b1;
           if constexpr (OP == XOP_FP8) {
@@ -558,8 +573,13 @@ void expert_gemm_kernel(XArgs p) {
           const int bs1 = static_cast<int>((bs[SL][1] >> (8 * s)) & 0xFFu);
           const int as = static_cast<int>((asw[buf] >> (8 * ((2 * s + g) & 3))) & 0xFFu);
           constexpr int fmt = OP == XOP_FP8 ? 0 : 4;
-          acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[buf], b0, acc[i][0], fmt, fmt, 0, as, 0, bs0);
-          acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[buf], b1, acc[i][1], fmt, fmt, 0, as, 0, bs1);
+          if constexpr (kRowsInLanes) {
+            acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, afr[buf], acc[i][0], fmt, fmt, 0, bs0, 0, as);
+            acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, afr[buf], acc[i][1], fmt, fmt, 0, bs1, 0, as);
+          } else {
+            acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[buf], b0, acc[i][0], fmt, fmt, 0, as, 0, bs0);
+            acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[buf], b1, acc[i][1], fmt, fmt, 0, as, 0, bs1);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -623,6 +643,51 @@ void expert_gemm_kernel(XArgs p) {
     // them, so the wait is explicit
     wait_vmcnt<0>();
     __syncthreads();
+
+    if constexpr (kRowsInLanes) {
+      // ---- plain epilogue from registers: in a 32x32 block lane l holds
+      // row l % 32 and, in registers 4k..4k+3, columns 8k + 4g + 0..3 (g =
+      // l / 32). One permlane32 swap per dword pair of the blocks k and k+2
+      // gives lane l < 32 columns [8k', 8k' + 8) and lane l + 32 columns
+      // [16 + 8k', 16 + 8k' + 8) (k' = k); so lane l writes columns [0, 16)
+      // and lane l + 32 columns [16, 32) of its row, 32 contiguous bytes ----
+      const float gs = OP == XOP_NVFP4 ? p.a_g * p.w_g[e] : 1.f;
+      if (active) {
+#pragma unroll
+        for (int i = 0; i < MAXNV; ++i) {
+          const int r = 32 * i + (lane & 31);
+          if (i < nrb) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const f32x16_t& a = acc[i][c];
+              uint32_t w[8];
+#pragma unroll
+              for (int k = 0; k < 2; ++k) {
+                // blocks k (columns 8k + 4g ..) and k + 2 (16 + 8k + 4g ..)
+                const uint32_t x0 = pack_bf16x2(a[4 * k] * gs, a[4 * k + 1] * gs);
+                const uint32_t x1 = pack_bf16x2(a[4 * k + 2] * gs, a[4 * k + 3] * gs);
+                const uint32_t y0 = pack_bf16x2(a[4 * k + 8] * gs, a[4 * k + 9] * gs);
+                const uint32_t y1 = pack_bf16x2(a[4 * k + 10] * gs, a[4 * k + 11] * gs);
+                const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+                w[4 * k + 0] = s0[0];
+                w[4 * k + 1] = s1[0];
+                w[4 * k + 2] = s0[1];
+                w[4 * k + 3] = s1[1];
+              }
+              if (r < nrows) {
+                const int col = nt * kTileCols + 64 * wave + 32 * c + 16 * g;
+                u32x4_t* o = reinterpret_cast<u32x4_t*>(p.out + static_cast<int64_t>(row0 + r) * p.out_row_bytes +
+                                                        static_cast<int64_t>(col) * 2);
+                o[0] = u32x4_t{w[0], w[1], w[2], w[3]};
+                o[1] = u32x4_t{w[4], w[5], w[6], w[7]};
+              }
+            }
+          }
+        }
+      }
+      continue;
+    }
 
     // ---- epilogue in passes of up to 128 rows through an fp32 LDS tile ----
     // C layout of a 32x32 MFMA: lane l, element r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
