@@ -45,13 +45,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       int H, void* __restrict__ out) {
   const int t = blockIdx.x;
   const int nvec = H / 8;
-  // the token's k rows and weights (uniform across the workgroup)
+  // the token's k rows and weights (uniform across the workgroup): lane j
+  // of every wave loads entry j (one memory round trip for all of them),
+  // then each is broadcast from its lane
+  const int lane = threadIdx.x & 63;
+  int rv = 0;
+  float wv = 1.f;
+  if (lane < k) {
+    rv = row_map[static_cast<int64_t>(t) * k + lane];
+    if (w) wv = w[static_cast<int64_t>(t) * k + lane];
+  }
   int64_t rows[kMaxK];
   float wts[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
-    rows[j] = j < k ? static_cast<int64_t>(row_map[static_cast<int64_t>(t) * k + j]) * H : 0;
-    wts[j] = j < k ? (w ? w[static_cast<int64_t>(t) * k + j] : 1.f) : 0.f;
+    rows[j] = j < k ? static_cast<int64_t>(__builtin_amdgcn_readlane(rv, j)) * H : 0;
+    wts[j] = j < k ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), j)) : 0.f;
   }
   constexpr int kWords = YF == MOE_BF16 ? 1 : 2;  // 16-byte words per 8 values
   for (int c = threadIdx.x; c < nvec; c += 256) {

@@ -15,7 +15,8 @@
 //      marks every row of src_row as padding (-1).
 //   2. scan: one workgroup turns the [chunks, E] histogram into per-chunk
 //      row bases (column prefix + padded exclusive scan over experts) and
-//      writes counts and offsets.
+//      writes counts and offsets; each expert column is split over up to 32
+//      threads, whose partial sums are combined in LDS.
 //   3. scatter: each wavefront re-walks its chunk in order; an entry's row is
 //      its chunk base + running count + number of lower lanes with the same
 //      expert, which keeps (token, slot) order. It writes row_map and
@@ -81,24 +82,46 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ hist, 
   __shared__ int32_t padded[kMaxE];
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
-  // column prefix: hist[c][e] becomes the rows of expert e in chunks < c
-  for (int e = tid; e < E; e += 1024) {
-    int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = hist[static_cast<int64_t>(c) * E + e];
-      hist[static_cast<int64_t>(c) * E + e] = run;
-      run += v;
+  // tpc threads per expert column, each over a contiguous range of chunks
+  // (tpc a power of two, tpc * E <= 1024); loads go out eight at a time
+  int tpc = 1;
+  while (tpc < 32 && 2 * tpc * E <= 1024) tpc <<= 1;
+  const int e = tid / tpc, q = tid % tpc;
+  const int per = (nchunks + tpc - 1) / tpc;
+  const int c_lo = min(nchunks, q * per), c_hi = min(nchunks, c_lo + per);
+  const bool col = e < E;
+  // pass 1: rows of expert e in this thread's chunks
+  int sum = 0;
+  if (col) {
+    for (int c = c_lo; c < c_hi; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = c + u < c_hi ? hist[static_cast<int64_t>(c + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += v[u];
     }
-    counts[e] = run;
-    padded[e] = (run + align - 1) / align * align;
+    part[tid] = sum;
   }
   __syncthreads();
-  // exclusive scan of padded counts: each thread sums a contiguous run of
-  // experts, then the 1024 partial sums are scanned in LDS
-  const int per = (E + 1023) / 1024;
-  const int lo = tid * per, hi = min(E, lo + per);
+  // counts and padded counts per expert
+  for (int x = tid; x < E; x += 1024) {
+    int run = 0;
+    for (int r = 0; r < tpc; ++r) run += part[x * tpc + r];
+    counts[x] = run;
+    padded[x] = (run + align - 1) / align * align;
+  }
+  __syncthreads();
+  // exclusive scan of the padded counts: each thread sums a contiguous run
+  // of experts, then the 1024 partial sums are scanned in LDS (part[] is
+  // read into registers first: it is reused here)
+  int before = 0;  // rows of expert e in the chunks before this thread's
+  if (col)
+    for (int r = 0; r < q; ++r) before += part[e * tpc + r];
+  __syncthreads();
+  const int pe = (E + 1023) / 1024;
+  const int lo = tid * pe, hi = min(E, lo + pe);
   int s = 0;
-  for (int e = lo; e < hi; ++e) s += padded[e];
+  for (int x = lo; x < hi; ++x) s += padded[x];
   part[tid] = s;
   __syncthreads();
   for (int d = 1; d < 1024; d <<= 1) {
@@ -108,16 +131,28 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ hist, 
     __syncthreads();
   }
   int run = tid > 0 ? part[tid - 1] : 0;
-  for (int e = lo; e < hi; ++e) {
-    const int p = padded[e];
-    padded[e] = run;  // becomes the exclusive offset
+  for (int x = lo; x < hi; ++x) {
+    const int p = padded[x];
+    padded[x] = run;  // becomes the exclusive offset
     run += p;
   }
   if (tid == 1023) offsets[E] = part[1023];
   __syncthreads();
-  for (int e = tid; e < E; e += 1024) {
-    offsets[e] = padded[e];
-    for (int c = 0; c < nchunks; ++c) hist[static_cast<int64_t>(c) * E + e] += padded[e];
+  for (int x = tid; x < E; x += 1024) offsets[x] = padded[x];
+  // pass 2: hist[c][e] becomes the first row of expert e's entries of chunk
+  // c: the expert's offset plus its rows in the chunks before c
+  if (col) {
+    int r0 = padded[e] + before;
+    for (int c = c_lo; c < c_hi; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = c + u < c_hi ? hist[static_cast<int64_t>(c + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (c + u < c_hi) hist[static_cast<int64_t>(c + u) * E + e] = r0;
+        r0 += v[u];
+      }
+    }
   }
 }
 
