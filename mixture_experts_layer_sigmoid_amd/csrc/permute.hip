@@ -64,10 +64,18 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   for (int e = lane; e < E; e += 64) cnt[wave][e] = 0;
   wave_lds_sync();
   const int64_t base = static_cast<int64_t>(c) * kChunk;
-  for (int it = 0; it < kChunk; it += 64) {
-    const int64_t i = base + it + lane;
+  // the chunk's indices, all loads in flight at once
+  int ev[kChunk / 64];
+#pragma unroll
+  for (int it = 0; it < kChunk / 64; ++it) {
+    const int64_t i = base + 64 * it + lane;
+    ev[it] = i < n ? idx[i] : 0;
+  }
+#pragma unroll
+  for (int it = 0; it < kChunk / 64; ++it) {
+    const int64_t i = base + 64 * it + lane;
     const bool valid = i < n;
-    const int e = valid ? idx[i] : 0;
+    const int e = ev[it];
     const unsigned long long peers = same_value_lanes(e, valid, nbits);
     if (valid && lane == __ffsll(static_cast<long long>(peers)) - 1)
       cnt[wave][e] += __popcll(peers);
@@ -169,10 +177,17 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   wave_lds_sync();
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int64_t base = static_cast<int64_t>(c) * kChunk;
-  for (int it = 0; it < kChunk; it += 64) {
-    const int64_t i = base + it + lane;
+  int ev[kChunk / 64];
+#pragma unroll
+  for (int it = 0; it < kChunk / 64; ++it) {
+    const int64_t i = base + 64 * it + lane;
+    ev[it] = i < n ? idx[i] : 0;
+  }
+#pragma unroll
+  for (int it = 0; it < kChunk / 64; ++it) {
+    const int64_t i = base + 64 * it + lane;
     const bool valid = i < n;
-    const int e = valid ? idx[i] : 0;
+    const int e = ev[it];
     const unsigned long long peers = same_value_lanes(e, valid, nbits);
     int row = 0;
     if (valid) row = run[wave][e] + __popcll(peers & below);
