@@ -73,6 +73,8 @@ constexpr int kTileCost = 220;
 // evenly among the routed experts, so every XCD runs a share of its
 // compute-bound tiles beside its share of the weight stream.
 constexpr int kDenseParts = 8;
+// row tiles per group in the tile order of a long segment
+constexpr int kRowGroup = 8;
 constexpr int kMaxVirt = kMaxGroups + kDenseParts;
 
 enum { XOP_BF16 = 0, XOP_FP8 = 1, XOP_FP4 = 2, XOP_NVFP4 = 3 };
@@ -343,8 +345,15 @@ void expert_gemm_kernel(XArgs p) {
     const bool dn = e >= E;                      // a part of the dense expert
     const int mtiles = s_mt[v + 1] - s_mt[v];
     const int64_t local = t - static_cast<int64_t>(s_mt[v]) * p.n_tiles;
-    const int nt = static_cast<int>(local / mtiles);
-    const int mt = static_cast<int>(local % mtiles);
+    // a long segment's row tiles run in groups of kRowGroup: group, then
+    // column tile, then row tile (the tiles an XCD runs at once cover
+    // kRowGroup row tiles x a few column tiles, sharing both operands in its
+    // L2); a segment of at most kRowGroup row tiles is one group
+    const int grp = static_cast<int>(local / (kRowGroup * p.n_tiles));
+    const int gm = min(kRowGroup, mtiles - kRowGroup * grp);
+    const int idx = static_cast<int>(local - static_cast<int64_t>(grp) * kRowGroup * p.n_tiles);
+    const int nt = idx / gm;
+    const int mt = kRowGroup * grp + idx % gm;
     const int dlo = dn ? p.d_rows * (e - E) / kDenseParts : 0;   // first dense row of the part
     const int seg_lo = dn ? p.d_row0 + dlo : s_off[e];
     const int n_e = vrows(v);
