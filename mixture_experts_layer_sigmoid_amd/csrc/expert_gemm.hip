@@ -74,7 +74,7 @@ constexpr int kTileCost = 220;
 // compute-bound tiles beside its share of the weight stream.
 constexpr int kDenseParts = 8;
 // row tiles per group in the tile order of a long segment
-constexpr int kRowGroup = 8;
+constexpr int kRowGroup = 4;
 constexpr int kMaxVirt = kMaxGroups + kDenseParts;
 
 enum { XOP_BF16 = 0, XOP_FP8 = 1, XOP_FP4 = 2, XOP_NVFP4 = 3 };
