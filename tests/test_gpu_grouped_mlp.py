@@ -87,7 +87,9 @@ def _oracle_rows(cfg, h, offsets, src, E):
 @pytest.mark.parametrize("name,T,k,heavy,align", [
     ("mini_fp32", 200, 3, 0, 1), ("mini_bf16", 600, 2, 420, 1), ("mini_bf16", 37, 8, 0, 32),
     ("mini_mxfp8_decode", 40, 8, 0, 1), ("mini_mxfp8_decode", 500, 3, 380, 16),
-    ("mini_mxfp4", 500, 6, 300, 1), ("mini_skew_mxfp8", 300, 6, 290, 32)])
+    ("mini_mxfp4", 500, 6, 300, 1), ("mini_skew_mxfp8", 300, 6, 290, 32),
+    # a segment of 6 / 7 row tiles: groups of 4 row tiles and a partial group
+    ("mini_bf16", 1500, 2, 1450, 1), ("mini_mxfp4", 1500, 6, 1450, 1)])
 def test_stage_parity(gpu_lib, name, T, k, heavy, align):
     cfg = configs.get(name)
     log(f"grouped MLP stage {name} T={T} k={k} heavy={heavy} align={align}")
@@ -98,6 +100,8 @@ def test_stage_parity(gpu_lib, name, T, k, heavy, align):
     idx = _routing(T, cfg.E, k, T + k, heavy)
     counts, offsets, row_map, src = pm.permute_maps(idx, cfg.E, align)
     assert counts.max() > 256 or heavy == 0
+    if heavy > 1000:
+        assert counts.max() > 5 * 256 and counts.max() % (4 * 256) != 0
     ew = _weights_dev(cfg, h)
     x_d = dev(x, cfg.act_dtype)
     y, save = _run(cfg, x_d, ew, offsets, src, len(src), T, act_save=True)
