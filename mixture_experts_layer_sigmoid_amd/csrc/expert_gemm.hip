@@ -40,10 +40,12 @@
 //   * The tile list (experts x column tiles x row tiles) is built in LDS
 //     from `offsets` by every workgroup, cut into 8 contiguous chunks, one
 //     per XCD; consecutive tiles are the row tiles of one weight tile, then
-//     the column tiles of one expert, so concurrent workgroups of an XCD
-//     share activation rows and weight tiles in its L2.
+//     the column tiles of one expert (a long segment in groups of 4 row
+//     tiles), so concurrent workgroups of an XCD share activation rows and
+//     weight tiles in its L2.
 //   * Epilogues go through LDS in passes of 128 rows to row-major 16-byte
-//     stores: SwiGLU (bf16 h, or MX-encoded 32-column blocks of h formed in
+//     stores (fc2 and the fc1 data gradient store rows straight from
+//     registers): SwiGLU (bf16 h, or MX-encoded 32-column blocks of h formed in
 //     registers when the fp32 fc1 output is not saved: a wave holds both
 //     halves of the same columns), plain bf16 y, or the SwiGLU backward (dA
 //     in MX or bf16, optional fp32 copy).
